@@ -1,0 +1,346 @@
+"""Plain, slow float64 CPU oracle for PISA's hot path.
+
+TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this module. The HIP library never calls it, and it
+shares no code with the HIP path. It follows the pages directly, one query unit
+at a time, with no blocking, fusion or reordering beyond what the definitions
+state.
+
+Pages cited (titles as published):
+  [digest]   "Block Sparse Attention with Log-Linear Complexity" -- ai-papers-daily digest of the
+             full paper. Sections: 工作参考价值 (engineering takeaways), 动机 (motivation),
+             方法关键点 (method key points), 关键实验 (key experiments).
+  [explainer] "PISA：log-linear 复杂度的金字塔稀疏注意力" -- papers.ananclaw.com explainer, written
+             from the abstract. Sections: 核心方法 §1 (pyramid), §2 (pyramid Top-K), §3 (complexity),
+             §7 (pseudocode).
+  [abstract] arxivdaily abstract page for arXiv 2609.31093 (英文摘要 / English abstract).
+
+Notation: C = leaf block size, g = merge factor (2), K = Top-K, G = query heads per
+KV head, s = 1/sqrt(d). A "unit" is one KV head at one query position i; its G
+query heads share one selection ([digest] 方法关键点, Kernel bullet: GQA heads of one
+KV head share the block selection).
+
+Readings where the pages are silent (each also listed in the design notes):
+  * node (l, j) spans tokens [j*C*g^l, min(n, (j+1)*C*g^l)), where n is the number
+    of tokens present; its mean is the mean of the raw keys in that span
+    (token-weighted, so a ragged node is the mean of what it holds);
+  * a node is eligible for query i iff its first token is <= i; a leaf's LSE
+    masks tokens t > i; an intermediate node's score uses only its eligible
+    children, each with its full-span mean;
+  * the same scale s at every level; GQA score = sum over the group's heads of
+    each head's LSE, at every level;
+  * a level whose candidate set has at most K nodes keeps all of them;
+  * Top-K order: score descending, then node index ascending; the selection is
+    output in ascending leaf order, padded with -1;
+  * attention normalises over the union of the selected leaves' tokens t <= i.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+NEG_INF = -np.inf
+
+
+# ----------------------------------------------------------------------------------------------
+# LogSumExp. [explainer] 核心方法 §4 and [abstract]: scores are LogSumExp values computed with a
+# running maximum; here the plain definition LSE(x) = m + log(sum(exp(x - m))), m = max(x).
+# ----------------------------------------------------------------------------------------------
+def logsumexp(x: np.ndarray, axis: int = -1) -> np.ndarray:
+    """LSE along `axis`; an all -inf (or empty) slice gives -inf."""
+    x = np.asarray(x, dtype=np.float64)
+    if x.shape[axis] == 0:
+        return np.full(np.delete(x.shape, axis if axis >= 0 else x.ndim + axis), NEG_INF)
+    m = np.max(x, axis=axis, keepdims=True)
+    finite = np.isfinite(m)
+    m_safe = np.where(finite, m, 0.0)
+    with np.errstate(divide="ignore"):
+        out = np.log(np.sum(np.exp(x - m_safe), axis=axis, keepdims=True)) + m_safe
+    out = np.where(finite, out, m)
+    return np.squeeze(out, axis=axis)
+
+
+# ----------------------------------------------------------------------------------------------
+# Pyramid. [digest] 方法关键点, pyramid bullet: the finest level is leaf blocks of C tokens, each
+# higher level mean-pools with merge factor 2, giving O(log N) levels up to one root.
+# [explainer] 核心方法 §1: level 0 has N/B blocks, level 1 N/(2B), ... up to a single block.
+# ----------------------------------------------------------------------------------------------
+def level_sizes(n_tokens: int, C: int, g: int = 2) -> list[int]:
+    """Node counts per level, leaf level first, ending with the single root."""
+    sizes = [max(1, -(-n_tokens // C))]
+    while sizes[-1] > 1:
+        sizes.append(-(-sizes[-1] // g))
+    return sizes
+
+
+def node_span(l: int, j: int, C: int, g: int, n_tokens: int) -> tuple[int, int]:
+    w = C * g ** l
+    return j * w, min(n_tokens, (j + 1) * w)
+
+
+@dataclasses.dataclass
+class Pyramid:
+    means: list[np.ndarray]  # per level, [n_l, d] float64
+    counts: list[np.ndarray]  # per level, [n_l] tokens held
+    C: int
+    g: int
+    n_tokens: int
+
+    @property
+    def n_levels(self) -> int:
+        return len(self.means)
+
+    @property
+    def root_level(self) -> int:
+        return len(self.means) - 1
+
+
+def build_pyramid(k: np.ndarray, C: int, g: int = 2, n_tokens: int | None = None) -> Pyramid:
+    """Mean-pooled key pyramid of one KV head.
+
+    Level 0 is the mean of each leaf's raw keys. Level l+1 is the token-weighted mean of
+    its (at most g) children, which equals the plain mean of the children's means when
+    they are full, and equals the direct mean over the node's span in every case.
+    """
+    k = np.asarray(k, dtype=np.float64)
+    n = k.shape[0] if n_tokens is None else int(n_tokens)
+    sizes = level_sizes(n, C, g)
+    means, counts = [], []
+    leaf_mean = np.zeros((sizes[0], k.shape[1]))
+    leaf_cnt = np.zeros(sizes[0])
+    for j in range(sizes[0]):
+        t0, t1 = node_span(0, j, C, g, n)
+        leaf_cnt[j] = t1 - t0
+        leaf_mean[j] = k[t0:t1].mean(axis=0) if t1 > t0 else 0.0
+    means.append(leaf_mean)
+    counts.append(leaf_cnt)
+    for l in range(1, len(sizes)):
+        prev_m, prev_c = means[-1], counts[-1]
+        m = np.zeros((sizes[l], k.shape[1]))
+        c = np.zeros(sizes[l])
+        for j in range(sizes[l]):
+            kids = [cj for cj in range(j * g, min((j + 1) * g, sizes[l - 1]))]
+            tot = sum(prev_c[cj] for cj in kids)
+            c[j] = tot
+            m[j] = sum(prev_c[cj] * prev_m[cj] for cj in kids) / tot
+        means.append(m)
+        counts.append(c)
+    return Pyramid(means=means, counts=counts, C=C, g=g, n_tokens=n)
+
+
+def eligible(l: int, j: int, i: int, C: int, g: int) -> bool:
+    """A node is eligible for query position i iff its first token is <= i (causal)."""
+    return j * C * g ** l <= i
+
+
+def children(l: int, j: int, pyr: Pyramid) -> list[int]:
+    """Indices (at level l-1) of node (l, j)'s children that exist."""
+    n_prev = pyr.means[l - 1].shape[0]
+    return [c for c in range(j * pyr.g, (j + 1) * pyr.g) if c < n_prev]
+
+
+# ----------------------------------------------------------------------------------------------
+# Scores. [digest] 方法关键点, scoring bullet: leaf blocks are scored by the exact LSE over their raw
+# keys; intermediate blocks by the LSE over their children's mean summaries. [digest] 工作参考价值,
+# third bullet: under GQA the per-head LSEs are summed over the query heads of a KV head.
+# ----------------------------------------------------------------------------------------------
+def leaf_lse_per_head(qg: np.ndarray, k: np.ndarray, j: int, i: int, C: int, scale: float,
+                      n_tokens: int) -> np.ndarray:
+    """[G] per-head LSE over tokens t of leaf j with t <= i of scale * q_h . k_t."""
+    t0 = j * C
+    t1 = min(n_tokens, (j + 1) * C, i + 1)
+    if t1 <= t0:
+        return np.full(qg.shape[0], NEG_INF)
+    logits = scale * (qg @ k[t0:t1].T)  # [G, T]
+    return logsumexp(logits, axis=-1)
+
+
+def node_lse_per_head(qg: np.ndarray, pyr: Pyramid, l: int, j: int, i: int, scale: float) -> np.ndarray:
+    """[G] per-head LSE over the eligible children c of node (l, j), l >= 1, of scale * q_h . mu(c)."""
+    kids = [c for c in children(l, j, pyr) if eligible(l - 1, c, i, pyr.C, pyr.g)]
+    if not kids:
+        return np.full(qg.shape[0], NEG_INF)
+    logits = scale * (qg @ pyr.means[l - 1][kids].T)  # [G, n_kids]
+    return logsumexp(logits, axis=-1)
+
+
+def _topk_order(cands: list[int], scores: np.ndarray) -> list[int]:
+    """Positions into `cands` ordered by score descending, then node index ascending."""
+    return sorted(range(len(cands)), key=lambda p: (-scores[p], cands[p]))
+
+
+@dataclasses.dataclass
+class UnitSelection:
+    sel: np.ndarray  # [K] ascending leaf indices, -1 padded
+    sel_lse: np.ndarray  # [G, K] per-head leaf LSE of each selected leaf (-inf for padding)
+    margin: float  # min over levels with > K candidates of S_(K) - S_(K+1); +inf if none
+    kept: dict  # level -> sorted kept node list
+    leaf_scores: dict  # leaf -> summed score, for the leaf candidates that were scored
+
+
+# ----------------------------------------------------------------------------------------------
+# Coarse-to-fine walk. [digest] 方法关键点, pyramid bullet: selection starts at the coarsest level
+# with a candidate set of one node; each level scores its bounded candidate set, keeps the Top-K and
+# expands only the kept nodes' children, down to the leaves. [digest] 方法关键点, complexity bullet:
+# at most g*K candidates per query per level. [explainer] 核心方法 §2 (the same loop, stated from the
+# coarsest level down).
+# ----------------------------------------------------------------------------------------------
+def select_unit(qg: np.ndarray, k: np.ndarray, pyr: Pyramid, i: int, K: int, scale: float) -> UnitSelection:
+    qg = np.asarray(qg, dtype=np.float64)
+    C, g, n = pyr.C, pyr.g, pyr.n_tokens
+    G = qg.shape[0]
+    assert 0 <= i < n
+    kept = {pyr.root_level: [0]}
+    active = [0]
+    margin = math.inf
+    leaf_scores = {}
+    leaf_head_lse = {}
+    for l in range(pyr.root_level - 1, -1, -1):
+        cand = sorted(c for p in active for c in children(l + 1, p, pyr) if eligible(l, c, i, C, g))
+        if l == 0:
+            per_head = [leaf_lse_per_head(qg, k, j, i, C, scale, n) for j in cand]
+            for j, ph in zip(cand, per_head):
+                leaf_head_lse[j] = ph
+        if len(cand) <= K:
+            active = cand
+        else:
+            if l == 0:
+                scores = np.array([leaf_head_lse[j].sum() for j in cand])
+                for j, s_ in zip(cand, scores):
+                    leaf_scores[j] = s_
+            else:
+                scores = np.array([node_lse_per_head(qg, pyr, l, c, i, scale).sum() for c in cand])
+            order = _topk_order(cand, scores)
+            margin = min(margin, scores[order[K - 1]] - scores[order[K]])
+            active = sorted(cand[p] for p in order[:K])
+        kept[l] = list(active)
+    if pyr.root_level == 0:
+        # a single leaf: it is the whole selection
+        leaf_head_lse[0] = leaf_lse_per_head(qg, k, 0, i, C, scale, n)
+    sel = np.full(K, -1, dtype=np.int64)
+    sel_lse = np.full((G, K), NEG_INF)
+    for s_, j in enumerate(active):
+        sel[s_] = j
+        sel_lse[:, s_] = leaf_head_lse[j]
+    return UnitSelection(sel=sel, sel_lse=sel_lse, margin=margin, kept=kept, leaf_scores=leaf_scores)
+
+
+# ----------------------------------------------------------------------------------------------
+# Block-sparse attention. [explainer] 核心方法 §7 (last step of the pseudocode: attention over the
+# selected finest blocks only) and [digest] 工作参考价值 fourth bullet (gradients flow only through the
+# selected attention). The softmax normaliser is over the selected tokens t <= i only.
+# ----------------------------------------------------------------------------------------------
+def attend_unit(qg: np.ndarray, k: np.ndarray, v: np.ndarray, sel: np.ndarray, i: int, C: int, scale: float,
+                n_tokens: int) -> tuple[np.ndarray, np.ndarray]:
+    """Returns (O [G, d], o_lse [G]) for one unit."""
+    toks = []
+    for j in sel:
+        if j < 0:
+            continue
+        toks.extend(range(j * C, min(n_tokens, (j + 1) * C, i + 1)))
+    toks = np.array(sorted(toks), dtype=np.int64)
+    logits = scale * (np.asarray(qg, dtype=np.float64) @ k[toks].T)  # [G, T]
+    o_lse = logsumexp(logits, axis=-1)
+    p = np.exp(logits - o_lse[:, None])
+    return p @ v[toks], o_lse
+
+
+# ----------------------------------------------------------------------------------------------
+# Flat block selection of ordinary block-sparse attention. [digest] 动机: it scores every
+# (query, key block) pair, O(N^2/C). Reading: one score per block, s * q . mu(leaf), summed over the
+# GQA heads; the Top-K order is the same as the walk's.
+# ----------------------------------------------------------------------------------------------
+def bsa_select_unit(qg: np.ndarray, leaf_means: np.ndarray, i: int, C: int, K: int, scale: float
+                    ) -> tuple[np.ndarray, float]:
+    n_elig = min(leaf_means.shape[0], i // C + 1)
+    cand = list(range(n_elig))
+    scores = np.array([float(np.sum(scale * (np.asarray(qg, dtype=np.float64) @ leaf_means[j]))) for j in cand])
+    sel = np.full(K, -1, dtype=np.int64)
+    if len(cand) <= K:
+        sel[:len(cand)] = cand
+        return sel, math.inf
+    order = _topk_order(cand, scores)
+    margin = scores[order[K - 1]] - scores[order[K]]
+    sel[:K] = sorted(cand[p] for p in order[:K])
+    return sel, margin
+
+
+# ----------------------------------------------------------------------------------------------
+# Brute-force flat exact Top-K (self-check only): the exact leaf LSE of every eligible leaf, taken
+# from one dense masked score row, then Top-K. When K is at least the level-1 node count the
+# pyramid walk must reproduce it.
+# ----------------------------------------------------------------------------------------------
+def flat_exact_select_unit(qg: np.ndarray, k: np.ndarray, i: int, C: int, K: int, scale: float
+                           ) -> tuple[np.ndarray, float]:
+    row = scale * (np.asarray(qg, dtype=np.float64) @ k[: i + 1].T)  # [G, i+1], the causal row
+    n_elig = i // C + 1
+    pad = n_elig * C - (i + 1)
+    padded = np.concatenate([row, np.full((row.shape[0], pad), NEG_INF)], axis=1)
+    F = logsumexp(padded.reshape(row.shape[0], n_elig, C), axis=-1).sum(axis=0)  # [n_elig]
+    cand = list(range(n_elig))
+    sel = np.full(K, -1, dtype=np.int64)
+    if n_elig <= K:
+        sel[:n_elig] = cand
+        return sel, math.inf
+    order = _topk_order(cand, F)
+    sel[:K] = sorted(order[:K])
+    return sel, F[order[K - 1]] - F[order[K]]
+
+
+# ----------------------------------------------------------------------------------------------
+# Decode. [digest] 工作参考价值 second bullet and 方法关键点 Kernel bullet: the decode step keeps a
+# cached mean pyramid and updates only the new token's ancestor path (amortised O(log N) per step).
+# Order: append the token at p = len, update its ancestors, then select and attend for query i = p.
+# ----------------------------------------------------------------------------------------------
+@dataclasses.dataclass
+class SumPyramid:
+    """Per-level node sums and token counts for capacity `n_max`, as a decode cache keeps them."""
+
+    sums: list[np.ndarray]
+    counts: list[np.ndarray]
+    C: int
+    g: int
+    n_max: int
+
+
+def empty_sum_pyramid(n_max: int, d: int, C: int, g: int = 2) -> SumPyramid:
+    sizes = level_sizes(n_max, C, g)
+    return SumPyramid(sums=[np.zeros((s, d)) for s in sizes], counts=[np.zeros(s) for s in sizes], C=C, g=g,
+                      n_max=n_max)
+
+
+def sum_pyramid_append(sp: SumPyramid, p: int, k_new: np.ndarray) -> None:
+    """Add the key of token p to the sum and count of every ancestor of its leaf."""
+    j = p // sp.C
+    for l in range(len(sp.sums)):
+        sp.sums[l][j] += k_new
+        sp.counts[l][j] += 1
+        j //= sp.g
+
+
+def sum_pyramid_means(sp: SumPyramid, n_tokens: int) -> Pyramid:
+    """The mean pyramid of the first n_tokens tokens, read off the sums (levels above the current root
+    are dropped)."""
+    sizes = level_sizes(n_tokens, sp.C, sp.g)
+    means, counts = [], []
+    for l, n_l in enumerate(sizes):
+        c = sp.counts[l][:n_l].copy()
+        m = sp.sums[l][:n_l] / np.where(c > 0, c, 1.0)[:, None]
+        means.append(m)
+        counts.append(c)
+    return Pyramid(means=means, counts=counts, C=sp.C, g=sp.g, n_tokens=n_tokens)
+
+
+def decode_step_unit(qg: np.ndarray, k_hist: np.ndarray, v_hist: np.ndarray, sp: SumPyramid, p: int,
+                     k_new: np.ndarray, v_new: np.ndarray, K: int, scale: float):
+    """One decode step of one unit. k_hist/v_hist hold at least p+1 rows; row p is overwritten with
+    the new token. Returns (UnitSelection, O [G, d], o_lse [G])."""
+    k_hist[p] = k_new
+    v_hist[p] = v_new
+    sum_pyramid_append(sp, p, k_new)
+    pyr = sum_pyramid_means(sp, p + 1)
+    us = select_unit(qg, k_hist, pyr, p, K, scale)
+    o, o_lse = attend_unit(qg, k_hist, v_hist, us.sel, p, sp.C, scale, p + 1)
+    return us, o, o_lse

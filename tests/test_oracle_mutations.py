@@ -1,0 +1,109 @@
+"""The oracle's pins are sensitive: each plausible mistake planted in the oracle (on the CPU, through
+monkeypatching) makes at least one pin check fail."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle as O
+from oracle import pisa_oracle as PO
+
+import test_oracle_pins as P
+
+
+def _pins_pass() -> bool:
+    checks = [
+        lambda: P.test_walk_equals_flat_exact_when_k_covers_level1(16),
+        lambda: P.test_walk_equals_dense_two_level_bruteforce(5, 2),
+        lambda: P.test_walk_monotone_keys_closed_form(+1, 1000),
+        lambda: P.test_walk_monotone_keys_closed_form(-1, 1000),
+        lambda: P.test_pyramid_recursive_equals_direct_span_mean(1000, 32),
+        lambda: P.test_attention_all_blocks_equals_dense_sdpa(),
+        lambda: P.test_selection_invariants(),
+        lambda: P.test_exact_ties_break_to_lowest_index(4),
+    ]
+    for c in checks:
+        try:
+            c()
+        except AssertionError:
+            return False
+    return True
+
+
+def test_unmutated_oracle_passes():
+    assert _pins_pass()
+
+
+def _mut_topk_ascending(cands, scores):
+    return sorted(range(len(cands)), key=lambda p: (scores[p], cands[p]))
+
+
+def _mut_tiebreak_high_index(cands, scores):
+    return sorted(range(len(cands)), key=lambda p: (-scores[p], -cands[p]))
+
+
+def _mut_leaf_no_causal_mask(qg, k, j, i, C, scale, n_tokens):
+    t0, t1 = j * C, min(n_tokens, (j + 1) * C)
+    return O.logsumexp(scale * (qg @ k[t0:t1].T), axis=-1)
+
+
+def _mut_node_uses_max(qg, pyr, l, j, i, scale):
+    kids = [c for c in PO.children(l, j, pyr) if PO.eligible(l - 1, c, i, pyr.C, pyr.g)]
+    return np.max(scale * (qg @ pyr.means[l - 1][kids].T), axis=-1)
+
+
+def _mut_node_ignores_eligibility(qg, pyr, l, j, i, scale):
+    kids = PO.children(l, j, pyr)
+    return O.logsumexp(scale * (qg @ pyr.means[l - 1][kids].T), axis=-1)
+
+
+def _mut_children_shifted(l, j, pyr):
+    n_prev = pyr.means[l - 1].shape[0]
+    return [c for c in range(j * pyr.g + 1, (j + 1) * pyr.g + 1) if c < n_prev]
+
+
+_orig_build = PO.build_pyramid
+
+
+def _mut_pyramid_sums(k, C, g=2, n_tokens=None):
+    p = _orig_build(k, C, g, n_tokens)
+    p.means = [m * c[:, None] for m, c in zip(p.means, p.counts)]
+    return p
+
+
+def _mut_pyramid_unweighted(k, C, g=2, n_tokens=None):
+    p = _orig_build(k, C, g, n_tokens)
+    for l in range(1, len(p.means)):
+        prev = p.means[l - 1]
+        for j in range(p.means[l].shape[0]):
+            kids = list(range(j * g, min((j + 1) * g, prev.shape[0])))
+            p.means[l][j] = prev[kids].mean(axis=0)
+    return p
+
+
+_orig_scale_attend = PO.attend_unit
+
+
+def _mut_attend_no_scale(qg, k, v, sel, i, C, scale, n_tokens):
+    return _orig_scale_attend(qg, k, v, sel, i, C, 1.0, n_tokens)
+
+
+MUTANTS = {
+    "topk_ascending": ("_topk_order", _mut_topk_ascending),
+    "tiebreak_high_index": ("_topk_order", _mut_tiebreak_high_index),
+    "leaf_no_causal_mask": ("leaf_lse_per_head", _mut_leaf_no_causal_mask),
+    "node_score_max": ("node_lse_per_head", _mut_node_uses_max),
+    "node_ignores_eligibility": ("node_lse_per_head", _mut_node_ignores_eligibility),
+    "children_off_by_one": ("children", _mut_children_shifted),
+    "pyramid_sums_not_means": ("build_pyramid", _mut_pyramid_sums),
+    "pyramid_unweighted_ragged": ("build_pyramid", _mut_pyramid_unweighted),
+    "attention_without_scale": ("attend_unit", _mut_attend_no_scale),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(PO, attr, fn)
+    monkeypatch.setattr(O, attr, fn, raising=False)
+    assert not _pins_pass(), f"mutant {name} survived every pin"
