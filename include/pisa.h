@@ -1,0 +1,153 @@
+/*
+ * pisa.h -- C ABI of libpisa.so: PISA pyramid Top-K block selection and block-sparse attention
+ * for AMD MI355X (gfx950).
+ *
+ * The method (pages cited by title and section):
+ *   "Block Sparse Attention with Log-Linear Complexity" (ai-papers-daily digest), section
+ *   方法关键点 (method key points): keys are cut into leaf blocks of C tokens and mean-pooled upward
+ *   with merge factor 2 into an O(log N) pyramid; each query walks coarse-to-fine from the root,
+ *   scores at most g*K candidates per level, keeps the Top-K and expands only their children; leaf
+ *   candidates are scored by the exact LogSumExp (LSE) over their raw keys, intermediate candidates
+ *   by the LSE over their children's mean keys; the query heads that share a KV head share one
+ *   selection, whose score is the sum of their per-head LSEs (section 工作参考价值, third bullet).
+ *   Attention then runs over the selected leaf blocks only ("PISA：log-linear 复杂度的金字塔稀疏
+ *   注意力" explainer, 核心方法 §7). The decode step keeps a cached mean pyramid, updates only the
+ *   new token's ancestor path and runs every level in one kernel (digest, 工作参考价值 second
+ *   bullet). bsa_select is the flat block selection of ordinary block-sparse attention that scores
+ *   every (query, block) pair (digest, 动机).
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers (HIP device memory), contiguous, 16-byte aligned.
+ *     host_lens is a HOST pointer. `stream` is a hipStream_t (NULL = the default stream).
+ *   - Layouts (head-major): Q and O are [B, Hq, N, d]; K and V are [B, Hkv, N, d]. Query heads
+ *     r*G .. r*G+G-1 (G = Hq/Hkv) share KV head r. A "unit" is (b, r, i): one KV head at one
+ *     query position; its G query heads share one selection.
+ *   - Element type of Q, K, V, O is pisa_shape.dtype (IEEE fp32 or bfloat16). Pyramids and LSEs
+ *     are fp32. Leaf indices are int32.
+ *   - Causal: a node is eligible for query i iff its first token is <= i; leaf scores and
+ *     attention mask tokens t > i.
+ *   - Selections are ascending leaf indices padded with -1 to K. Top-K order is score descending,
+ *     then node index ascending (ties go to the lower index).
+ *   - Ownership: the caller allocates every buffer, including the workspace (sized by
+ *     pisa_workspace_size). The library never allocates, frees or synchronises; every call only
+ *     enqueues work on `stream` and returns. Inputs are read-only; outputs are fully overwritten.
+ *   - Errors: a negative pisa_status. Arguments are validated before anything is enqueued, so an
+ *     error leaves every output untouched. A failed launch returns PISA_EHIP. pisa_last_error()
+ *     gives a thread-local message for the last non-OK return. Calls are reentrant.
+ */
+#ifndef PISA_H_
+#define PISA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PISA_OK = 0,
+  PISA_EINVAL = -1,       /* bad argument: null pointer, negative size, inconsistent shape */
+  PISA_EUNSUPPORTED = -2, /* valid but not supported by these kernels (see pisa_shape limits) */
+  PISA_EWORKSPACE = -3,   /* workspace missing or smaller than pisa_workspace_size() */
+  PISA_EHIP = -4          /* a HIP launch failed */
+} pisa_status;
+
+typedef enum { PISA_FP32 = 0, PISA_BF16 = 1 } pisa_dtype;
+
+/* Operation codes for pisa_workspace_size. */
+enum { PISA_OP_SELECT = 1, PISA_OP_ATTN = 2, PISA_OP_DECODE = 3, PISA_OP_BSA = 4 };
+
+/* Problem shape, passed by pointer to every call.
+ * Limits of these kernels (PISA_EUNSUPPORTED otherwise): head_dim in {64, 128}; block C in
+ * {32, 64}; 1 <= top_k <= 32; branch (merge factor g) == 2; G = Hq/Hkv in {1, 2, 4, 8, 16};
+ * q_tile in {1, 2, 4, 8, 16} with q_tile*G <= 16 (q_tile > 1 groups q_tile units that share a
+ * candidate block into one matrix tile; q_tile == 1 walks each unit to its leaves directly);
+ * units B*Hkv*seq_len < 2^27. */
+typedef struct {
+  int32_t batch;      /* B */
+  int32_t seq_len;    /* N: tokens (prefill), or the cache capacity Nmax (decode)          */
+  int32_t n_q_heads;  /* Hq                                                                */
+  int32_t n_kv_heads; /* Hkv, divides Hq                                                   */
+  int32_t head_dim;   /* d                                                                 */
+  int32_t block;      /* C: tokens per leaf block                                          */
+  int32_t top_k;      /* K: nodes kept per level                                           */
+  int32_t branch;     /* g: merge factor of the pyramid                                    */
+  int32_t q_tile;     /* units per matrix tile in the leaf stage (see above)               */
+  float scale;        /* score scale s; 0 means 1/sqrt(d)                                  */
+  int32_t dtype;      /* pisa_dtype of Q, K, V, O                                          */
+} pisa_shape;
+
+/* Pyramid layout for a shape (host only, enqueues nothing). Level l has n_l = ceil(n_{l-1}/2)
+ * nodes, n_0 = ceil(seq_len / C), up to a single root; levels are stored leaf-first, so node
+ * (l, j) of head (b, r) is row ((b*Hkv + r) * nodes_per_head + level_offset[l] + j) of a
+ * [B*Hkv*nodes_per_head, d] fp32 array. n_levels counts the root. level_offset has room for 32
+ * entries. */
+pisa_status pisa_pyramid_layout(const pisa_shape* shape, int32_t* n_levels, int64_t* level_offset,
+                                int64_t* nodes_per_head);
+
+/* Workspace bytes needed by an operation (host only). 0 is a valid answer. */
+pisa_status pisa_workspace_size(const pisa_shape* shape, int32_t op, size_t* bytes);
+
+/* Mean-pooled key pyramid (digest 方法关键点, pyramid bullet; explainer 核心方法 §1).
+ *   k         [B, Hkv, N, d] keys (dtype).
+ *   host_lens NULL: every sequence holds N tokens. Else a host array of B lengths (0 <= len <= N,
+ *             B <= 256): tokens at positions >= len are ignored (a decode cache holding len tokens).
+ *   pyr_mean  out, fp32 pyramid (pisa_pyramid_layout): node mean = mean of the keys present in the
+ *             node's span; nodes holding no token get 0.
+ *   pyr_sum   out, nullable, same layout: per-node key sums, needed by pisa_decode_step. */
+pisa_status pisa_build_pyramid(const pisa_shape* shape, const void* k, const int32_t* host_lens, float* pyr_mean,
+                               float* pyr_sum, void* stream);
+
+/* Pyramid Top-K selection with LSE scoring (digest 方法关键点, pyramid / scoring / complexity
+ * bullets; abstract). For each unit (b, r, i): walk from the root; at level l the candidates are the
+ * eligible children of the nodes kept at level l+1; a level with more than K candidates scores each
+ * candidate c as sum over the group's heads h of LSE over c's eligible children c' of
+ * s * q_{h,i} . mean(c') (levels >= 1), or of s * q_{h,i} . k_t over the leaf's tokens t <= i (leaf
+ * level), and keeps the Top-K; a level with at most K candidates keeps them all.
+ *   q        [B, Hq, N, d]; k [B, Hkv, N, d]; pyr_mean from pisa_build_pyramid (host_lens NULL).
+ *   sel      out int32 [B, Hkv, N, K]: selected leaves, ascending, -1 padded.
+ *   sel_lse  out, nullable, fp32 [B, Hq, N, K]: per-head leaf LSE of each selected leaf
+ *            (-inf where sel is -1).
+ *   ws       workspace of at least pisa_workspace_size(shape, PISA_OP_SELECT) bytes. */
+pisa_status pisa_select(const pisa_shape* shape, const void* q, const void* k, const float* pyr_mean, int32_t* sel,
+                        float* sel_lse, void* ws, size_t ws_bytes, void* stream);
+
+/* Block-sparse attention over the selected leaves (explainer 核心方法 §7, last step). For each
+ * (b, h, i): O = sum over t in T of softmax_t(s * q_{h,i} . k_t) v_t, T = the tokens t <= i of the
+ * leaves in sel[b, h/G, i, :]; the softmax normalises over T only.
+ *   sel      int32 [B, Hkv, N, K] as written by pisa_select (or bsa_select): each row ascending
+ *            leaves j with j*C <= i, -1 padded, at least one entry.
+ *   o        out [B, Hq, N, d] (dtype). o_lse out, nullable, fp32 [B, Hq, N]: LSE over T. */
+pisa_status pisa_sparse_attn(const pisa_shape* shape, const void* q, const void* k, const void* v, const int32_t* sel,
+                             void* o, float* o_lse, void* ws, size_t ws_bytes, void* stream);
+
+/* One fused decode step (digest 工作参考价值 second bullet; 方法关键点 Kernel bullet). For every
+ * sequence b with p = host_lens[b] tokens cached (shape.seq_len = capacity Nmax, p < Nmax): append
+ * k_new/v_new at position p; add k_new to the sum of each ancestor of leaf p/C in pyr_sum and
+ * refresh those nodes' means in pyr_mean; then run the pisa_select walk and pisa_sparse_attn for
+ * query position i = p over the p+1 cached tokens. One kernel launch does all of it. The caller
+ * advances host_lens afterwards.
+ *   q_new [B, Hq, d]; k_new, v_new [B, Hkv, d]; k_cache, v_cache [B, Hkv, Nmax, d] (updated);
+ *   pyr_sum, pyr_mean: the decode pyramid (layout of shape), initialised by pisa_build_pyramid with
+ *   pyr_sum set and host_lens = the cached lengths; o out [B, Hq, d]; sel_out out, nullable, int32
+ *   [B, Hkv, K]. ws may be NULL when pisa_workspace_size(PISA_OP_DECODE) is 0. */
+pisa_status pisa_decode_step(const pisa_shape* shape, const int32_t* host_lens, const void* q_new, const void* k_new,
+                             const void* v_new, void* k_cache, void* v_cache, float* pyr_sum, float* pyr_mean, void* o,
+                             int32_t* sel_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Flat block selection of ordinary block-sparse attention, for comparison (digest 动机: every
+ * (query, key block) pair is scored, O(N^2/C)). Per unit, each eligible leaf j gets
+ * B(j) = sum over the group's heads of s * q_{h,i} . mean(leaf j), and the Top-K leaves are kept.
+ * The leaf means are pooled inside the call (in the workspace).
+ *   sel out int32 [B, Hkv, N, K] ascending, -1 padded. */
+pisa_status bsa_select(const pisa_shape* shape, const void* q, const void* k, int32_t* sel, void* ws, size_t ws_bytes,
+                       void* stream);
+
+const char* pisa_status_string(pisa_status status);
+const char* pisa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PISA_H_ */

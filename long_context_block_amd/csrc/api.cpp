@@ -1,0 +1,421 @@
+// C ABI of libpisa.so: argument validation, workspace layout and launch sequencing.
+// Validation completes before anything is enqueued; the kernels live in the .hip files.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/pisa.h"
+#include "internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pisa_status fail(pisa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+pisa_status ok() {
+  g_last_error.clear();
+  return PISA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define PISA_CHECK_PTR(p, name)                                                     \
+  do {                                                                              \
+    if (!(p)) return fail(PISA_EINVAL, "%s: null pointer", name);                   \
+    if (!aligned16(p)) return fail(PISA_EINVAL, "%s: not 16-byte aligned", name);   \
+  } while (0)
+
+#define PISA_CHECK_OPT_PTR(p, name)                                                  \
+  do {                                                                              \
+    if ((p) && !aligned16(p)) return fail(PISA_EINVAL, "%s: not 16-byte aligned", name); \
+  } while (0)
+
+struct Plan {
+  pisa::SelDims sd;
+  long long U;       // units B*Hkv*N
+  long long BH;
+  int n1_buckets;    // buckets per KV head for the selection regroup (level-1 nodes, at least 1)
+  size_t elem;       // bytes per Q/K/V element
+};
+
+pisa_status make_levels(long long n_tokens, int C, pisa::Levels* lv) {
+  std::memset(lv, 0, sizeof(*lv));
+  long long n = (n_tokens + C - 1) / C;
+  if (n < 1) n = 1;
+  int l = 0;
+  long long off = 0;
+  while (true) {
+    if (l >= pisa::kMaxLevels) return fail(PISA_EUNSUPPORTED, "pyramid deeper than %d levels", pisa::kMaxLevels);
+    if (n > 0x7fffffffLL) return fail(PISA_EUNSUPPORTED, "too many leaves");
+    lv->n[l] = (int)n;
+    lv->off[l] = off;
+    off += n;
+    ++l;
+    if (n == 1) break;
+    n = (n + 1) / 2;
+  }
+  lv->n_levels = l;
+  lv->nodes = off;
+  return PISA_OK;
+}
+
+pisa_status plan(const pisa_shape* s, Plan* pl) {
+  if (!s) return fail(PISA_EINVAL, "shape: null pointer");
+  if (s->batch < 1 || s->seq_len < 1 || s->n_q_heads < 1 || s->n_kv_heads < 1)
+    return fail(PISA_EINVAL, "batch, seq_len and head counts must be >= 1");
+  if (s->n_q_heads % s->n_kv_heads) return fail(PISA_EINVAL, "n_q_heads %% n_kv_heads != 0");
+  const int G = s->n_q_heads / s->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
+    return fail(PISA_EUNSUPPORTED, "query heads per KV head must be 1, 2, 4, 8 or 16 (got %d)", G);
+  if (s->head_dim != 64 && s->head_dim != 128) return fail(PISA_EUNSUPPORTED, "head_dim must be 64 or 128");
+  if (s->block != 32 && s->block != 64) return fail(PISA_EUNSUPPORTED, "block must be 32 or 64");
+  if (s->top_k < 1) return fail(PISA_EINVAL, "top_k must be >= 1");
+  if (s->top_k > 32) return fail(PISA_EUNSUPPORTED, "top_k must be <= 32");
+  if (s->branch != 2) return fail(PISA_EUNSUPPORTED, "branch (merge factor) must be 2");
+  const int qt = s->q_tile;
+  if (qt != 1 && qt != 2 && qt != 4 && qt != 8 && qt != 16) return fail(PISA_EINVAL, "q_tile must be 1, 2, 4, 8 or 16");
+  if (qt * G > 16) return fail(PISA_EUNSUPPORTED, "q_tile * G must be <= 16");
+  if (s->dtype != PISA_FP32 && s->dtype != PISA_BF16) return fail(PISA_EINVAL, "dtype must be PISA_FP32 or PISA_BF16");
+  if (!(s->scale >= 0.f) || !std::isfinite(s->scale)) return fail(PISA_EINVAL, "scale must be finite and >= 0");
+  const long long U = (long long)s->batch * s->n_kv_heads * s->seq_len;
+  if (U >= (1LL << 27)) return fail(PISA_EUNSUPPORTED, "batch * n_kv_heads * seq_len must be < 2^27");
+  if (U * s->top_k >= (1LL << 31)) return fail(PISA_EUNSUPPORTED, "units * top_k must be < 2^31");
+  Plan p{};
+  p.sd.B = s->batch;
+  p.sd.Hq = s->n_q_heads;
+  p.sd.Hkv = s->n_kv_heads;
+  p.sd.G = G;
+  p.sd.N = s->seq_len;
+  p.sd.D = s->head_dim;
+  p.sd.C = s->block;
+  p.sd.K = s->top_k;
+  p.sd.q_tile = qt;
+  p.sd.scale = s->scale > 0.f ? s->scale : 1.f / std::sqrt((float)s->head_dim);
+  p.sd.bf16 = s->dtype == PISA_BF16;
+  pisa_status st = make_levels(s->seq_len, s->block, &p.sd.lv);
+  if (st != PISA_OK) return st;
+  p.U = U;
+  p.BH = (long long)s->batch * s->n_kv_heads;
+  p.n1_buckets = p.sd.lv.n_levels > 1 ? p.sd.lv.n[1] : 1;
+  p.elem = p.sd.bf16 ? 2 : 4;
+  *pl = p;
+  return PISA_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace carving: a list of (pointer, bytes) regions, each 256-byte aligned.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base((char*)b) {}
+  void* take(size_t bytes) {
+    void* p = base ? base + off : nullptr;
+    off += align256(bytes);
+    return p;
+  }
+};
+
+struct SelectWs {
+  uint16_t* hilo;
+  int* kept;
+  int* counts;
+  int* offsets;
+  int* ranks;
+  uint32_t* pairs;
+  float* leaf_lse;
+};
+
+size_t carve_select(const Plan& p, void* ws, SelectWs* w) {
+  Carver c(ws);
+  SelectWs x{};
+  if (p.sd.bf16) x.hilo = (uint16_t*)c.take((size_t)p.BH * p.sd.lv.nodes * 2 * p.sd.D * 2);
+  if (p.sd.q_tile > 1) {
+    const size_t pairs = (size_t)p.U * p.sd.K;
+    const size_t NB = (size_t)p.BH * p.n1_buckets;
+    x.kept = (int*)c.take(pairs * 4);
+    x.counts = (int*)c.take(NB * 4);
+    x.offsets = (int*)c.take((NB + 1) * 4);
+    x.ranks = (int*)c.take(pairs * 4);
+    x.pairs = (uint32_t*)c.take(pairs * 4);
+    x.leaf_lse = (float*)c.take(pairs * 2 * p.sd.G * 4);
+  }
+  if (w) *w = x;
+  return c.off;
+}
+
+struct AttnWs {
+  int* counts;
+  int* offsets;
+  int* ranks;
+  uint32_t* pairs;
+  void* part;
+  float* part_lse;
+};
+
+size_t carve_attn(const Plan& p, void* ws, AttnWs* w) {
+  Carver c(ws);
+  AttnWs x{};
+  const size_t pairs = (size_t)p.U * p.sd.K;
+  const size_t NB = (size_t)p.BH * p.sd.lv.n[0];
+  x.counts = (int*)c.take(NB * 4);
+  x.offsets = (int*)c.take((NB + 1) * 4);
+  x.ranks = (int*)c.take(pairs * 4);
+  x.pairs = (uint32_t*)c.take(pairs * 4);
+  x.part = c.take(pairs * p.sd.G * p.sd.D * p.elem);
+  x.part_lse = (float*)c.take(pairs * p.sd.G * 4);
+  if (w) *w = x;
+  return c.off;
+}
+
+struct BsaWs {
+  float* mean;
+  uint16_t* hilo;
+};
+
+size_t carve_bsa(const Plan& p, void* ws, BsaWs* w) {
+  Carver c(ws);
+  BsaWs x{};
+  const size_t rows = (size_t)p.BH * p.sd.lv.n[0];
+  x.mean = (float*)c.take(rows * p.sd.D * 4);
+  if (p.sd.bf16) x.hilo = (uint16_t*)c.take(rows * 2 * p.sd.D * 2);
+  if (w) *w = x;
+  return c.off;
+}
+
+pisa_status check_ws(size_t need, const void* ws, size_t ws_bytes) {
+  if (need == 0) return PISA_OK;
+  if (!ws) return fail(PISA_EWORKSPACE, "workspace is null, %zu bytes needed", need);
+  if (!aligned16(ws)) return fail(PISA_EINVAL, "workspace: not 16-byte aligned");
+  if (ws_bytes < need) return fail(PISA_EWORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, need);
+  return PISA_OK;
+}
+
+pisa_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(PISA_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+pisa_status lens_arg(const int32_t* host_lens, int B, int Hkv, int lo, int hi_incl, pisa::LensArg* la) {
+  std::memset(la, 0, sizeof(*la));
+  la->hkv = Hkv;
+  if (!host_lens) return PISA_OK;
+  if (B > pisa::kMaxLensBatch) return fail(PISA_EUNSUPPORTED, "host_lens supports batch <= %d", pisa::kMaxLensBatch);
+  la->has = 1;
+  for (int b = 0; b < B; ++b) {
+    if (host_lens[b] < lo || host_lens[b] > hi_incl)
+      return fail(PISA_EINVAL, "host_lens[%d] = %d outside [%d, %d]", b, host_lens[b], lo, hi_incl);
+    la->len[b] = host_lens[b];
+  }
+  return PISA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pisa_status_string(pisa_status s) {
+  switch (s) {
+    case PISA_OK: return "PISA_OK";
+    case PISA_EINVAL: return "PISA_EINVAL: invalid argument";
+    case PISA_EUNSUPPORTED: return "PISA_EUNSUPPORTED: unsupported shape";
+    case PISA_EWORKSPACE: return "PISA_EWORKSPACE: workspace missing or too small";
+    case PISA_EHIP: return "PISA_EHIP: HIP launch failed";
+  }
+  return "unknown pisa_status";
+}
+
+const char* pisa_last_error(void) { return g_last_error.c_str(); }
+
+pisa_status pisa_pyramid_layout(const pisa_shape* shape, int32_t* n_levels, int64_t* level_offset,
+                                int64_t* nodes_per_head) {
+  Plan p;
+  pisa_status st = plan(shape, &p);
+  if (st != PISA_OK) return st;
+  if (n_levels) *n_levels = p.sd.lv.n_levels;
+  if (level_offset)
+    for (int l = 0; l < pisa::kMaxLevels; ++l) level_offset[l] = l < p.sd.lv.n_levels ? p.sd.lv.off[l] : -1;
+  if (nodes_per_head) *nodes_per_head = p.sd.lv.nodes;
+  return ok();
+}
+
+pisa_status pisa_workspace_size(const pisa_shape* shape, int32_t op, size_t* bytes) {
+  if (!bytes) return fail(PISA_EINVAL, "bytes: null pointer");
+  Plan p;
+  pisa_status st = plan(shape, &p);
+  if (st != PISA_OK) return st;
+  switch (op) {
+    case PISA_OP_SELECT: *bytes = carve_select(p, nullptr, nullptr); break;
+    case PISA_OP_ATTN: *bytes = carve_attn(p, nullptr, nullptr); break;
+    case PISA_OP_DECODE: *bytes = 0; break;
+    case PISA_OP_BSA: *bytes = carve_bsa(p, nullptr, nullptr); break;
+    default: return fail(PISA_EINVAL, "unknown op %d", op);
+  }
+  return ok();
+}
+
+pisa_status pisa_build_pyramid(const pisa_shape* shape, const void* k, const int32_t* host_lens, float* pyr_mean,
+                               float* pyr_sum, void* stream) {
+  Plan p;
+  pisa_status st = plan(shape, &p);
+  if (st != PISA_OK) return st;
+  PISA_CHECK_PTR(k, "k");
+  PISA_CHECK_PTR(pyr_mean, "pyr_mean");
+  PISA_CHECK_OPT_PTR(pyr_sum, "pyr_sum");
+  pisa::LensArg la;
+  st = lens_arg(host_lens, p.sd.B, p.sd.Hkv, 0, p.sd.N, &la);
+  if (st != PISA_OK) return st;
+  pisa::PyrDims pd{(int)p.BH, p.sd.N, p.sd.C, p.sd.D, p.sd.lv};
+  return hip_status(pisa::launch_pool(k, p.sd.bf16, pd, la, p.sd.lv.n_levels - 1, pyr_mean, pyr_sum,
+                                      (hipStream_t)stream),
+                    "pisa_build_pyramid");
+}
+
+pisa_status pisa_select(const pisa_shape* shape, const void* q, const void* k, const float* pyr_mean, int32_t* sel,
+                        float* sel_lse, void* ws, size_t ws_bytes, void* stream) {
+  Plan p;
+  pisa_status st = plan(shape, &p);
+  if (st != PISA_OK) return st;
+  PISA_CHECK_PTR(q, "q");
+  PISA_CHECK_PTR(k, "k");
+  PISA_CHECK_PTR(pyr_mean, "pyr_mean");
+  PISA_CHECK_PTR(sel, "sel");
+  PISA_CHECK_OPT_PTR(sel_lse, "sel_lse");
+  const size_t need = carve_select(p, nullptr, nullptr);
+  st = check_ws(need, ws, ws_bytes);
+  if (st != PISA_OK) return st;
+  SelectWs w;
+  carve_select(p, ws, &w);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  const void* nodes = pyr_mean;
+  if (p.sd.bf16) {
+    e = pisa::launch_split_hilo(pyr_mean, p.BH * p.sd.lv.nodes, p.sd.D, w.hilo, s);
+    if (e != hipSuccess) return hip_status(e, "split_hilo");
+    nodes = w.hilo;
+  }
+  if (p.sd.q_tile == 1) {
+    e = pisa::launch_route(p.sd, q, k, nodes, true, nullptr, sel, sel_lse, s);
+    return hip_status(e, "route (fused leaf stage)");
+  }
+  e = pisa::launch_route(p.sd, q, k, nodes, false, w.kept, nullptr, nullptr, s);
+  if (e != hipSuccess) return hip_status(e, "route");
+  e = pisa::launch_regroup(w.kept, p.U, p.sd.K, p.sd.N, p.n1_buckets, (int)p.BH, w.counts, w.offsets, w.ranks,
+                           w.pairs, s);
+  if (e != hipSuccess) return hip_status(e, "regroup");
+  const int* total = w.offsets + p.BH * p.n1_buckets;
+  e = pisa::launch_leaf_lse(p.sd, q, k, w.kept, w.pairs, total, w.leaf_lse, s);
+  if (e != hipSuccess) return hip_status(e, "leaf_lse");
+  e = pisa::launch_finalize(p.sd, w.kept, w.leaf_lse, sel, sel_lse, s);
+  return hip_status(e, "finalize");
+}
+
+pisa_status pisa_sparse_attn(const pisa_shape* shape, const void* q, const void* k, const void* v, const int32_t* sel,
+                             void* o, float* o_lse, void* ws, size_t ws_bytes, void* stream) {
+  Plan p;
+  pisa_status st = plan(shape, &p);
+  if (st != PISA_OK) return st;
+  PISA_CHECK_PTR(q, "q");
+  PISA_CHECK_PTR(k, "k");
+  PISA_CHECK_PTR(v, "v");
+  PISA_CHECK_PTR(sel, "sel");
+  PISA_CHECK_PTR(o, "o");
+  PISA_CHECK_OPT_PTR(o_lse, "o_lse");
+  const size_t need = carve_attn(p, nullptr, nullptr);
+  st = check_ws(need, ws, ws_bytes);
+  if (st != PISA_OK) return st;
+  AttnWs w;
+  carve_attn(p, ws, &w);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = pisa::launch_regroup(sel, p.U, p.sd.K, p.sd.N, p.sd.lv.n[0], (int)p.BH, w.counts, w.offsets, w.ranks,
+                                      w.pairs, s);
+  if (e != hipSuccess) return hip_status(e, "regroup");
+  const int* total = w.offsets + p.BH * p.sd.lv.n[0];
+  e = pisa::launch_attn_leaf(p.sd, q, k, v, sel, w.pairs, total, w.part, w.part_lse, s);
+  if (e != hipSuccess) return hip_status(e, "attn_leaf");
+  e = pisa::launch_attn_merge(p.sd, sel, w.part, w.part_lse, o, o_lse, s);
+  return hip_status(e, "attn_merge");
+}
+
+pisa_status pisa_decode_step(const pisa_shape* shape, const int32_t* host_lens, const void* q_new, const void* k_new,
+                             const void* v_new, void* k_cache, void* v_cache, float* pyr_sum, float* pyr_mean, void* o,
+                             int32_t* sel_out, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  Plan p;
+  pisa_status st = plan(shape, &p);
+  if (st != PISA_OK) return st;
+  if (!host_lens) return fail(PISA_EINVAL, "host_lens: null pointer");
+  PISA_CHECK_PTR(q_new, "q_new");
+  PISA_CHECK_PTR(k_new, "k_new");
+  PISA_CHECK_PTR(v_new, "v_new");
+  PISA_CHECK_PTR(k_cache, "k_cache");
+  PISA_CHECK_PTR(v_cache, "v_cache");
+  PISA_CHECK_PTR(pyr_sum, "pyr_sum");
+  PISA_CHECK_PTR(pyr_mean, "pyr_mean");
+  PISA_CHECK_PTR(o, "o");
+  PISA_CHECK_OPT_PTR(sel_out, "sel_out");
+  pisa::DecodeArgs da{};
+  st = lens_arg(host_lens, p.sd.B, p.sd.Hkv, 0, p.sd.N - 1, &da.lens);
+  if (st != PISA_OK) return st;
+  da.B = p.sd.B;
+  da.Hq = p.sd.Hq;
+  da.Hkv = p.sd.Hkv;
+  da.G = p.sd.G;
+  da.Nmax = p.sd.N;
+  da.D = p.sd.D;
+  da.C = p.sd.C;
+  da.K = p.sd.K;
+  da.scale = p.sd.scale;
+  da.bf16 = p.sd.bf16;
+  da.lv = p.sd.lv;
+  return hip_status(pisa::launch_decode(da, q_new, k_new, v_new, k_cache, v_cache, pyr_sum, pyr_mean, o, sel_out,
+                                        (hipStream_t)stream),
+                    "decode_step");
+}
+
+pisa_status bsa_select(const pisa_shape* shape, const void* q, const void* k, int32_t* sel, void* ws, size_t ws_bytes,
+                       void* stream) {
+  Plan p;
+  pisa_status st = plan(shape, &p);
+  if (st != PISA_OK) return st;
+  PISA_CHECK_PTR(q, "q");
+  PISA_CHECK_PTR(k, "k");
+  PISA_CHECK_PTR(sel, "sel");
+  const size_t need = carve_bsa(p, nullptr, nullptr);
+  st = check_ws(need, ws, ws_bytes);
+  if (st != PISA_OK) return st;
+  BsaWs w;
+  carve_bsa(p, ws, &w);
+  hipStream_t s = (hipStream_t)stream;
+  pisa::LensArg la;
+  std::memset(&la, 0, sizeof la);
+  la.hkv = p.sd.Hkv;
+  // leaf means only: the leaf level is the whole pyramid the flat selection needs
+  pisa::PyrDims pd{(int)p.BH, p.sd.N, p.sd.C, p.sd.D, p.sd.lv};
+  pd.lv.n_levels = 1;
+  pd.lv.nodes = p.sd.lv.n[0];
+  hipError_t e = pisa::launch_pool(k, p.sd.bf16, pd, la, 0, w.mean, nullptr, s);
+  if (e != hipSuccess) return hip_status(e, "bsa leaf pooling");
+  if (p.sd.bf16) {
+    e = pisa::launch_split_hilo(w.mean, p.BH * p.sd.lv.n[0], p.sd.D, w.hilo, s);
+    if (e != hipSuccess) return hip_status(e, "bsa split");
+  }
+  e = pisa::launch_bsa(p.sd, q, w.mean, w.hilo, sel, s);
+  return hip_status(e, "bsa_select");
+}
+
+}  // extern "C"

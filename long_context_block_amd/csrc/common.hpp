@@ -1,0 +1,183 @@
+// Shared device helpers for the PISA kernels (gfx950 / CDNA4, wave64).
+//
+// Matrix tiles use v_mfma_f32_16x16x32_bf16 (bf16 inputs, fp32 accumulate) or, for fp32 inputs,
+// eight v_mfma_f32_16x16x4_f32 per 32-wide k step. Per lane: A row = B column = lane % 16, lane group
+// g = lane / 16 supplies 8 consecutive k elements of the step; the D tile gives lane (col = lane % 16,
+// g) the rows 4g .. 4g+3. Each k step here covers d elements [(d/4) g + 8 s, +8) of lane group g, so
+// a lane reads 64 (or 32) contiguous bytes of a row across the steps.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pisa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr int kMaxLevels = 32;
+
+// Pyramid layout of one KV head: level sizes and leaf-first offsets (rows of d floats).
+struct Levels {
+  int n_levels;  // including the root
+  int n[kMaxLevels];
+  long long off[kMaxLevels];
+  long long nodes;  // rows per KV head
+};
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t x) { return __uint_as_float(((uint32_t)x) << 16); }
+
+// fp32 -> bf16, round to nearest, ties to even.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;  // NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <typename T>
+__device__ __forceinline__ float to_f32(T x);
+template <>
+__device__ __forceinline__ float to_f32<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ float to_f32<uint16_t>(uint16_t x) { return bf16_to_f32(x); }
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float x);
+template <>
+__device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ uint16_t from_f32<uint16_t>(float x) { return f32_to_bf16(x); }
+
+// 8 consecutive k elements of one lane.
+template <typename T>
+struct Frag;
+
+template <>
+struct Frag<uint16_t> {
+  uint4 u;
+  __device__ __forceinline__ void zero() { u = make_uint4(0u, 0u, 0u, 0u); }
+  __device__ __forceinline__ void load(const uint16_t* p) { u = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ float get(int e) const {
+    uint32_t w = e < 2 ? u.x : e < 4 ? u.y : e < 6 ? u.z : u.w;
+    return bf16_to_f32((uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu)));
+  }
+};
+
+template <>
+struct Frag<float> {
+  float4 a, b;
+  __device__ __forceinline__ void zero() {
+    a = make_float4(0.f, 0.f, 0.f, 0.f);
+    b = a;
+  }
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const float4*>(p);
+    b = *reinterpret_cast<const float4*>(p + 4);
+  }
+};
+
+__device__ __forceinline__ void mma(f32x4& acc, const Frag<uint16_t>& a, const Frag<uint16_t>& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a.u), __builtin_bit_cast(bf16x8_t, b.u),
+                                                acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ void mma(f32x4& acc, const Frag<float>& a, const Frag<float>& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.a.x, b.a.x, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.a.y, b.a.y, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.a.z, b.a.z, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.a.w, b.a.w, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.b.x, b.b.x, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.b.y, b.b.y, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.b.z, b.b.z, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.b.w, b.b.w, acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Max / sum over the 4 lane groups that hold one tile column (lanes c, c+16, c+32, c+48).
+// Every lane of the column ends with the same, order-fixed result.
+__device__ __forceinline__ float colgroup_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  return fmaxf(v, __shfl_xor(v, 32));
+}
+__device__ __forceinline__ float colgroup_sum(float v) {
+  v += __shfl_xor(v, 16);
+  return v + __shfl_xor(v, 32);
+}
+
+// LSE of scale * x over the NV values this lane holds for a column plus those of the column's
+// other 3 lane groups. Invalid entries are -inf. Returns -inf if all are invalid.
+template <int NV>
+__device__ __forceinline__ float column_lse(const float (&x)[NV], float scale) {
+  float m = x[0];
+#pragma unroll
+  for (int j = 1; j < NV; ++j) m = fmaxf(m, x[j]);
+  m = colgroup_max(m);
+  const bool any = m != kNegInf;
+  const float ms = any ? m : 0.f;
+  const float c = scale * kLog2e;
+  float acc = 0.f;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) acc += fast_exp2((x[j] - ms) * c);
+  acc = colgroup_sum(acc);
+  return any ? scale * ms + kLn2 * fast_log2(acc) : kNegInf;
+}
+
+// LSE of two already-scaled values.
+__device__ __forceinline__ float lse2(float a, float b) {
+  const float m = fmaxf(a, b);
+  const float d = fminf(a, b) - m;
+  return m + kLn2 * fast_log2(1.f + fast_exp2(d * kLog2e));
+}
+
+// Lanes [0, n) hold candidates in ascending node order with their scores. True for the lanes among
+// the K best by (score descending, node ascending). n and K are wave-uniform.
+__device__ __forceinline__ bool topk_keep(float score, int n, int K) {
+  const int lane = lane_id();
+  int rank = 0;
+  for (int c = 0; c < n; ++c) {
+    const float sc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(score), c));
+    rank += (sc > score) || (sc == score && c < lane);
+  }
+  return lane < n && rank < K;
+}
+
+// Stable compaction: lanes with keep move to [0, count) in lane order, the others after them.
+// Returns the value that lands on this lane.
+__device__ __forceinline__ int compact_lanes(bool keep, int value, int* count) {
+  const int lane = lane_id();
+  const unsigned long long m = __ballot(keep);
+  const unsigned long long below = lane ? (m & ((~0ull) >> (64 - lane))) : 0ull;
+  const int pos = __popcll(below);
+  const int total = __popcll(m);
+  const int dst = keep ? pos : total + (lane - pos);
+  *count = total;
+  return __builtin_amdgcn_ds_permute(dst << 2, value);
+}
+
+// Wave-uniform read of lane c.
+__device__ __forceinline__ int readlane(int v, int c) { return __builtin_amdgcn_readlane(v, c); }
+__device__ __forceinline__ float readlane(float v, int c) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), c));
+}
+
+// Work-group index remapped so that consecutive logical indices run on the same XCD (dispatch
+// places work-group w on XCD w % 8), keeping each XCD's L2 on a contiguous slice of the work.
+__device__ __forceinline__ int xcd_logical_block(int nblocks) {
+  const int w = blockIdx.x;
+  const int per = (nblocks + 7) >> 3;
+  const int xcd = w & 7;
+  const int idx = w >> 3;
+  const int full = nblocks & 7 ? (nblocks & 7) : 8;  // XCDs that get `per` blocks
+  return xcd < full ? xcd * per + idx : full * per + (xcd - full) * (per - 1) + idx;
+}
+
+}  // namespace pisa

@@ -1,0 +1,73 @@
+// Internal launcher declarations shared by the C ABI (api.cpp) and the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace pisa {
+
+constexpr int kMaxLensBatch = 256;
+
+// Per-sequence token counts, passed by value in the kernel arguments.
+struct LensArg {
+  int has;  // 0: every sequence holds N tokens
+  int hkv;  // KV heads (to map a (b, r) row to b)
+  int len[kMaxLensBatch];
+};
+
+struct PyrDims {
+  int BH;  // B * Hkv
+  int N;   // tokens per sequence (or capacity)
+  int C;
+  int D;
+  Levels lv;
+};
+
+struct SelDims {
+  int B, Hq, Hkv, G, N, D, C, K, q_tile;
+  float scale;
+  bool bf16;
+  Levels lv;
+};
+
+hipError_t launch_pool(const void* k, bool bf16, const PyrDims& pd, LensArg lens, int max_level, float* mean,
+                       float* sum, hipStream_t st);
+hipError_t launch_split_hilo(const float* mean, long long rows, int D, uint16_t* hilo, hipStream_t st);
+
+// Selection. `nodes` is the bf16 hi/lo pyramid (bf16 inputs) or the fp32 means (fp32 inputs).
+hipError_t launch_route(const SelDims& sd, const void* q, const void* k, const void* nodes, bool fused, int* kept,
+                        int* sel, float* sel_lse, hipStream_t st);
+
+// Bucket (unit, slot) pairs by node: node lists [U, K] (-1 = none) -> pairs sorted by
+// (b*Hkv + r, node), packed as (unit << 5) | slot. counts/offsets have n_buckets (+1) entries.
+hipError_t launch_regroup(const int* nodes, long long U, int K, int N, int buckets_per_head, int n_heads,
+                          int* counts, int* offsets, int* ranks, uint32_t* pairs, hipStream_t st);
+
+hipError_t launch_leaf_lse(const SelDims& sd, const void* q, const void* k, const int* kept, const uint32_t* pairs,
+                           const int* total, float* leaf_lse, hipStream_t st);
+hipError_t launch_finalize(const SelDims& sd, const int* kept, const float* leaf_lse, int* sel, float* sel_lse,
+                           hipStream_t st);
+
+// Attention over selected leaves.
+hipError_t launch_attn_leaf(const SelDims& sd, const void* q, const void* k, const void* v, const int* sel,
+                            const uint32_t* pairs, const int* total, void* part, float* part_lse, hipStream_t st);
+hipError_t launch_attn_merge(const SelDims& sd, const int* sel, const void* part, const float* part_lse, void* o,
+                             float* o_lse, hipStream_t st);
+
+// Flat block selection.
+hipError_t launch_bsa(const SelDims& sd, const void* q, const float* leaf_mean, const uint16_t* leaf_hilo, int* sel,
+                      hipStream_t st);
+
+// Decode step.
+struct DecodeArgs {
+  int B, Hq, Hkv, G, Nmax, D, C, K;
+  float scale;
+  bool bf16;
+  Levels lv;
+  LensArg lens;
+};
+hipError_t launch_decode(const DecodeArgs& da, const void* q_new, const void* k_new, const void* v_new, void* k_cache,
+                         void* v_cache, float* pyr_sum, float* pyr_mean, void* o, int* sel_out, hipStream_t st);
+
+}  // namespace pisa

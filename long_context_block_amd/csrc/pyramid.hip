@@ -1,0 +1,211 @@
+// Mean-pooled key pyramid ("Block Sparse Attention with Log-Linear Complexity" digest, 方法关键点,
+// pyramid bullet: leaf blocks of C tokens, mean pooling upward with merge factor 2, O(log N) levels).
+//
+// Stage 1 (pool_subtree): one work-group per (KV head, run of LB = 2048/d leaves). Thread (leaf,
+// 8-column chunk) sums its leaf's C keys in fp32 (token order), then the work-group builds levels
+// 1..log2(LB) of its subtree in LDS. Stage 2 (pool_upper): one work-group per KV head builds the
+// remaining levels from the stage-1 roots. A parent's mean is the token-weighted mean of its
+// children's means, (c1 m1 + c2 m2) / (c1 + c2), which is the mean of the raw keys in its span; with
+// full children it is (m1 + m2) / 2 rounded once. Node token counts are computed from the span.
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace pisa {
+
+__device__ __forceinline__ int node_count(long long len, int span_log2_tokens_unused, long long j, long long span) {
+  long long lo = j * span;
+  long long c = len - lo;
+  return c <= 0 ? 0 : (c >= span ? (int)span : (int)c);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void pool_subtree_kernel(const T* __restrict__ k, int N, int nsub, Levels lv, int C,
+                                                           LensArg lens, int top_level, float* __restrict__ mean,
+                                                           float* __restrict__ sum) {
+  constexpr int CH = D / 8;       // 8-column chunks per row
+  constexpr int LB = 256 / CH;    // leaves per work-group
+  __shared__ float s_mean[LB][D];
+  __shared__ float s_sum[LB][D];
+  const int bh = blockIdx.x / nsub;
+  const int sub = blockIdx.x % nsub;
+  const int b = bh / lens.hkv;
+  const long long len = lens.has ? lens.len[b] : N;
+  const int lam = threadIdx.x / CH;
+  const int ch = threadIdx.x % CH;
+  const long long head_row = (long long)bh * lv.nodes;
+  // ---- leaves
+  {
+    const long long j = (long long)sub * LB + lam;
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    int cnt = 0;
+    if (j < lv.n[0]) {
+      cnt = node_count(len, 0, j, C);
+      const T* src = k + ((long long)bh * N + j * C) * D + ch * 8;
+      for (int t = 0; t < cnt; ++t) {
+        Frag<T> f;
+        f.load(src + (long long)t * D);
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[e] += f.get(e);
+        } else {
+          acc[0] += f.a.x; acc[1] += f.a.y; acc[2] += f.a.z; acc[3] += f.a.w;
+          acc[4] += f.b.x; acc[5] += f.b.y; acc[6] += f.b.z; acc[7] += f.b.w;
+        }
+      }
+      const float inv = cnt > 0 ? 1.f / (float)cnt : 0.f;
+      float* mrow = mean + (head_row + lv.off[0] + j) * D + ch * 8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mrow[e] = cnt > 0 ? acc[e] / (float)cnt : 0.f;
+      (void)inv;
+      if (sum) {
+        float* srow = sum + (head_row + lv.off[0] + j) * D + ch * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) srow[e] = acc[e];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      s_mean[lam][ch * 8 + e] = cnt > 0 ? acc[e] / (float)cnt : 0.f;
+      s_sum[lam][ch * 8 + e] = acc[e];
+    }
+  }
+  __syncthreads();
+  // ---- levels inside the subtree
+  int nloc = LB;
+  for (int l = 1; l <= top_level; ++l) {
+    nloc >>= 1;
+    const long long span = (long long)C << l;
+    const long long cspan = (long long)C << (l - 1);
+    float pm[8], ps[8];
+    long long j = -1;
+    if (lam < nloc) {
+      j = (long long)sub * nloc + lam;
+      const long long c0 = 2 * j, c1 = 2 * j + 1;
+      const float w0 = (float)node_count(len, 0, c0, cspan);
+      const float w1 = (float)node_count(len, 0, c1, cspan);
+      const float wt = w0 + w1;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float m0 = s_mean[2 * lam][ch * 8 + e], m1 = s_mean[2 * lam + 1][ch * 8 + e];
+        pm[e] = wt > 0.f ? (w0 * m0 + w1 * m1) / wt : 0.f;
+        ps[e] = s_sum[2 * lam][ch * 8 + e] + s_sum[2 * lam + 1][ch * 8 + e];
+      }
+      (void)span;
+    }
+    __syncthreads();
+    if (lam < nloc) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        s_mean[lam][ch * 8 + e] = pm[e];
+        s_sum[lam][ch * 8 + e] = ps[e];
+      }
+      if (j < lv.n[l]) {
+        float* mrow = mean + (head_row + lv.off[l] + j) * D + ch * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mrow[e] = pm[e];
+        if (sum) {
+          float* srow = sum + (head_row + lv.off[l] + j) * D + ch * 8;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) srow[e] = ps[e];
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// Levels first_level .. n_levels-1 of each KV head, from the level below (written earlier).
+template <int D>
+__global__ __launch_bounds__(256) void pool_upper_kernel(int first_level, Levels lv, int C, LensArg lens, int N,
+                                                         float* __restrict__ mean, float* __restrict__ sum) {
+  constexpr int CH = D / 8;
+  const int bh = blockIdx.x;
+  const int b = bh / lens.hkv;
+  const long long len = lens.has ? lens.len[b] : N;
+  const long long head_row = (long long)bh * lv.nodes;
+  for (int l = first_level; l < lv.n_levels; ++l) {
+    const long long cspan = (long long)C << (l - 1);
+    const int items = lv.n[l] * CH;
+    for (int it = threadIdx.x; it < items; it += blockDim.x) {
+      const int j = it / CH, ch = it % CH;
+      const long long c0 = 2LL * j, c1 = 2LL * j + 1;
+      const bool has1 = c1 < lv.n[l - 1];
+      const float w0 = (float)node_count(len, 0, c0, cspan);
+      const float w1 = has1 ? (float)node_count(len, 0, c1, cspan) : 0.f;
+      const float wt = w0 + w1;
+      const float* m0 = mean + (head_row + lv.off[l - 1] + c0) * D + ch * 8;
+      const float* m1 = mean + (head_row + lv.off[l - 1] + (has1 ? c1 : c0)) * D + ch * 8;
+      float* mo = mean + (head_row + lv.off[l] + j) * D + ch * 8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float a = m0[e], bb = has1 ? m1[e] : 0.f;
+        mo[e] = wt > 0.f ? (w0 * a + w1 * bb) / wt : 0.f;
+      }
+      if (sum) {
+        const float* s0 = sum + (head_row + lv.off[l - 1] + c0) * D + ch * 8;
+        const float* s1 = sum + (head_row + lv.off[l - 1] + (has1 ? c1 : c0)) * D + ch * 8;
+        float* so = sum + (head_row + lv.off[l] + j) * D + ch * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) so[e] = s0[e] + (has1 ? s1[e] : 0.f);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// fp32 means -> bf16 hi and lo planes: row (head_row + node) holds hi[d] then lo[d], with
+// hi = rne(m) and lo = rne(m - hi), so hi + lo carries about 16 significant bits of m.
+__global__ __launch_bounds__(256) void split_hilo_kernel(const float* __restrict__ mean, long long rows, int D,
+                                                        uint16_t* __restrict__ hilo) {
+  const long long total = rows * D;
+  for (long long x = (long long)blockIdx.x * blockDim.x + threadIdx.x; x < total; x += (long long)gridDim.x * blockDim.x) {
+    const long long row = x / D;
+    const int c = (int)(x % D);
+    const float m = mean[x];
+    const uint16_t hi = f32_to_bf16(m);
+    const uint16_t lo = f32_to_bf16(m - bf16_to_f32(hi));
+    hilo[row * 2 * D + c] = hi;
+    hilo[row * 2 * D + D + c] = lo;
+  }
+}
+
+// ------------------------------------------------------------------------------------------ host
+template <typename T, int D>
+static hipError_t launch_pool_t(const T* k, const PyrDims& pd, LensArg lens, int max_level, float* mean, float* sum,
+                                hipStream_t st) {
+  constexpr int LB = 256 / (D / 8);
+  int sub_top = 0;
+  while ((1 << (sub_top + 1)) <= LB && sub_top + 1 <= max_level) ++sub_top;
+  const int nsub = (pd.lv.n[0] + LB - 1) / LB;
+  const int grid = pd.BH * nsub;
+  hipLaunchKernelGGL((pool_subtree_kernel<T, D>), dim3(grid), dim3(256), 0, st, k, pd.N, nsub, pd.lv, pd.C, lens,
+                     sub_top, mean, sum);
+  if (max_level > sub_top) {
+    hipLaunchKernelGGL((pool_upper_kernel<D>), dim3(pd.BH), dim3(256), 0, st, sub_top + 1, pd.lv, pd.C, lens, pd.N,
+                       mean, sum);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_pool(const void* k, bool bf16, const PyrDims& pd, LensArg lens, int max_level, float* mean, float* sum,
+                       hipStream_t st) {
+  if (bf16) {
+    if (pd.D == 128) return launch_pool_t<uint16_t, 128>((const uint16_t*)k, pd, lens, max_level, mean, sum, st);
+    return launch_pool_t<uint16_t, 64>((const uint16_t*)k, pd, lens, max_level, mean, sum, st);
+  }
+  if (pd.D == 128) return launch_pool_t<float, 128>((const float*)k, pd, lens, max_level, mean, sum, st);
+  return launch_pool_t<float, 64>((const float*)k, pd, lens, max_level, mean, sum, st);
+}
+
+hipError_t launch_split_hilo(const float* mean, long long rows, int D, uint16_t* hilo, hipStream_t st) {
+  const long long total = rows * D;
+  long long blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(split_hilo_kernel, dim3((unsigned)blocks), dim3(256), 0, st, mean, rows, D, hilo);
+  return hipGetLastError();
+}
+
+}  // namespace pisa

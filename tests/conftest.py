@@ -12,8 +12,11 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
 
 
-@pytest.fixture(scope="session")
-def gpu_available():
-    import torch
+def pytest_sessionstart(session):
+    # Use the library that is built; build it only when none is present.
+    from long_context_block_amd import pisa
 
-    return torch.cuda.is_available()
+    if not os.path.exists(pisa.LIB_PATH):
+        from long_context_block_amd import build
+
+        build.build()

@@ -1,0 +1,202 @@
+"""Shared plumbing for the GPU parity tests: upload seeded inputs, run the HIP path through the C ABI,
+and compare with the float64 oracle unit by unit."""
+from __future__ import annotations
+
+import dataclasses
+import math
+import sys
+
+import numpy as np
+import torch
+
+import oracle as O
+from long_context_block_amd import inputs as I
+from long_context_block_amd import pisa as P
+
+DEV = "cuda"
+TOL_ATTN = {"fp32": 1e-5, "bf16": 2e-2}
+MARGIN = 1e-3
+
+
+def say(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_device(t: I.Tensor) -> torch.Tensor:
+    if t.dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(t.data).view(np.int16)).to(DEV).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(t.data)).to(DEV)
+
+
+def shape_of(pf: I.Prefill, q_tile: int) -> P.Shape:
+    return P.make_shape(batch=pf.B, seq_len=pf.N, n_q_heads=pf.Hq, n_kv_heads=pf.Hkv, head_dim=pf.d, block=pf.C,
+                        top_k=pf.K, q_tile=q_tile, dtype=pf.dtype)
+
+
+@dataclasses.dataclass
+class GpuOut:
+    pyr: np.ndarray
+    sel: np.ndarray
+    sel_lse: np.ndarray | None
+    o: np.ndarray | None
+    o_lse: np.ndarray | None
+    bsa: np.ndarray | None
+
+
+def run_gpu(pf: I.Prefill, q_tile: int, *, lse=True, attn=True, bsa=False, dev=None) -> GpuOut:
+    s = shape_of(pf, q_tile)
+    q = to_device(pf.q) if dev is None else dev["q"]
+    k = to_device(pf.k) if dev is None else dev["k"]
+    v = (to_device(pf.v) if dev is None else dev["v"]) if attn else None
+    rows = P.pyramid_rows(s)
+    pyr = torch.empty((rows, pf.d), dtype=torch.float32, device=DEV)
+    P.pisa_build_pyramid(s, k, pyr)
+    sel = torch.empty((pf.B, pf.Hkv, pf.N, pf.K), dtype=torch.int32, device=DEV)
+    sel_lse = torch.empty((pf.B, pf.Hq, pf.N, pf.K), dtype=torch.float32, device=DEV) if lse else None
+    ws = P.alloc_workspace(s, P.PISA_OP_SELECT)
+    P.pisa_select(s, q, k, pyr, sel, sel_lse, ws)
+    o = o_lse = None
+    if attn:
+        o = torch.empty_like(q)
+        o_lse = torch.empty((pf.B, pf.Hq, pf.N), dtype=torch.float32, device=DEV)
+        wsa = P.alloc_workspace(s, P.PISA_OP_ATTN)
+        P.pisa_sparse_attn(s, q, k, v, sel, o, o_lse, wsa)
+    bsel = None
+    if bsa:
+        bsel = torch.empty_like(sel)
+        wsb = P.alloc_workspace(s, P.PISA_OP_BSA)
+        P.bsa_select(s, q, k, bsel, wsb)
+    torch.cuda.synchronize()
+    out = GpuOut(pyr=pyr.cpu().numpy(), sel=sel.cpu().numpy(), sel_lse=sel_lse.cpu().numpy() if lse else None,
+                 o=o.float().cpu().numpy() if attn else None, o_lse=o_lse.cpu().numpy() if attn else None,
+                 bsa=bsel.cpu().numpy() if bsa else None)
+    return out
+
+
+class OracleCache:
+    """Per (b, r) float64 keys/values and pyramid, computed lazily."""
+
+    def __init__(self, pf: I.Prefill):
+        self.pf = pf
+        self._heads = {}
+
+    def head(self, b, r):
+        if (b, r) not in self._heads:
+            k = self.pf.k.f64((b, r))
+            v = self.pf.v.f64((b, r))
+            self._heads[(b, r)] = (k, v, O.build_pyramid(k, self.pf.C, 2))
+        return self._heads[(b, r)]
+
+    def q(self, b, r, i):
+        G = self.pf.G
+        return self.pf.q.f64((b, slice(r * G, (r + 1) * G), i))  # [G, d]
+
+
+def units_all(pf):
+    return [(b, r, i) for b in range(pf.B) for r in range(pf.Hkv) for i in range(pf.N)]
+
+
+def units_sample(pf, n, seed=0, extra=()):
+    rng = np.random.default_rng(seed)
+    U = pf.B * pf.Hkv * pf.N
+    picks = set(int(x) for x in rng.choice(U, size=min(n, U), replace=False))
+    # always include the edges of each head: first, last, leaf boundaries near the end
+    for b in range(pf.B):
+        for r in range(pf.Hkv):
+            base = (b * pf.Hkv + r) * pf.N
+            for i in (0, 1, pf.C - 1, pf.C, pf.N - 1, pf.N - pf.C, pf.N - 2):
+                if 0 <= i < pf.N:
+                    picks.add(base + i)
+    for u in extra:
+        picks.add(int(u))
+    out = []
+    for u in sorted(picks):
+        bh, i = divmod(u, pf.N)
+        out.append((bh // pf.Hkv, bh % pf.Hkv, i))
+    return out
+
+
+@dataclasses.dataclass
+class Report:
+    n_units: int = 0
+    n_decided: int = 0
+    sel_mismatch: list = dataclasses.field(default_factory=list)
+    invariant_fail: list = dataclasses.field(default_factory=list)
+    lse_err: float = 0.0
+    attn_err: float = 0.0
+    olse_err: float = 0.0
+    bsa_mismatch: list = dataclasses.field(default_factory=list)
+    bsa_decided: int = 0
+
+
+def check_invariants(sel_row, i, C, K):
+    got = [int(j) for j in sel_row if j >= 0]
+    ok = len(got) == min(K, i // C + 1)
+    ok &= got == sorted(set(got))
+    ok &= all(j * C <= i for j in got)
+    ok &= all(int(j) == -1 for j in sel_row[len(got):])
+    return ok
+
+
+def compare(pf: I.Prefill, g: GpuOut, units, oc: OracleCache | None = None, check_attn=True, check_bsa=False) -> Report:
+    oc = oc or OracleCache(pf)
+    rep = Report()
+    G, C, K = pf.G, pf.C, pf.K
+    for (b, r, i) in units:
+        k, v, pyr = oc.head(b, r)
+        qg = oc.q(b, r, i)
+        us = O.select_unit(qg, k, pyr, i, K, pf.scale)
+        gsel = g.sel[b, r, i]
+        rep.n_units += 1
+        if not check_invariants(gsel, i, C, K):
+            rep.invariant_fail.append((b, r, i, gsel.tolist()))
+        if us.margin >= MARGIN:
+            rep.n_decided += 1
+            if gsel.tolist() != us.sel.tolist():
+                rep.sel_mismatch.append((b, r, i, gsel.tolist(), us.sel.tolist(), us.margin))
+            elif g.sel_lse is not None:
+                nsel = int((us.sel >= 0).sum())
+                e = np.abs(g.sel_lse[b, r * G:(r + 1) * G, i, :nsel] - us.sel_lse[:, :nsel]).max()
+                rep.lse_err = max(rep.lse_err, float(e))
+        if check_attn and g.o is not None:
+            o_ref, lse_ref = O.attend_unit(qg, k, v, gsel, i, C, pf.scale, pf.N)
+            e = np.abs(g.o[b, r * G:(r + 1) * G, i] - o_ref).max()
+            rep.attn_err = max(rep.attn_err, float(e))
+            el = np.abs(g.o_lse[b, r * G:(r + 1) * G, i] - lse_ref).max()
+            rep.olse_err = max(rep.olse_err, float(el))
+        if check_bsa and g.bsa is not None:
+            bsel, bm = O.bsa_select_unit(qg, pyr.means[0], i, C, K, pf.scale)
+            if bm >= MARGIN:
+                rep.bsa_decided += 1
+                if g.bsa[b, r, i].tolist() != bsel.tolist():
+                    rep.bsa_mismatch.append((b, r, i, g.bsa[b, r, i].tolist(), bsel.tolist(), bm))
+            if not check_invariants(g.bsa[b, r, i], i, C, K):
+                rep.invariant_fail.append(("bsa", b, r, i))
+    return rep
+
+
+def assert_report(rep: Report, dtype: str, check_attn=True, pyr_err=None):
+    say(f"units={rep.n_units} decided={rep.n_decided} sel_mismatch={len(rep.sel_mismatch)} "
+        f"invariant_fail={len(rep.invariant_fail)} lse_err={rep.lse_err:.3g} attn_err={rep.attn_err:.3g} "
+        f"olse_err={rep.olse_err:.3g} bsa_decided={rep.bsa_decided} bsa_mismatch={len(rep.bsa_mismatch)}")
+    assert not rep.invariant_fail, rep.invariant_fail[:5]
+    assert not rep.sel_mismatch, rep.sel_mismatch[:5]
+    assert not rep.bsa_mismatch, rep.bsa_mismatch[:5]
+    assert rep.lse_err <= 2e-4 if dtype == "bf16" else rep.lse_err <= 2e-5
+    if check_attn:
+        assert rep.attn_err <= TOL_ATTN[dtype], rep.attn_err
+        assert rep.olse_err <= (2e-4 if dtype == "bf16" else 2e-5), rep.olse_err
+
+
+def pyramid_err(pf: I.Prefill, g: GpuOut, oc: OracleCache, heads=None) -> float:
+    n, offs, nodes = P.pisa_pyramid_layout(shape_of(pf, 1))
+    err = 0.0
+    heads = heads or [(b, r) for b in range(pf.B) for r in range(pf.Hkv)]
+    for (b, r) in heads:
+        _, _, pyr = oc.head(b, r)
+        base = (b * pf.Hkv + r) * nodes
+        for l in range(n):
+            got = g.pyr[base + offs[l]: base + offs[l] + pyr.means[l].shape[0]]
+            err = max(err, float(np.abs(got - pyr.means[l]).max()))
+    return err

@@ -1,0 +1,139 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Rules: selections must equal the oracle's bit for bit (ascending, -1 padded) on every unit whose oracle
+margin (K-th minus (K+1)-th score, minimum over the scored levels) is at least 1e-3; every unit must
+satisfy the selection invariants; per-head leaf LSEs within 2e-4 (bf16) / 2e-5 (fp32); attention on
+the GPU's own selection within 2e-2 (bf16) / 1e-5 (fp32) max-abs of the oracle. The unit-major
+(q_tile = 1) and tiled (q_tile > 1) leaf stages must agree bit for bit."""
+import numpy as np
+import pytest
+
+from long_context_block_amd import inputs as I
+
+from gpu_common import (OracleCache, assert_report, compare, pyramid_err, run_gpu, say, units_all, units_sample)
+
+pytestmark = pytest.mark.gpu
+
+
+SMALL = {
+    "tiny_fp32": dict(B=1, Hq=1, Hkv=1, N=1024, d=64, C=32, K=4, dtype="fp32", keys="iid"),
+    "tiny_fp32_k_n1": dict(B=1, Hq=1, Hkv=1, N=1024, d=64, C=32, K=16, dtype="fp32", keys="iid"),
+    "tiny_fp32_k_n0": dict(B=1, Hq=1, Hkv=1, N=1024, d=64, C=32, K=32, dtype="fp32", keys="iid"),
+    "fp32_gqa_ragged": dict(B=2, Hq=4, Hkv=2, N=700, d=64, C=32, K=5, dtype="fp32", keys="ar1"),
+    "bf16_ragged": dict(B=2, Hq=8, Hkv=2, N=1000, d=128, C=64, K=4, dtype="bf16", keys="ar1"),
+    "bf16_d64_c32": dict(B=1, Hq=4, Hkv=2, N=777, d=64, C=32, K=6, dtype="bf16", keys="ar1"),
+    "bf16_d128_c32": dict(B=1, Hq=4, Hkv=1, N=1500, d=128, C=32, K=8, dtype="bf16", keys="ar1"),
+    "bf16_d64_c64": dict(B=1, Hq=2, Hkv=1, N=1300, d=64, C=64, K=3, dtype="bf16", keys="iid"),
+    "single_leaf": dict(B=1, Hq=4, Hkv=1, N=40, d=128, C=64, K=4, dtype="bf16", keys="ar1"),
+    "one_token": dict(B=2, Hq=4, Hkv=2, N=1, d=128, C=64, K=4, dtype="bf16", keys="iid"),
+    "k_covers_leaves": dict(B=1, Hq=4, Hkv=1, N=500, d=64, C=32, K=16, dtype="bf16", keys="ar1"),
+    "g16": dict(B=1, Hq=16, Hkv=1, N=600, d=128, C=64, K=4, dtype="bf16", keys="ar1"),
+    "g8": dict(B=1, Hq=16, Hkv=2, N=900, d=128, C=64, K=5, dtype="bf16", keys="ar1"),
+    "k1": dict(B=1, Hq=4, Hkv=1, N=900, d=128, C=32, K=1, dtype="bf16", keys="ar1"),
+    "k32": dict(B=1, Hq=2, Hkv=1, N=4096, d=64, C=32, K=32, dtype="bf16", keys="ar1"),
+}
+
+
+def _max_qtile(G):
+    return max(1, min(4, 16 // G))
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_small_all_units(name):
+    spec = SMALL[name]
+    say(f"[small] {name} {spec}")
+    pf = I.make_prefill(seed=0, workload_id=100, **spec)
+    qt = _max_qtile(pf.G)
+    g1 = run_gpu(pf, 1, bsa=True)
+    gt = run_gpu(pf, qt, bsa=False) if qt > 1 else g1
+    assert np.array_equal(g1.sel, gt.sel)
+    assert np.array_equal(g1.sel_lse.view(np.uint32), gt.sel_lse.view(np.uint32))
+    oc = OracleCache(pf)
+    perr = pyramid_err(pf, g1, oc)
+    say(f"pyramid max abs err {perr:.3g}")
+    assert perr <= (1e-5 if pf.dtype == "bf16" else 1e-5)
+    rep = compare(pf, g1, units_all(pf), oc, check_bsa=True)
+    assert_report(rep, pf.dtype)
+    # attention computed after the tiled selection matches too
+    rep_t = compare(pf, gt, units_all(pf)[:: max(1, pf.N // 200)], oc)
+    assert_report(rep_t, pf.dtype)
+
+
+def test_determinism_and_qtile_identity_64k_slice():
+    """Two runs give identical bits; q_tile 1 and 4 agree bit for bit (GQA 4, 8K tokens)."""
+    pf = I.make_prefill(B=1, Hq=8, Hkv=2, N=8192, d=128, C=64, K=16, dtype="bf16", keys="ar1", seed=0,
+                        workload_id=101)
+    a = run_gpu(pf, 4)
+    b = run_gpu(pf, 4)
+    c = run_gpu(pf, 1)
+    for x, y in ((a, b), (a, c)):
+        assert np.array_equal(x.sel, y.sel)
+        assert np.array_equal(x.sel_lse.view(np.uint32), y.sel_lse.view(np.uint32))
+    assert np.array_equal(a.o.view(np.uint32), b.o.view(np.uint32))
+    rep = compare(pf, a, units_sample(pf, 300, seed=1))
+    assert_report(rep, "bf16")
+
+
+def _full(name, q_tiles, n_sample, extra_units=(), check_bsa=True):
+    say(f"[full] generating {name}")
+    pf = I.make_workload(name)
+    say(f"[full] {name}: B={pf.B} Hq={pf.Hq} Hkv={pf.Hkv} N={pf.N} d={pf.d} C={pf.C} K={pf.K}")
+    outs = {}
+    for qt in q_tiles:
+        outs[qt] = run_gpu(pf, qt, bsa=check_bsa and qt == q_tiles[0], attn=qt == q_tiles[-1])
+        say(f"[full] {name}: q_tile={qt} done")
+    if len(q_tiles) > 1:
+        a, b = outs[q_tiles[0]], outs[q_tiles[-1]]
+        assert np.array_equal(a.sel, b.sel)
+        assert np.array_equal(a.sel_lse.view(np.uint32), b.sel_lse.view(np.uint32))
+        say(f"[full] {name}: q_tile {q_tiles} bitwise identical")
+    g = outs[q_tiles[-1]]
+    if check_bsa:
+        g.bsa = outs[q_tiles[0]].bsa
+    oc = OracleCache(pf)
+    units = units_sample(pf, n_sample, seed=2, extra=extra_units)
+    rep = compare(pf, g, units, oc, check_bsa=check_bsa)
+    assert_report(rep, pf.dtype)
+    perr = pyramid_err(pf, g, oc, heads=[(0, 0), (pf.B - 1, pf.Hkv - 1)])
+    say(f"[full] {name}: pyramid max abs err {perr:.3g}")
+    assert perr <= 1e-5
+    return pf, g, oc
+
+
+@pytest.mark.timeout(900)
+def test_full_16k():
+    _full("prefill_16k", [1, 2], 250)
+
+
+@pytest.mark.timeout(900)
+def test_full_64k_qtile_1_and_4():
+    _full("prefill_64k", [1, 4], 250)
+
+
+@pytest.mark.timeout(1200)
+def test_full_256k_needles():
+    pf = I.make_workload("prefill_256k_needles")
+    # needle units: queries of head 0 in each KV head group
+    extra = []
+    for r in range(pf.Hkv):
+        h = r * pf.G
+        for i in pf.needle_queries[0, h][::400]:
+            extra.append((0 * pf.Hkv + r) * pf.N + int(i))
+    del pf
+    pf, g, oc = _full("prefill_256k_needles", [4], 120, extra_units=extra, check_bsa=False)
+    # needle recall@K on sampled needle queries, GPU versus oracle
+    import oracle as O
+    rec_g, rec_o = [], []
+    for u in extra:
+        bh, i = divmod(u, pf.N)
+        b, r = divmod(bh, pf.Hkv)
+        E = [int(j) for j in pf.needle_leaves[b, r] if j * pf.C <= i]
+        if not E:
+            continue
+        k, v, pyr = oc.head(b, r)
+        us = O.select_unit(oc.q(b, r, i), k, pyr, i, pf.K, pf.scale)
+        den = min(pf.K, len(E))
+        rec_g.append(len(set(g.sel[b, r, i].tolist()) & set(E)) / den)
+        rec_o.append(len(set(us.sel.tolist()) & set(E)) / den)
+    say(f"[full] needle recall@K gpu={np.mean(rec_g):.4f} oracle={np.mean(rec_o):.4f} over {len(rec_g)} queries")
+    assert abs(np.mean(rec_g) - np.mean(rec_o)) < 0.02
