@@ -147,6 +147,17 @@ pisa_status bsa_select(const pisa_shape* shape, const void* q, const void* k, in
 const char* pisa_status_string(pisa_status status);
 const char* pisa_last_error(void);
 
+/* Stage timing for profiling, off by default. While enabled (per calling thread), every call
+ * records a pair of HIP events on its stream around each of its kernel launches (a launcher that
+ * issues several small kernels, such as the regroup, is one stage). pisa_stage_times() waits for
+ * the recorded events, adds each stage's elapsed time to a per-name total and count, forgets the
+ * events and writes up to `cap` entries: names (NUL-terminated, at most 31 characters),
+ * total milliseconds and launch counts. It returns the number of distinct stage names (which may
+ * exceed cap), or a negative pisa_status. pisa_stage_timing(0) also discards the totals. Event
+ * creation happens here, so do not enable it under stream capture. */
+pisa_status pisa_stage_timing(int32_t enable);
+int32_t pisa_stage_times(char (*names)[32], double* total_ms, int32_t* count, int32_t cap);
+
 #ifdef __cplusplus
 }
 #endif

@@ -6,7 +6,9 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <map>
 #include <string>
+#include <vector>
 
 #include "../../include/pisa.h"
 #include "internal.hpp"
@@ -29,6 +31,53 @@ pisa_status ok() {
   g_last_error.clear();
   return PISA_OK;
 }
+
+// ---- optional stage timing (per calling thread)
+struct StageEvent {
+  std::string name;
+  hipEvent_t a, b;
+};
+struct StageTimer {
+  bool on = false;
+  std::vector<StageEvent> pending;
+  std::vector<hipEvent_t> pool;
+  std::map<std::string, std::pair<double, int>> totals;
+  hipEvent_t get() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+};
+thread_local StageTimer g_timer;
+
+// Records events around one launcher when stage timing is on.
+struct Stage {
+  hipStream_t s;
+  const char* name;
+  hipEvent_t a = nullptr;
+  Stage(hipStream_t st, const char* n) : s(st), name(n) {
+    if (g_timer.on) {
+      a = g_timer.get();
+      if (a) hipEventRecord(a, s);
+    }
+  }
+  ~Stage() {
+    if (a) {
+      hipEvent_t b = g_timer.get();
+      if (b) {
+        hipEventRecord(b, s);
+        g_timer.pending.push_back({name, a, b});
+      } else {
+        g_timer.pool.push_back(a);
+      }
+    }
+  }
+};
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -279,9 +328,12 @@ pisa_status pisa_build_pyramid(const pisa_shape* shape, const void* k, const int
   st = lens_arg(host_lens, p.sd.B, p.sd.Hkv, 0, p.sd.N, &la);
   if (st != PISA_OK) return st;
   pisa::PyrDims pd{(int)p.BH, p.sd.N, p.sd.C, p.sd.D, p.sd.lv};
-  return hip_status(pisa::launch_pool(k, p.sd.bf16, pd, la, p.sd.lv.n_levels - 1, pyr_mean, pyr_sum,
-                                      (hipStream_t)stream),
-                    "pisa_build_pyramid");
+  hipError_t e;
+  {
+    Stage sc((hipStream_t)stream, "pyramid");
+    e = pisa::launch_pool(k, p.sd.bf16, pd, la, p.sd.lv.n_levels - 1, pyr_mean, pyr_sum, (hipStream_t)stream);
+  }
+  return hip_status(e, "pisa_build_pyramid");
 }
 
 pisa_status pisa_select(const pisa_shape* shape, const void* q, const void* k, const float* pyr_mean, int32_t* sel,
@@ -303,23 +355,41 @@ pisa_status pisa_select(const pisa_shape* shape, const void* q, const void* k, c
   hipError_t e = hipSuccess;
   const void* nodes = pyr_mean;
   if (p.sd.bf16) {
-    e = pisa::launch_split_hilo(pyr_mean, p.BH * p.sd.lv.nodes, p.sd.D, w.hilo, s);
+    {
+      Stage sc(s, "split_hilo");
+      e = pisa::launch_split_hilo(pyr_mean, p.BH * p.sd.lv.nodes, p.sd.D, w.hilo, s);
+    }
     if (e != hipSuccess) return hip_status(e, "split_hilo");
     nodes = w.hilo;
   }
   if (p.sd.q_tile == 1) {
-    e = pisa::launch_route(p.sd, q, k, nodes, true, nullptr, sel, sel_lse, s);
+    {
+      Stage sc(s, "route_fused_leaf");
+      e = pisa::launch_route(p.sd, q, k, nodes, true, nullptr, sel, sel_lse, s);
+    }
     return hip_status(e, "route (fused leaf stage)");
   }
-  e = pisa::launch_route(p.sd, q, k, nodes, false, w.kept, nullptr, nullptr, s);
+  {
+    Stage sc(s, "route");
+    e = pisa::launch_route(p.sd, q, k, nodes, false, w.kept, nullptr, nullptr, s);
+  }
   if (e != hipSuccess) return hip_status(e, "route");
-  e = pisa::launch_regroup(w.kept, p.U, p.sd.K, p.sd.N, p.n1_buckets, (int)p.BH, w.counts, w.offsets, w.ranks,
-                           w.pairs, s);
+  {
+    Stage sc(s, "regroup_select");
+    e = pisa::launch_regroup(w.kept, p.U, p.sd.K, p.sd.N, p.n1_buckets, (int)p.BH, w.counts, w.offsets, w.ranks,
+                             w.pairs, s);
+  }
   if (e != hipSuccess) return hip_status(e, "regroup");
   const int* total = w.offsets + p.BH * p.n1_buckets;
-  e = pisa::launch_leaf_lse(p.sd, q, k, w.kept, w.pairs, total, w.leaf_lse, s);
+  {
+    Stage sc(s, "leaf_lse");
+    e = pisa::launch_leaf_lse(p.sd, q, k, w.kept, w.pairs, total, w.leaf_lse, s);
+  }
   if (e != hipSuccess) return hip_status(e, "leaf_lse");
-  e = pisa::launch_finalize(p.sd, w.kept, w.leaf_lse, sel, sel_lse, s);
+  {
+    Stage sc(s, "finalize");
+    e = pisa::launch_finalize(p.sd, w.kept, w.leaf_lse, sel, sel_lse, s);
+  }
   return hip_status(e, "finalize");
 }
 
@@ -340,13 +410,23 @@ pisa_status pisa_sparse_attn(const pisa_shape* shape, const void* q, const void*
   AttnWs w;
   carve_attn(p, ws, &w);
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = pisa::launch_regroup(sel, p.U, p.sd.K, p.sd.N, p.sd.lv.n[0], (int)p.BH, w.counts, w.offsets, w.ranks,
-                                      w.pairs, s);
+  hipError_t e;
+  {
+    Stage sc(s, "regroup_attn");
+    e = pisa::launch_regroup(sel, p.U, p.sd.K, p.sd.N, p.sd.lv.n[0], (int)p.BH, w.counts, w.offsets, w.ranks,
+                             w.pairs, s);
+  }
   if (e != hipSuccess) return hip_status(e, "regroup");
   const int* total = w.offsets + p.BH * p.sd.lv.n[0];
-  e = pisa::launch_attn_leaf(p.sd, q, k, v, sel, w.pairs, total, w.part, w.part_lse, s);
+  {
+    Stage sc(s, "attn_leaf");
+    e = pisa::launch_attn_leaf(p.sd, q, k, v, sel, w.pairs, total, w.part, w.part_lse, s);
+  }
   if (e != hipSuccess) return hip_status(e, "attn_leaf");
-  e = pisa::launch_attn_merge(p.sd, sel, w.part, w.part_lse, o, o_lse, s);
+  {
+    Stage sc(s, "attn_merge");
+    e = pisa::launch_attn_merge(p.sd, sel, w.part, w.part_lse, o, o_lse, s);
+  }
   return hip_status(e, "attn_merge");
 }
 
@@ -382,9 +462,13 @@ pisa_status pisa_decode_step(const pisa_shape* shape, const int32_t* host_lens, 
   da.scale = p.sd.scale;
   da.bf16 = p.sd.bf16;
   da.lv = p.sd.lv;
-  return hip_status(pisa::launch_decode(da, q_new, k_new, v_new, k_cache, v_cache, pyr_sum, pyr_mean, o, sel_out,
-                                        (hipStream_t)stream),
-                    "decode_step");
+  hipError_t e;
+  {
+    Stage sc((hipStream_t)stream, "decode_step");
+    e = pisa::launch_decode(da, q_new, k_new, v_new, k_cache, v_cache, pyr_sum, pyr_mean, o, sel_out,
+                            (hipStream_t)stream);
+  }
+  return hip_status(e, "decode_step");
 }
 
 pisa_status bsa_select(const pisa_shape* shape, const void* q, const void* k, int32_t* sel, void* ws, size_t ws_bytes,
@@ -408,14 +492,59 @@ pisa_status bsa_select(const pisa_shape* shape, const void* q, const void* k, in
   pisa::PyrDims pd{(int)p.BH, p.sd.N, p.sd.C, p.sd.D, p.sd.lv};
   pd.lv.n_levels = 1;
   pd.lv.nodes = p.sd.lv.n[0];
-  hipError_t e = pisa::launch_pool(k, p.sd.bf16, pd, la, 0, w.mean, nullptr, s);
-  if (e != hipSuccess) return hip_status(e, "bsa leaf pooling");
-  if (p.sd.bf16) {
-    e = pisa::launch_split_hilo(w.mean, p.BH * p.sd.lv.n[0], p.sd.D, w.hilo, s);
-    if (e != hipSuccess) return hip_status(e, "bsa split");
+  hipError_t e;
+  {
+    Stage sc(s, "bsa_pool");
+    e = pisa::launch_pool(k, p.sd.bf16, pd, la, 0, w.mean, nullptr, s);
+    if (e == hipSuccess && p.sd.bf16) e = pisa::launch_split_hilo(w.mean, p.BH * p.sd.lv.n[0], p.sd.D, w.hilo, s);
   }
-  e = pisa::launch_bsa(p.sd, q, w.mean, w.hilo, sel, s);
+  if (e != hipSuccess) return hip_status(e, "bsa leaf pooling");
+  {
+    Stage sc(s, "bsa_select");
+    e = pisa::launch_bsa(p.sd, q, w.mean, w.hilo, sel, s);
+  }
   return hip_status(e, "bsa_select");
+}
+
+pisa_status pisa_stage_timing(int32_t enable) {
+  g_timer.on = enable != 0;
+  if (!enable) {
+    for (auto& e : g_timer.pending) {
+      hipEventSynchronize(e.b);
+      g_timer.pool.push_back(e.a);
+      g_timer.pool.push_back(e.b);
+    }
+    g_timer.pending.clear();
+    g_timer.totals.clear();
+  }
+  return ok();
+}
+
+int32_t pisa_stage_times(char (*names)[32], double* total_ms, int32_t* count, int32_t cap) {
+  for (auto& e : g_timer.pending) {
+    if (hipEventSynchronize(e.b) != hipSuccess) return fail(PISA_EHIP, "hipEventSynchronize failed");
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, e.a, e.b) != hipSuccess) return fail(PISA_EHIP, "hipEventElapsedTime failed");
+    auto& t = g_timer.totals[e.name];
+    t.first += ms;
+    t.second += 1;
+    g_timer.pool.push_back(e.a);
+    g_timer.pool.push_back(e.b);
+  }
+  g_timer.pending.clear();
+  int32_t n = 0;
+  for (auto& kv : g_timer.totals) {
+    if (n < cap) {
+      if (names) {
+        std::strncpy(names[n], kv.first.c_str(), 31);
+        names[n][31] = 0;
+      }
+      if (total_ms) total_ms[n] = kv.second.first;
+      if (count) count[n] = kv.second.second;
+    }
+    ++n;
+  }
+  return n;
 }
 
 }  // extern "C"

@@ -10,6 +10,7 @@
 // The K tile rows are permuted so that after the first MFMA each lane group holds 8 consecutive
 // tokens per 32-token step, which is exactly the B operand the second MFMA needs (no shuffle).
 // attn_merge combines a unit's K partials with weights exp(lse_k - LSE), LSE = LSE_k lse_k.
+#include "attn_tiles.hpp"
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -29,10 +30,7 @@ struct AttnParams {
   float* part_lse; // [U, K, G]
 };
 
-constexpr int kAttnTask = 64;
-
-// Token offset (within the leaf) of D-row 4*grp + j of M-tile m after the first MFMA.
-__device__ __forceinline__ int attn_token(int m, int grp, int j) { return 32 * (m >> 1) + 8 * grp + 4 * (m & 1) + j; }
+constexpr int kAttnTask = 256;
 
 template <typename T, int D, int C>
 __global__ __launch_bounds__(256) void attn_leaf_kernel(AttnParams<T> p) {
@@ -44,164 +42,74 @@ __global__ __launch_bounds__(256) void attn_leaf_kernel(AttnParams<T> p) {
   const int lane = lane_id(), wave = threadIdx.x >> 6, r16 = lane & 15, grp = lane >> 4;
   const int task = xcd_logical_block(gridDim.x) * 4 + wave;
   const long long total = *p.total;
-  long long pos = (long long)task * kAttnTask;
-  if (task >= p.tasks || pos >= total) return;
-  const long long end = pos + kAttnTask < total ? pos + kAttnTask : total;
+  const long long pos0 = (long long)task * kAttnTask;
+  if (task >= p.tasks || pos0 >= total) return;
   const int tile_units = 16 / p.G;
-  while (pos < end) {
-    const uint32_t pr = p.pairs[pos];
-    const long long u = pr >> 5;
-    const long long bh = u / p.N;
-    const int leaf = p.sel[u * p.K + (pr & 31)];
-    long long seg = end;
-    for (long long base = pos; base < end; base += 64) {
-      const long long x = base + lane;
-      bool diff = false;
-      if (x < end) {
-        const uint32_t q2 = p.pairs[x];
-        const long long u2 = q2 >> 5;
-        diff = (u2 / p.N != bh) || (p.sel[u2 * p.K + (q2 & 31)] != leaf);
-      }
-      const unsigned long long m = __ballot(diff);
-      if (m) {
-        seg = base + __ffsll((long long)m) - 1;
-        break;
-      }
-    }
+  PairRun run;
+  run.base = pos0;
+  run.end = pos0 + kAttnTask < total ? pos0 + kAttnTask : total;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const long long x = pos0 + 64 * w + lane;
+    run.pr[w] = x < run.end ? p.pairs[x] : 0u;
+  }
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const long long x = pos0 + 64 * w + lane;
+    const long long u = run.pr[w] >> 5;
+    run.key[w] = x < run.end ? (u / p.N) * (1LL << 32) + p.sel[u * p.K + (run.pr[w] & 31)] : -1;
+  }
+  long long pos = pos0;
+  while (pos < run.end) {
+    const uint32_t pr0 = run.pair(pos);
+    const long long u0 = readlane((int)(pr0 >> 5), 0);
+    const long long bh = u0 / p.N;
+    const int leaf = p.sel[u0 * p.K + (readlane((int)pr0, 0) & 31)];
+    const long long seg = run.run_end(pos, bh * (1LL << 32) + leaf);
     const long long t0 = (long long)leaf * C;
     const T* kbh = p.k + bh * (long long)p.N * D;
     const T* vbh = p.v + bh * (long long)p.N * D;
-    // K tile, rows permuted (see attn_token).
     Frag<T> kf[MS][D / 32];
-#pragma unroll
-    for (int m = 0; m < MS; ++m) {
-      const long long t = t0 + attn_token(m, r16 >> 2, r16 & 3);
+    load_attn_k<T, D, C>(kbh, t0, p.N, kf);
+    Frag<T> vf[MO][KS];
+    load_attn_vt<T, D, C>(vbh, t0, p.N, s_vt[(sizeof(T) == 2) ? wave : 0], vf);
+    const int b = (int)(bh / p.Hkv), r = (int)(bh % p.Hkv);
+    const int h = r16 % p.G;
+    const T* qhead = p.q + (((long long)b * p.Hq + (long long)r * p.G + h) * p.N) * D + 8 * grp;
+    const long long ubase = bh * p.N;
+    struct Tile {
+      Frag<T> qf[D / 32];
+      long long u;
+      int slot;
+      bool valid;
+    };
+    auto fetch = [&](Tile& t, long long tp) {
+      const long long pi = tp + r16 / p.G;
+      t.valid = pi < seg;
+      const uint32_t pc = run.pair(t.valid ? pi : pos);
+      t.u = pc >> 5;
+      t.slot = pc & 31;
+      const T* qrow = qhead + (t.u - ubase) * D;
 #pragma unroll
       for (int s = 0; s < D / 32; ++s) {
-        if (t < p.N)
-          kf[m][s].load(kbh + t * D + (D / 4) * grp + 8 * s);
+        if (t.valid)
+          t.qf[s].load(qrow + 32 * s);
         else
-          kf[m][s].zero();
+          t.qf[s].zero();
       }
-    }
-    // V^T tile: lane (row n = 16 mt + r16, grp) needs V[32 ks + 8 grp + e][n], e = 0..7.
-    Frag<T> vf[MO][KS];
-    if constexpr (sizeof(T) == 2) {
-      constexpr int CHR = D / 8;  // 8-element chunks per V row
-#pragma unroll
-      for (int it = 0; it < (C * CHR) / 64; ++it) {
-        const int qd = it * 64 + lane;
-        const int t = qd / CHR, c0 = (qd % CHR) * 8;
-        Frag<uint16_t> f;
-        if (t0 + t < p.N)
-          f.load((const uint16_t*)vbh + (t0 + t) * D + c0);
-        else
-          f.zero();
-        const uint32_t w[4] = {f.u.x, f.u.y, f.u.z, f.u.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) s_vt[wave][c0 + e][t] = (uint16_t)((e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xffffu));
-      }
-      __threadfence_block();
-#pragma unroll
-      for (int mt = 0; mt < MO; ++mt)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          vf[mt][ks].u = *reinterpret_cast<const uint4*>(&s_vt[wave][16 * mt + r16][32 * ks + 8 * grp]);
-      __threadfence_block();
-    } else {
-#pragma unroll
-      for (int mt = 0; mt < MO; ++mt)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          float e8[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const long long t = t0 + 32 * ks + 8 * grp + e;
-            e8[e] = t < p.N ? (float)vbh[t * D + 16 * mt + r16] : 0.f;
-          }
-          Frag<float>& f = reinterpret_cast<Frag<float>&>(vf[mt][ks]);
-          f.a = make_float4(e8[0], e8[1], e8[2], e8[3]);
-          f.b = make_float4(e8[4], e8[5], e8[6], e8[7]);
-        }
-    }
-    const int b = (int)(bh / p.Hkv), r = (int)(bh % p.Hkv);
-    for (long long tp = pos; tp < seg; tp += tile_units) {
-      const long long pi = tp + r16 / p.G;
-      const int h = r16 % p.G;
-      const bool cv = pi < seg;
-      long long uc = 0, ic = -1;
-      int slot = 0;
+    };
+    auto attend = [&](const Tile& cur) {
       Frag<T> qf[D / 32];
-      if (cv) {
-        const uint32_t pc = p.pairs[pi];
-        uc = pc >> 5;
-        slot = pc & 31;
-        ic = uc % p.N;
-        const T* qrow = p.q + ((((long long)b * p.Hq + (long long)r * p.G + h) * p.N) + ic) * D + (D / 4) * grp;
 #pragma unroll
-        for (int s = 0; s < D / 32; ++s) qf[s].load(qrow + 8 * s);
-      } else {
-#pragma unroll
-        for (int s = 0; s < D / 32; ++s) qf[s].zero();
-      }
-      f32x4 sacc[MS];
-#pragma unroll
-      for (int m = 0; m < MS; ++m) sacc[m] = zero4();
-#pragma unroll
-      for (int s = 0; s < D / 32; ++s)
-#pragma unroll
-        for (int m = 0; m < MS; ++m) mma(sacc[m], kf[m][s], qf[s]);
-      // masked softmax statistics per column
-      float mx = kNegInf;
-#pragma unroll
-      for (int m = 0; m < MS; ++m)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const long long t = t0 + attn_token(m, grp, j);
-          const float x = t <= ic ? sacc[m][j] : kNegInf;
-          sacc[m][j] = x;
-          mx = fmaxf(mx, x);
-        }
-      mx = colgroup_max(mx);
-      const bool any = mx != kNegInf;
-      const float ms = any ? mx : 0.f;
-      const float c2 = p.scale * kLog2e;
-      float lsum = 0.f;
-#pragma unroll
-      for (int m = 0; m < MS; ++m)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float e = fast_exp2((sacc[m][j] - ms) * c2);
-          sacc[m][j] = e;
-          lsum += e;
-        }
-      lsum = colgroup_sum(lsum);
-      // P as the B operand of O^T = V^T P
-      Frag<T> pf[KS];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        if constexpr (sizeof(T) == 2) {
-          const f32x4 a = sacc[2 * ks], bb = sacc[2 * ks + 1];
-          Frag<uint16_t>& f = reinterpret_cast<Frag<uint16_t>&>(pf[ks]);
-          f.u.x = (uint32_t)f32_to_bf16(a[0]) | ((uint32_t)f32_to_bf16(a[1]) << 16);
-          f.u.y = (uint32_t)f32_to_bf16(a[2]) | ((uint32_t)f32_to_bf16(a[3]) << 16);
-          f.u.z = (uint32_t)f32_to_bf16(bb[0]) | ((uint32_t)f32_to_bf16(bb[1]) << 16);
-          f.u.w = (uint32_t)f32_to_bf16(bb[2]) | ((uint32_t)f32_to_bf16(bb[3]) << 16);
-        } else {
-          Frag<float>& f = reinterpret_cast<Frag<float>&>(pf[ks]);
-          f.a = make_float4(sacc[2 * ks][0], sacc[2 * ks][1], sacc[2 * ks][2], sacc[2 * ks][3]);
-          f.b = make_float4(sacc[2 * ks + 1][0], sacc[2 * ks + 1][1], sacc[2 * ks + 1][2], sacc[2 * ks + 1][3]);
-        }
-      }
+      for (int s = 0; s < D / 32; ++s) qf[s] = cur.qf[s];
+      const long long uc = cur.u;
+      const int slot = cur.slot;
+      const bool cv = cur.valid;
+      const long long ic = cv ? uc - ubase : -1;
       f32x4 oacc[MO];
-#pragma unroll
-      for (int mt = 0; mt < MO; ++mt) {
-        oacc[mt] = zero4();
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) mma(oacc[mt], vf[mt][ks], pf[ks]);
-      }
+      float lse, inv;
+      attend_tile<T, D, C>(kf, vf, qf, t0, ic, p.scale, oacc, lse, inv);
       if (cv) {
-        const float inv = any ? 1.f / lsum : 0.f;
         const long long prow = (uc * p.K + slot) * p.G + h;
         T* dst = p.part + prow * D;
 #pragma unroll
@@ -217,7 +125,19 @@ __global__ __launch_bounds__(256) void attn_leaf_kernel(AttnParams<T> p) {
                 make_float4(oacc[mt][0] * inv, oacc[mt][1] * inv, oacc[mt][2] * inv, oacc[mt][3] * inv);
           }
         }
-        if (grp == 0) p.part_lse[prow] = any ? p.scale * ms + kLn2 * fast_log2(lsum) : kNegInf;
+        if (grp == 0) p.part_lse[prow] = lse;
+      }
+    };
+    const long long ntiles = (seg - pos + tile_units - 1) / tile_units;
+    Tile X, Y;
+    fetch(X, pos);
+    if (ntiles > 1) fetch(Y, pos + tile_units);
+    for (long long t = 0; t < ntiles; t += 2) {
+      attend(X);
+      if (t + 2 < ntiles) fetch(X, pos + (t + 2) * tile_units);
+      if (t + 1 < ntiles) {
+        attend(Y);
+        if (t + 3 < ntiles) fetch(Y, pos + (t + 3) * tile_units);
       }
     }
     pos = seg;

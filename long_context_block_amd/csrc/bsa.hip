@@ -47,7 +47,7 @@ __global__ __launch_bounds__(256) void bsa_kernel(BsaParams<T> p) {
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
     if (col_ok) {
       for (int h = 0; h < p.G; ++h) {
-        const T* qrow = p.q + ((((long long)b * p.Hq + (long long)r * p.G + h) * p.N) + ic) * D + (D / 4) * grp + 8 * s;
+        const T* qrow = p.q + ((((long long)b * p.Hq + (long long)r * p.G + h) * p.N) + ic) * D + 32 * s + 8 * grp;
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] += to_f32<T>(qrow[e]);
       }
@@ -91,7 +91,7 @@ __global__ __launch_bounds__(256) void bsa_kernel(BsaParams<T> p) {
       if constexpr (sizeof(T) == 2) {
         Frag<uint16_t> ahi, alo;
         if (rv) {
-          const uint16_t* row = p.hilo + ((bh * p.n0) + jr) * 2 * D + (D / 4) * grp + 8 * s;
+          const uint16_t* row = p.hilo + ((bh * p.n0) + jr) * 2 * D + 32 * s + 8 * grp;
           ahi.load(row);
           alo.load(row + D);
         } else {
@@ -104,7 +104,7 @@ __global__ __launch_bounds__(256) void bsa_kernel(BsaParams<T> p) {
       } else {
         Frag<float> a;
         if (rv)
-          a.load(p.mean + ((bh * p.n0) + jr) * D + (D / 4) * grp + 8 * s);
+          a.load(p.mean + ((bh * p.n0) + jr) * D + 32 * s + 8 * grp);
         else
           a.zero();
         mma(acc, a, reinterpret_cast<Frag<float>&>(qhi[s]));

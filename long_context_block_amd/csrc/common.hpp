@@ -3,8 +3,9 @@
 // Matrix tiles use v_mfma_f32_16x16x32_bf16 (bf16 inputs, fp32 accumulate) or, for fp32 inputs,
 // eight v_mfma_f32_16x16x4_f32 per 32-wide k step. Per lane: A row = B column = lane % 16, lane group
 // g = lane / 16 supplies 8 consecutive k elements of the step; the D tile gives lane (col = lane % 16,
-// g) the rows 4g .. 4g+3. Each k step here covers d elements [(d/4) g + 8 s, +8) of lane group g, so
-// a lane reads 64 (or 32) contiguous bytes of a row across the steps.
+// g) the rows 4g .. 4g+3. The k order inside a dot product is free, so k step s of lane group g covers
+// d elements [32 s + 8 g, +8): the four lanes of a row read 64 (bf16) or 128 (fp32) contiguous bytes
+// per load instruction.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -138,14 +139,31 @@ __device__ __forceinline__ float lse2(float a, float b) {
   return m + kLn2 * fast_log2(1.f + fast_exp2(d * kLog2e));
 }
 
-// Lanes [0, n) hold candidates in ascending node order with their scores. True for the lanes among
-// the K best by (score descending, node ascending). n and K are wave-uniform.
-__device__ __forceinline__ bool topk_keep(float score, int n, int K) {
+// Sum over the 16 lanes of each row by DPP row rotations: every lane gets the row total (the order of
+// the additions depends on the lane, so read one fixed lane when bit reproducibility matters).
+template <int CTRL>
+__device__ __forceinline__ float dpp_rot(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp_rot<0x128>(v);  // row_ror:8
+  v += dpp_rot<0x124>(v);  // row_ror:4
+  v += dpp_rot<0x122>(v);  // row_ror:2
+  return v + dpp_rot<0x121>(v);  // row_ror:1
+}
+
+// Candidates c in [0, n) have scores s[c] (LDS, this wave's 64-entry slice) in ascending node order.
+// True for the lanes among the K best by (score descending, node ascending). n, K wave-uniform.
+__device__ __forceinline__ bool topk_keep_lds(const float* s, int n, int K) {
   const int lane = lane_id();
+  const float mine = s[lane < n ? lane : 0];
   int rank = 0;
-  for (int c = 0; c < n; ++c) {
-    const float sc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(score), c));
-    rank += (sc > score) || (sc == score && c < lane);
+  for (int c = 0; c < n; c += 4) {
+    const float4 v = *reinterpret_cast<const float4*>(s + c);
+    rank += (c + 0 < n) && (v.x > mine || (v.x == mine && c + 0 < lane));
+    rank += (c + 1 < n) && (v.y > mine || (v.y == mine && c + 1 < lane));
+    rank += (c + 2 < n) && (v.z > mine || (v.z == mine && c + 2 < lane));
+    rank += (c + 3 < n) && (v.w > mine || (v.w == mine && c + 3 < lane));
   }
   return lane < n && rank < K;
 }
@@ -162,6 +180,34 @@ __device__ __forceinline__ int compact_lanes(bool keep, int value, int* count) {
   *count = total;
   return __builtin_amdgcn_ds_permute(dst << 2, value);
 }
+
+// A run of up to 256 consecutive entries of a bucket-sorted (unit << 5 | slot) pair list, held four
+// per lane (entry x in register x / 64 of lane x % 64), with each pair's bucket key.
+struct PairRun {
+  uint32_t pr[4];
+  long long key[4];
+  long long base, end;  // entries [base, end)
+  // pair at absolute index x (base <= x < base + 256); every lane may ask for a different x
+  __device__ __forceinline__ uint32_t pair(long long x) const {
+    const int idx = (int)(x - base);
+    const int src = idx & 63, which = idx >> 6;
+    const uint32_t v0 = (uint32_t)__shfl((int)pr[0], src), v1 = (uint32_t)__shfl((int)pr[1], src);
+    const uint32_t v2 = (uint32_t)__shfl((int)pr[2], src), v3 = (uint32_t)__shfl((int)pr[3], src);
+    return which == 0 ? v0 : which == 1 ? v1 : which == 2 ? v2 : v3;
+  }
+  // first index >= from whose key differs from `key_at_from` (end if none); wave-uniform
+  __device__ __forceinline__ long long run_end(long long from, long long key_at_from) const {
+    const int lane = lane_id();
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const long long x = base + 64 * w + lane;
+      const bool diff = x >= from && x < end && key[w] != key_at_from;
+      const unsigned long long m = __ballot(diff);
+      if (m) return base + 64 * w + __ffsll((long long)m) - 1;
+    }
+    return end;
+  }
+};
 
 // Wave-uniform read of lane c.
 __device__ __forceinline__ int readlane(int v, int c) { return __builtin_amdgcn_readlane(v, c); }

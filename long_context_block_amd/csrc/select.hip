@@ -24,195 +24,9 @@
 // per-column arithmetic and sum the heads in the same order, so their outputs agree bit for bit.
 #include "common.hpp"
 #include "internal.hpp"
+#include "walk_tiles.hpp"
 
 namespace pisa {
-
-template <typename T, int D>
-struct NodeRows;
-
-// bf16 path: row r at base + r*2D holds hi[D] then lo[D].
-template <int D>
-struct NodeRows<uint16_t, D> {
-  const uint16_t* base;
-  __device__ __forceinline__ void dot(f32x4& acc, long long row, bool valid, int grp,
-                                      const Frag<uint16_t> (&qf)[D / 32]) const {
-    const uint16_t* p = base + row * 2 * D + (D / 4) * grp;
-#pragma unroll
-    for (int s = 0; s < D / 32; ++s) {
-      Frag<uint16_t> hi, lo;
-      if (valid) {
-        hi.load(p + 8 * s);
-        lo.load(p + D + 8 * s);
-      } else {
-        hi.zero();
-        lo.zero();
-      }
-      mma(acc, hi, qf[s]);
-      mma(acc, lo, qf[s]);
-    }
-  }
-};
-
-// fp32 path: row r at base + r*D.
-template <int D>
-struct NodeRows<float, D> {
-  const float* base;
-  __device__ __forceinline__ void dot(f32x4& acc, long long row, bool valid, int grp,
-                                      const Frag<float> (&qf)[D / 32]) const {
-    const float* p = base + row * D + (D / 4) * grp;
-#pragma unroll
-    for (int s = 0; s < D / 32; ++s) {
-      Frag<float> m;
-      if (valid)
-        m.load(p + 8 * s);
-      else
-        m.zero();
-      mma(acc, m, qf[s]);
-    }
-  }
-};
-
-// Scores of the candidates in lanes [0, n_cand) (node index cn, ascending) at a level l >= 1:
-// sum over heads of the LSE over the eligible children (level l-1, first token <= i) of
-// scale * q . mean(child). cspan = tokens per child node. Lanes >= n_cand get -inf.
-template <typename T, int D>
-__device__ float score_candidates(const NodeRows<T, D>& rows, long long level_off, const Frag<T> (&qf)[D / 32], int cn,
-                                  int n_cand, long long cspan, long long i, int G, float scale) {
-  const int lane = lane_id(), r16 = lane & 15, grp = lane >> 4;
-  const int MT = (2 * n_cand + 15) >> 4;
-  float res = kNegInf;
-#pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    if (m < MT) {
-      const int row = 16 * m + r16;
-      const int cidx = row >> 1;
-      const int cnode = __shfl(cn, cidx);
-      const long long child = 2LL * cnode + (row & 1);
-      const bool valid = cidx < n_cand && child * cspan <= i;
-      f32x4 acc = zero4();
-      rows.dot(acc, level_off + (valid ? child : 0), valid, grp, qf);
-      float hs[2];
-#pragma unroll
-      for (int a = 0; a < 2; ++a) {
-        const int c = 8 * m + 2 * grp + a;
-        const int pn = __shfl(cn, c);
-        const bool v1 = c < n_cand && (2LL * pn + 1) * cspan <= i;
-        const float x0 = scale * acc[2 * a], x1 = scale * acc[2 * a + 1];
-        float l = v1 ? lse2(x0, x1) : x0;
-        l = r16 < G ? l : 0.f;
-        l += __shfl_xor(l, 1);
-        l += __shfl_xor(l, 2);
-        l += __shfl_xor(l, 4);
-        l += __shfl_xor(l, 8);
-        hs[a] = l;
-      }
-#pragma unroll
-      for (int a = 0; a < 2; ++a) {
-        const float t = __shfl(hs[a], 16 * ((lane & 7) >> 1));
-        if ((lane >> 3) == m && (lane & 1) == a) res = t;
-      }
-    }
-  }
-  return lane < n_cand ? res : kNegInf;
-}
-
-// Walk from the root to level 1. Levels whose eligible node count is <= K keep every node, so the
-// walk starts below the highest level with more than K eligible nodes. Returns the number of kept
-// level-1 nodes; lane c < n holds the c-th (ascending). A pyramid of one leaf has the virtual
-// level-1 node 0.
-template <typename T, int D>
-__device__ int walk_to_level1(const NodeRows<T, D>& rows, const Levels& lv, const Frag<T> (&qf)[D / 32], int C, int K,
-                              int G, float scale, long long i, int* kept_out) {
-  const int lane = lane_id();
-  const int L = lv.n_levels - 1;
-  int lstar = 0;
-  for (int l = L; l >= 1; --l) {
-    if (i / ((long long)C << l) + 1 > K) {
-      lstar = l;
-      break;
-    }
-  }
-  int nk, kept;
-  if (lstar == 0) {
-    nk = (int)(i / (2LL * C) + 1);
-    *kept_out = lane < nk ? lane : -1;
-    return nk;
-  }
-  nk = (int)(i / ((long long)C << (lstar + 1)) + 1);
-  kept = lane < nk ? lane : -1;
-  for (int l = lstar; l >= 1; --l) {
-    const long long span = (long long)C << l;
-    const int par = __shfl(kept, lane >> 1);
-    const int cn = 2 * par + (lane & 1);
-    int n_cand = 2 * nk;
-    const int last = readlane(cn, n_cand - 1);
-    if ((long long)last * span > i) --n_cand;
-    if (n_cand <= K) {
-      kept = lane < n_cand ? cn : -1;
-      nk = n_cand;
-      continue;
-    }
-    const float sc = score_candidates<T, D>(rows, lv.off[l - 1], qf, cn, n_cand, (long long)C << (l - 1), i, G, scale);
-    const bool keep = topk_keep(sc, n_cand, K);
-    int cnt;
-    const int nxt = compact_lanes(keep, cn, &cnt);
-    kept = lane < cnt ? nxt : -1;
-    nk = cnt;
-  }
-  *kept_out = kept;
-  return nk;
-}
-
-// Key tile of leaves 2p and 2p+1: rows = tokens t0 .. t0+2C-1 of one KV head (zero past N).
-template <typename T, int D, int C>
-__device__ __forceinline__ void load_leaf_pair(const T* kbh, long long t0, int N, Frag<T> (&kf)[C / 8][D / 32]) {
-  const int r16 = lane_id() & 15, grp = lane_id() >> 4;
-#pragma unroll
-  for (int m = 0; m < C / 8; ++m) {
-    const long long t = t0 + 16 * m + r16;
-#pragma unroll
-    for (int s = 0; s < D / 32; ++s) {
-      if (t < N)
-        kf[m][s].load(kbh + t * D + (D / 4) * grp + 8 * s);
-      else
-        kf[m][s].zero();
-    }
-  }
-}
-
-// Per-column LSE over leaf 2p (lse0) and leaf 2p+1 (lse1) of scale * q_col . k_t for t <= icol.
-template <typename T, int D, int C>
-__device__ __forceinline__ void leaf_pair_lse(const Frag<T> (&kf)[C / 8][D / 32], const Frag<T> (&qf)[D / 32],
-                                              long long t0, long long icol, float scale, float& lse0, float& lse1) {
-  constexpr int MT = C / 8;
-  constexpr int ML = C / 16;  // M-tiles per leaf
-  const int grp = lane_id() >> 4;
-  f32x4 acc[MT];
-#pragma unroll
-  for (int m = 0; m < MT; ++m) acc[m] = zero4();
-#pragma unroll
-  for (int s = 0; s < D / 32; ++s) {
-#pragma unroll
-    for (int m = 0; m < MT; ++m) mma(acc[m], kf[m][s], qf[s]);
-  }
-#pragma unroll
-  for (int bit = 0; bit < 2; ++bit) {
-    float x[ML * 4];
-#pragma unroll
-    for (int mm = 0; mm < ML; ++mm) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const long long t = t0 + 16 * (bit * ML + mm) + 4 * grp + j;
-        x[mm * 4 + j] = t <= icol ? acc[bit * ML + mm][j] : kNegInf;
-      }
-    }
-    const float l = column_lse<ML * 4>(x, scale);
-    if (bit == 0)
-      lse0 = l;
-    else
-      lse1 = l;
-  }
-}
 
 template <typename T>
 struct RouteParams {
@@ -231,7 +45,7 @@ struct RouteParams {
 // (leaf 2*kept[slot] + bit); ell(c, h) gives its per-head LSE. The heads are summed in index order.
 template <typename F>
 __device__ __forceinline__ void leaf_topk_write(int n_cand, int leaf_c, int G, int K, long long u, long long qrow0,
-                                                long long qstride, F ell, int* sel, float* sel_lse) {
+                                                long long qstride, F ell, int* sel, float* sel_lse, float* s_sc) {
   const int lane = lane_id();
   const bool need_rank = n_cand > K;
   bool keep = lane < n_cand;
@@ -239,8 +53,10 @@ __device__ __forceinline__ void leaf_topk_write(int n_cand, int leaf_c, int G, i
     float sc = 0.f;
     if (lane < n_cand)
       for (int h = 0; h < G; ++h) sc += ell(lane, h);
-    sc = lane < n_cand ? sc : kNegInf;
-    keep = topk_keep(sc, n_cand, K);
+    s_sc[lane] = sc;
+    __threadfence_block();
+    keep = topk_keep_lds(s_sc, n_cand, K);
+    __threadfence_block();
   }
   int nsel;
   const int leaf_sel = compact_lanes(keep, leaf_c, &nsel);
@@ -253,9 +69,11 @@ __device__ __forceinline__ void leaf_topk_write(int n_cand, int leaf_c, int G, i
   }
 }
 
-template <typename T, int D, int C, bool FUSED>
-__global__ __launch_bounds__(256) void route_kernel(RouteParams<T> p) {
-  __shared__ float s_ell[4][64][17];
+template <typename T, int D, int C, bool FUSED, int KM>
+__global__ __launch_bounds__(256, 2) void route_kernel(RouteParams<T> p) {
+  constexpr int kLog2C = C == 64 ? 6 : 5;
+  __shared__ float s_ell[FUSED ? 4 : 1][64][17];
+  __shared__ __align__(16) float s_sc[4][64];
   const int lane = lane_id(), wave = threadIdx.x >> 6, r16 = lane & 15, grp = lane >> 4;
   const long long U = (long long)p.B * p.Hkv * p.N;
   const int lb = xcd_logical_block(gridDim.x);
@@ -269,11 +87,11 @@ __global__ __launch_bounds__(256) void route_kernel(RouteParams<T> p) {
     Frag<T> qf[D / 32];
     const bool hv = r16 < p.G;
     const long long qrow0 = ((long long)b * p.Hq + (long long)r * p.G) * p.N + i;
-    const T* qrow = p.q + (qrow0 + (long long)(hv ? r16 : 0) * p.N) * D + (D / 4) * grp;
+    const T* qrow = p.q + (qrow0 + (long long)(hv ? r16 : 0) * p.N) * D + 8 * grp;
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) {
       if (hv)
-        qf[s].load(qrow + 8 * s);
+        qf[s].load(qrow + 32 * s);
       else
         qf[s].zero();
     }
@@ -283,7 +101,7 @@ __global__ __launch_bounds__(256) void route_kernel(RouteParams<T> p) {
     else
       rows.base = (const float*)p.nodes + bh * p.lv.nodes * D;
     int kept;
-    const int nk = walk_to_level1<T, D>(rows, p.lv, qf, C, p.K, p.G, p.scale, i, &kept);
+    const int nk = walk_to_level1<T, D, KM>(rows, p.lv, qf, kLog2C, p.K, p.G, p.scale, (int)i, &kept, s_sc[wave]);
     if constexpr (!FUSED) {
       if (lane < p.K) p.kept[u * p.K + lane] = lane < nk ? kept : -1;
     } else {
@@ -303,14 +121,15 @@ __global__ __launch_bounds__(256) void route_kernel(RouteParams<T> p) {
           float l0, l1;
           leaf_pair_lse<T, D, C>(kf, qf, 2 * pn * C, i, p.scale, l0, l1);
           if (grp == 0 && hv) {
-            s_ell[wave][2 * slot][r16] = l0;
-            s_ell[wave][2 * slot + 1][r16] = l1;
+            s_ell[FUSED ? wave : 0][2 * slot][r16] = l0;
+            s_ell[FUSED ? wave : 0][2 * slot + 1][r16] = l1;
           }
         }
         __threadfence_block();
       }
       leaf_topk_write(
-          n_cand, leaf_c, p.G, p.K, u, qrow0, p.N, [&](int c, int h) { return s_ell[wave][c][h]; }, p.sel, p.sel_lse);
+          n_cand, leaf_c, p.G, p.K, u, qrow0, p.N, [&](int c, int h) { return s_ell[FUSED ? wave : 0][c][h]; }, p.sel,
+          p.sel_lse, s_sc[wave]);
       __threadfence_block();
     }
   }
@@ -328,71 +147,92 @@ struct LeafParams {
   float* leaf_lse;  // [U, K, 2, G]
 };
 
-constexpr int kLeafTask = 64;  // pairs per wave task
+constexpr int kLeafTask = 256;  // pairs per wave task
 
-// The tiled leaf stage: wave task t covers pairs [64 t, 64 t + 64) of the bucket-sorted list. Within
-// each run of one bucket (same KV head and level-1 node) the key tile is loaded once and tiles of
-// q_tile units x G heads are scored against it.
+// One tile of q_tile pairs x G heads (16 columns): the column's query fragments and its pair.
+template <typename T, int D>
+struct LeafTile {
+  Frag<T> qf[D / 32];
+  long long u;
+  int slot;
+  bool valid;
+};
+
+// The tiled leaf stage: wave task t covers pairs [256 t, 256 t + 256) of the bucket-sorted list. For
+// each run of one bucket (same KV head and level-1 node) the key tile is loaded once into registers
+// and tiles of q_tile units x G heads are scored against it; the query fragments of the tile two
+// ahead are in flight while a tile runs.
 template <typename T, int D, int C>
 __global__ __launch_bounds__(256) void leaf_lse_kernel(LeafParams<T> p) {
   const int lane = lane_id(), wave = threadIdx.x >> 6, r16 = lane & 15, grp = lane >> 4;
   const int task = xcd_logical_block(gridDim.x) * 4 + wave;
   const long long total = *p.total;
-  long long pos = (long long)task * kLeafTask;
-  if (task >= p.tasks || pos >= total) return;
-  const long long end = pos + kLeafTask < total ? pos + kLeafTask : total;
-  while (pos < end) {
-    const uint32_t pr = p.pairs[pos];
-    const long long u = pr >> 5;
-    const long long bh = u / p.N;
-    const int node = p.kept[u * p.K + (pr & 31)];
-    // end of this bucket's run inside [pos, end)
-    long long seg = end;
-    for (long long base = pos; base < end; base += 64) {
-      const long long x = base + lane;
-      bool diff = false;
-      if (x < end) {
-        const uint32_t q2 = p.pairs[x];
-        const long long u2 = q2 >> 5;
-        diff = (u2 / p.N != bh) || (p.kept[u2 * p.K + (q2 & 31)] != node);
-      }
-      const unsigned long long m = __ballot(diff);
-      if (m) {
-        seg = base + __ffsll((long long)m) - 1;
-        break;
-      }
-    }
+  const long long pos0 = (long long)task * kLeafTask;
+  if (task >= p.tasks || pos0 >= total) return;
+  PairRun run;
+  run.base = pos0;
+  run.end = pos0 + kLeafTask < total ? pos0 + kLeafTask : total;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const long long x = pos0 + 64 * w + lane;
+    run.pr[w] = x < run.end ? p.pairs[x] : 0u;
+  }
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const long long x = pos0 + 64 * w + lane;
+    const long long u = run.pr[w] >> 5;
+    run.key[w] = x < run.end ? (u / p.N) * (1LL << 32) + p.kept[u * p.K + (run.pr[w] & 31)] : -1;
+  }
+  const int h = r16 % p.G;
+  const int cols = p.q_tile * p.G;
+  long long pos = pos0;
+  while (pos < run.end) {
+    const uint32_t pr0 = run.pair(pos);
+    const long long u0 = readlane((int)(pr0 >> 5), 0);
+    const long long bh = u0 / p.N;
+    const int node = p.kept[u0 * p.K + (readlane((int)pr0, 0) & 31)];
+    const long long seg = run.run_end(pos, bh * (1LL << 32) + node);
     const T* kbh = p.k + bh * (long long)p.N * D;
     const long long t0 = 2LL * node * C;
     Frag<T> kf[C / 8][D / 32];
     load_leaf_pair<T, D, C>(kbh, t0, p.N, kf);
     const int b = (int)(bh / p.Hkv), r = (int)(bh % p.Hkv);
-    const int cols = p.q_tile * p.G;
-    for (long long tp = pos; tp < seg; tp += p.q_tile) {
+    const T* qhead = p.q + (((long long)b * p.Hq + (long long)r * p.G + h) * p.N) * D + 8 * grp;
+    const long long ubase = bh * p.N;
+    auto fetch = [&](LeafTile<T, D>& t, long long tp) {
       const long long pi = tp + r16 / p.G;
-      const int h = r16 % p.G;
-      const bool cv = r16 < cols && pi < seg;
-      long long uc = 0, ic = 0;
-      int slot = 0;
-      Frag<T> qf[D / 32];
-      if (cv) {
-        const uint32_t pc = p.pairs[pi];
-        uc = pc >> 5;
-        slot = pc & 31;
-        ic = uc % p.N;
-        const T* qrow = p.q + ((((long long)b * p.Hq + (long long)r * p.G + h) * p.N) + ic) * D + (D / 4) * grp;
+      t.valid = r16 < cols && pi < seg;
+      const uint32_t pc = run.pair(t.valid ? pi : pos);
+      t.u = pc >> 5;
+      t.slot = pc & 31;
+      const T* qrow = qhead + (t.u - ubase) * D;
 #pragma unroll
-        for (int s = 0; s < D / 32; ++s) qf[s].load(qrow + 8 * s);
-      } else {
-#pragma unroll
-        for (int s = 0; s < D / 32; ++s) qf[s].zero();
+      for (int s = 0; s < D / 32; ++s) {
+        if (t.valid)
+          t.qf[s].load(qrow + 32 * s);
+        else
+          t.qf[s].zero();
       }
+    };
+    auto score = [&](const LeafTile<T, D>& t) {
       float l0, l1;
-      leaf_pair_lse<T, D, C>(kf, qf, t0, cv ? ic : -1, p.scale, l0, l1);
-      if (grp == 0 && cv) {
-        float* dst = p.leaf_lse + ((uc * p.K + slot) * 2) * p.G + h;
+      leaf_pair_lse<T, D, C>(kf, t.qf, t0, t.valid ? t.u - ubase : -1, p.scale, l0, l1);
+      if (grp == 0 && t.valid) {
+        float* dst = p.leaf_lse + ((t.u * p.K + t.slot) * 2) * p.G + h;
         dst[0] = l0;
         dst[p.G] = l1;
+      }
+    };
+    const long long ntiles = (seg - pos + p.q_tile - 1) / p.q_tile;
+    LeafTile<T, D> X, Y;
+    fetch(X, pos);
+    if (ntiles > 1) fetch(Y, pos + p.q_tile);
+    for (long long t = 0; t < ntiles; t += 2) {
+      score(X);
+      if (t + 2 < ntiles) fetch(X, pos + (t + 2) * p.q_tile);
+      if (t + 1 < ntiles) {
+        score(Y);
+        if (t + 3 < ntiles) fetch(Y, pos + (t + 3) * p.q_tile);
       }
     }
     pos = seg;
@@ -409,6 +249,7 @@ struct FinParams {
 };
 
 __global__ __launch_bounds__(256) void finalize_kernel(FinParams<float> p) {
+  __shared__ __align__(16) float s_sc[4][64];
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const long long U = (long long)p.B * p.Hkv * p.N;
   const long long first = ((long long)xcd_logical_block(gridDim.x) * 4 + wave) * p.upw;
@@ -425,7 +266,8 @@ __global__ __launch_bounds__(256) void finalize_kernel(FinParams<float> p) {
     const long long qrow0 = ((long long)b * p.Hq + (long long)r * p.G) * p.N + i;
     const float* ll = p.leaf_lse + u * p.K * 2 * p.G;
     leaf_topk_write(
-        n_cand, leaf_c, p.G, p.K, u, qrow0, p.N, [&](int c, int h) { return ll[c * p.G + h]; }, p.sel, p.sel_lse);
+        n_cand, leaf_c, p.G, p.K, u, qrow0, p.N, [&](int c, int h) { return ll[c * p.G + h]; }, p.sel, p.sel_lse,
+        s_sc[wave]);
   }
 }
 
@@ -549,7 +391,10 @@ static hipError_t route_t(const SelDims& sd, const void* q, const void* k, const
   p.upw = 4;
   const long long waves = (U + p.upw - 1) / p.upw;
   const long long blocks = (waves + 3) / 4;
-  hipLaunchKernelGGL((route_kernel<T, D, C, FUSED>), dim3((unsigned)blocks), dim3(256), 0, st, p);
+  if (sd.K <= 16)
+    hipLaunchKernelGGL((route_kernel<T, D, C, FUSED, 4>), dim3((unsigned)blocks), dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL((route_kernel<T, D, C, FUSED, 8>), dim3((unsigned)blocks), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 

@@ -19,7 +19,8 @@ PISA_FP32, PISA_BF16 = 0, 1
 PISA_OP_SELECT, PISA_OP_ATTN, PISA_OP_DECODE, PISA_OP_BSA = 1, 2, 3, 4
 
 EXPORTED = ["pisa_pyramid_layout", "pisa_workspace_size", "pisa_build_pyramid", "pisa_select", "pisa_sparse_attn",
-            "pisa_decode_step", "bsa_select", "pisa_status_string", "pisa_last_error"]
+            "pisa_decode_step", "bsa_select", "pisa_status_string", "pisa_last_error", "pisa_stage_timing",
+            "pisa_stage_times"]
 
 
 class Shape(ctypes.Structure):
@@ -73,6 +74,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pisa_status_string.restype = ctypes.c_char_p
     lib.pisa_last_error.argtypes = []
     lib.pisa_last_error.restype = ctypes.c_char_p
+    lib.pisa_stage_timing.argtypes = [ctypes.c_int32]
+    lib.pisa_stage_timing.restype = ctypes.c_int
+    lib.pisa_stage_times.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32),
+                                     ctypes.c_int32]
+    lib.pisa_stage_times.restype = ctypes.c_int32
     _lib = lib
     return lib
 
@@ -151,6 +157,23 @@ def bsa_select(shape, q, k, sel, ws=None, stream=None):
     nbytes = ws.numel() * ws.element_size() if ws is not None else 0
     _check(load().bsa_select(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(sel), _ptr(ws), nbytes, _stream(stream)),
            "bsa_select")
+
+
+def pisa_stage_timing(enable: bool):
+    _check(load().pisa_stage_timing(1 if enable else 0), "pisa_stage_timing")
+
+
+def pisa_stage_times() -> dict:
+    """{stage name: (total ms, launches)} accumulated since stage timing was enabled."""
+    lib = load()
+    cap = 64
+    names = (ctypes.c_char * 32 * cap)()
+    tot = (ctypes.c_double * cap)()
+    cnt = (ctypes.c_int32 * cap)()
+    n = lib.pisa_stage_times(names, tot, cnt, cap)
+    if n < 0:
+        _check(n, "pisa_stage_times")
+    return {bytes(names[i]).split(b"\0")[0].decode(): (tot[i], cnt[i]) for i in range(min(n, cap))}
 
 
 # ------------------------------------------------------------------------------------- allocation helpers

@@ -1,0 +1,137 @@
+"""GPU parity of the fused decode step against the oracle's decode (incremental sum pyramid, then the
+walk and attention for query position p over the p+1 cached tokens).
+
+Selections must equal the oracle's on every unit-step whose oracle margin is >= 1e-3 and satisfy the
+invariants everywhere; outputs within 2e-2 (bf16) / 1e-5 (fp32) of the oracle attention on the GPU's own
+selection; after the steps the decode pyramid equals the oracle's rebuild."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from long_context_block_amd import inputs as I
+from long_context_block_amd import pisa as P
+
+from gpu_common import MARGIN, TOL_ATTN, check_invariants, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _shape(dec: I.Decode):
+    return P.make_shape(batch=dec.B, seq_len=dec.Nmax, n_q_heads=dec.Hq, n_kv_heads=dec.Hkv, head_dim=dec.d,
+                        block=dec.C, top_k=dec.K, q_tile=1, dtype=dec.dtype)
+
+
+def _run_decode(dec: I.Decode, check_units, check_all_steps=(), every_step_units=None):
+    """Runs all steps on the GPU; checks `check_units` [(b, r)] at every step and every unit at the steps in
+    check_all_steps. Returns the max attention error."""
+    s = _shape(dec)
+    kc = to_device(dec.k_cache)
+    vc = to_device(dec.v_cache)
+    rows = P.pyramid_rows(s)
+    psum = torch.zeros((rows, dec.d), dtype=torch.float32, device="cuda")
+    pmean = torch.zeros_like(psum)
+    lens = [int(x) for x in dec.lens0]
+    P.pisa_build_pyramid(s, kc, pmean, psum, host_lens=lens)
+    qn, kn, vn = to_device(dec.q_new), to_device(dec.k_new), to_device(dec.v_new)
+    o = torch.empty((dec.B, dec.Hq, dec.d), dtype=qn.dtype, device="cuda")
+    sel = torch.empty((dec.B, dec.Hkv, dec.K), dtype=torch.int32, device="cuda")
+    # oracle state for the checked units
+    all_units = [(b, r) for b in range(dec.B) for r in range(dec.Hkv)]
+    tracked = sorted(set(check_units) | (set(all_units) if check_all_steps else set()))
+    st = {}
+    for (b, r) in tracked:
+        n0 = lens[b]
+        kh = np.zeros((dec.Nmax, dec.d))
+        vh = np.zeros((dec.Nmax, dec.d))
+        kh[:n0] = dec.k_cache.f64((b, r, slice(0, n0)))
+        vh[:n0] = dec.v_cache.f64((b, r, slice(0, n0)))
+        sp = O.empty_sum_pyramid(dec.Nmax, dec.d, dec.C)
+        base = O.build_pyramid(kh[:n0], dec.C, 2)
+        for l in range(len(base.means)):
+            sp.sums[l][:base.means[l].shape[0]] = base.means[l] * base.counts[l][:, None]
+            sp.counts[l][:base.counts[l].shape[0]] = base.counts[l]
+        st[(b, r)] = (kh, vh, sp)
+    worst = 0.0
+    mism = []
+    decided = total = 0
+    for step in range(dec.steps):
+        P.pisa_decode_step(s, lens, qn[step], kn[step], vn[step], kc, vc, psum, pmean, o, sel)
+        torch.cuda.synchronize()
+        units = all_units if step in check_all_steps else check_units
+        if units:
+            on = o.float().cpu().numpy()
+            sn = sel.cpu().numpy()
+        for (b, r) in units:
+            kh, vh, sp = st[(b, r)]
+            p_ = lens[b]
+            qg = dec.q_new.f64((step, b, slice(r * dec.G, (r + 1) * dec.G)))
+            us, _, _ = O.decode_step_unit(qg, kh, vh, sp, p_, dec.k_new.f64((step, b, r)),
+                                          dec.v_new.f64((step, b, r)), dec.K, 1.0 / math.sqrt(dec.d))
+            total += 1
+            assert check_invariants(sn[b, r], p_, dec.C, dec.K), (step, b, r, sn[b, r])
+            if us.margin >= MARGIN:
+                decided += 1
+                if sn[b, r].tolist() != us.sel.tolist():
+                    mism.append((step, b, r, sn[b, r].tolist(), us.sel.tolist(), us.margin))
+            o_ref, _ = O.attend_unit(qg, kh, vh, sn[b, r], p_, dec.C, 1.0 / math.sqrt(dec.d), p_ + 1)
+            worst = max(worst, float(np.abs(on[b, r * dec.G:(r + 1) * dec.G] - o_ref).max()))
+        # units not checked this step still advance the oracle state
+        for (b, r) in tracked:
+            if (b, r) in units:
+                continue
+            kh, vh, sp = st[(b, r)]
+            p_ = lens[b]
+            kh[p_] = dec.k_new.f64((step, b, r))
+            vh[p_] = dec.v_new.f64((step, b, r))
+            O.sum_pyramid_append(sp, p_, kh[p_])
+        lens = [x + 1 for x in lens]
+        if step % 32 == 0:
+            say(f"[decode] step {step}: checked {total} unit-steps, {decided} decided, {len(mism)} mismatches, "
+                f"attn err {worst:.3g}")
+    say(f"[decode] done: {total} unit-steps, {decided} decided, mismatches {len(mism)}, attn err {worst:.3g}")
+    assert not mism, mism[:5]
+    assert worst <= TOL_ATTN[dec.dtype], worst
+    # decode pyramid == oracle rebuild of the final prefix, for the tracked units
+    n, offs, nodes = P.pisa_pyramid_layout(s)
+    pm = pmean.cpu().numpy()
+    ck = kc.float().cpu().numpy() if dec.dtype == "bf16" else kc.cpu().numpy()
+    perr = 0.0
+    for (b, r) in tracked[:4]:
+        kh = st[(b, r)][0]
+        np.testing.assert_array_equal(ck[b, r, :lens[b]], kh[:lens[b]].astype(np.float32))
+        reb = O.build_pyramid(kh[:lens[b]], dec.C, 2)
+        base = (b * dec.Hkv + r) * nodes
+        for l in range(len(reb.means)):
+            got = pm[base + offs[l]: base + offs[l] + reb.means[l].shape[0]]
+            perr = max(perr, float(np.abs(got - reb.means[l]).max()))
+    say(f"[decode] pyramid max abs err {perr:.3g}")
+    assert perr <= 2e-5
+    return worst
+
+
+@pytest.mark.parametrize("dtype,d,C,K,G", [("bf16", 128, 64, 4, 4), ("bf16", 64, 32, 6, 2), ("fp32", 64, 32, 4, 1),
+                                         ("bf16", 128, 64, 16, 8)])
+def test_decode_small_every_step(dtype, d, C, K, G):
+    Hkv = 2
+    dec = I.make_decode(B=2, Hq=G * Hkv, Hkv=Hkv, N0=[300, 129], d=d, C=C, K=K, steps=70, Nmax=400, dtype=dtype,
+                        seed=0, workload_id=300)
+    units = [(b, r) for b in range(2) for r in range(Hkv)]
+    _run_decode(dec, units)
+
+
+def test_decode_from_tiny_cache():
+    # the cache starts with one token: the tree grows from a single leaf
+    dec = I.make_decode(B=1, Hq=4, Hkv=1, N0=1, d=128, C=64, K=4, steps=300, Nmax=512, dtype="bf16", seed=0,
+                        workload_id=301)
+    _run_decode(dec, [(0, 0)])
+
+
+@pytest.mark.timeout(1200)
+def test_decode_128k_full_size():
+    say("[decode] generating decode_128k")
+    dec = I.make_workload("decode_128k")
+    say(f"[decode] B={dec.B} Hq={dec.Hq} Hkv={dec.Hkv} N0={int(dec.lens0[0])} Nmax={dec.Nmax} steps={dec.steps}")
+    _run_decode(dec, [(0, 0), (3, 5), (7, 7)], check_all_steps=(0, dec.steps - 1))
