@@ -10,7 +10,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/pisa.h"
+#include "pisa.h"
 #include "internal.hpp"
 
 namespace {
@@ -96,7 +96,8 @@ struct Plan {
   pisa::SelDims sd;
   long long U;       // units B*Hkv*N
   long long BH;
-  int n1_buckets;    // buckets per KV head for the selection regroup (level-1 nodes, at least 1)
+  int n1_buckets;    // buckets per KV head and chunk for the selection regroup (level-1 nodes, at least 1)
+  int nch;           // position chunks per KV head
   size_t elem;       // bytes per Q/K/V element
 };
 
@@ -160,6 +161,10 @@ pisa_status plan(const pisa_shape* s, Plan* pl) {
   p.BH = (long long)s->batch * s->n_kv_heads;
   p.n1_buckets = p.sd.lv.n_levels > 1 ? p.sd.lv.n[1] : 1;
   p.elem = p.sd.bf16 ? 2 : 4;
+  // Pairs may be bucketed per position chunk (2^chunk_log2 positions) so that a run of buckets gathers
+  // the queries of one chunk; measured slower on MI355X than one chunk per KV head, so one chunk.
+  p.sd.chunk_log2 = 30;
+  p.nch = 1;
   *pl = p;
   return PISA_OK;
 }
@@ -180,6 +185,7 @@ struct Carver {
 
 struct SelectWs {
   uint16_t* hilo;
+  float* norms;
   int* kept;
   int* counts;
   int* offsets;
@@ -191,10 +197,13 @@ struct SelectWs {
 size_t carve_select(const Plan& p, void* ws, SelectWs* w) {
   Carver c(ws);
   SelectWs x{};
-  if (p.sd.bf16) x.hilo = (uint16_t*)c.take((size_t)p.BH * p.sd.lv.nodes * 2 * p.sd.D * 2);
+  if (p.sd.bf16) {
+    x.hilo = (uint16_t*)c.take((size_t)p.BH * p.sd.lv.nodes * 2 * p.sd.D * 2);
+    x.norms = (float*)c.take((size_t)p.BH * p.sd.lv.nodes * 4);
+  }
   if (p.sd.q_tile > 1) {
     const size_t pairs = (size_t)p.U * p.sd.K;
-    const size_t NB = (size_t)p.BH * p.n1_buckets;
+    const size_t NB = (size_t)p.BH * p.nch * p.n1_buckets;
     x.kept = (int*)c.take(pairs * 4);
     x.counts = (int*)c.take(NB * 4);
     x.offsets = (int*)c.take((NB + 1) * 4);
@@ -219,7 +228,7 @@ size_t carve_attn(const Plan& p, void* ws, AttnWs* w) {
   Carver c(ws);
   AttnWs x{};
   const size_t pairs = (size_t)p.U * p.sd.K;
-  const size_t NB = (size_t)p.BH * p.sd.lv.n[0];
+  const size_t NB = (size_t)p.BH * p.nch * p.sd.lv.n[0];
   x.counts = (int*)c.take(NB * 4);
   x.offsets = (int*)c.take((NB + 1) * 4);
   x.ranks = (int*)c.take(pairs * 4);
@@ -358,6 +367,7 @@ pisa_status pisa_select(const pisa_shape* shape, const void* q, const void* k, c
     {
       Stage sc(s, "split_hilo");
       e = pisa::launch_split_hilo(pyr_mean, p.BH * p.sd.lv.nodes, p.sd.D, w.hilo, s);
+      if (e == hipSuccess) e = pisa::launch_row_norms(pyr_mean, p.BH * p.sd.lv.nodes, p.sd.D, w.norms, s);
     }
     if (e != hipSuccess) return hip_status(e, "split_hilo");
     nodes = w.hilo;
@@ -365,22 +375,22 @@ pisa_status pisa_select(const pisa_shape* shape, const void* q, const void* k, c
   if (p.sd.q_tile == 1) {
     {
       Stage sc(s, "route_fused_leaf");
-      e = pisa::launch_route(p.sd, q, k, nodes, true, nullptr, sel, sel_lse, s);
+      e = pisa::launch_route(p.sd, q, k, nodes, w.norms, true, nullptr, sel, sel_lse, s);
     }
     return hip_status(e, "route (fused leaf stage)");
   }
   {
     Stage sc(s, "route");
-    e = pisa::launch_route(p.sd, q, k, nodes, false, w.kept, nullptr, nullptr, s);
+    e = pisa::launch_route(p.sd, q, k, nodes, w.norms, false, w.kept, nullptr, nullptr, s);
   }
   if (e != hipSuccess) return hip_status(e, "route");
   {
     Stage sc(s, "regroup_select");
-    e = pisa::launch_regroup(w.kept, p.U, p.sd.K, p.sd.N, p.n1_buckets, (int)p.BH, w.counts, w.offsets, w.ranks,
-                             w.pairs, s);
+    e = pisa::launch_regroup(w.kept, p.U, p.sd.K, p.sd.N, p.n1_buckets, (int)p.BH, p.sd.chunk_log2, w.counts,
+                             w.offsets, w.ranks, w.pairs, s);
   }
   if (e != hipSuccess) return hip_status(e, "regroup");
-  const int* total = w.offsets + p.BH * p.n1_buckets;
+  const int* total = w.offsets + p.BH * p.nch * p.n1_buckets;
   {
     Stage sc(s, "leaf_lse");
     e = pisa::launch_leaf_lse(p.sd, q, k, w.kept, w.pairs, total, w.leaf_lse, s);
@@ -413,11 +423,11 @@ pisa_status pisa_sparse_attn(const pisa_shape* shape, const void* q, const void*
   hipError_t e;
   {
     Stage sc(s, "regroup_attn");
-    e = pisa::launch_regroup(sel, p.U, p.sd.K, p.sd.N, p.sd.lv.n[0], (int)p.BH, w.counts, w.offsets, w.ranks,
-                             w.pairs, s);
+    e = pisa::launch_regroup(sel, p.U, p.sd.K, p.sd.N, p.sd.lv.n[0], (int)p.BH, p.sd.chunk_log2, w.counts,
+                             w.offsets, w.ranks, w.pairs, s);
   }
   if (e != hipSuccess) return hip_status(e, "regroup");
-  const int* total = w.offsets + p.BH * p.sd.lv.n[0];
+  const int* total = w.offsets + p.BH * p.nch * p.sd.lv.n[0];
   {
     Stage sc(s, "attn_leaf");
     e = pisa::launch_attn_leaf(p.sd, q, k, v, sel, w.pairs, total, w.part, w.part_lse, s);

@@ -24,7 +24,7 @@ struct AttnParams {
   const int* sel;
   const uint32_t* pairs;
   const int* total;
-  int B, Hq, Hkv, G, N, K, tasks;
+  int B, Hq, Hkv, G, N, K, tasks, chunk_log2;
   float scale;
   T* part;         // [U, K, G, D]
   float* part_lse; // [U, K, G]
@@ -48,6 +48,7 @@ __global__ __launch_bounds__(256) void attn_leaf_kernel(AttnParams<T> p) {
   PairRun run;
   run.base = pos0;
   run.end = pos0 + kAttnTask < total ? pos0 + kAttnTask : total;
+  const long long nch = ((long long)p.N + (1LL << p.chunk_log2) - 1) >> p.chunk_log2;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
     const long long x = pos0 + 64 * w + lane;
@@ -57,7 +58,9 @@ __global__ __launch_bounds__(256) void attn_leaf_kernel(AttnParams<T> p) {
   for (int w = 0; w < 4; ++w) {
     const long long x = pos0 + 64 * w + lane;
     const long long u = run.pr[w] >> 5;
-    run.key[w] = x < run.end ? (u / p.N) * (1LL << 32) + p.sel[u * p.K + (run.pr[w] & 31)] : -1;
+    run.key[w] = x < run.end ? ((u / p.N) * nch + ((u % p.N) >> p.chunk_log2)) * (1LL << 32) +
+                                   p.sel[u * p.K + (run.pr[w] & 31)]
+                             : -1;
   }
   long long pos = pos0;
   while (pos < run.end) {
@@ -65,7 +68,7 @@ __global__ __launch_bounds__(256) void attn_leaf_kernel(AttnParams<T> p) {
     const long long u0 = readlane((int)(pr0 >> 5), 0);
     const long long bh = u0 / p.N;
     const int leaf = p.sel[u0 * p.K + (readlane((int)pr0, 0) & 31)];
-    const long long seg = run.run_end(pos, bh * (1LL << 32) + leaf);
+    const long long seg = run.run_end(pos, (bh * nch + ((u0 % p.N) >> p.chunk_log2)) * (1LL << 32) + leaf);
     const long long t0 = (long long)leaf * C;
     const T* kbh = p.k + bh * (long long)p.N * D;
     const T* vbh = p.v + bh * (long long)p.N * D;
@@ -209,6 +212,7 @@ static hipError_t attn_leaf_t(const SelDims& sd, const void* q, const void* k, c
   p.G = sd.G;
   p.N = sd.N;
   p.K = sd.K;
+  p.chunk_log2 = sd.chunk_log2;
   p.scale = sd.scale;
   p.part = (T*)part;
   p.part_lse = part_lse;

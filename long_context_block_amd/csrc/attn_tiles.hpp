@@ -95,12 +95,13 @@ __device__ __forceinline__ void attend_tile(const Frag<T> (&kf)[C / 16][D / 32],
 #pragma unroll
     for (int m = 0; m < MS; ++m) mma(sacc[m], kf[m][s], qf[s]);
   float mx = kNegInf;
+  const long long lim64 = ic - t0;
+  const int lim = lim64 < 0 ? -1 : (lim64 > C ? C : (int)lim64);
 #pragma unroll
   for (int m = 0; m < MS; ++m)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const long long t = t0 + attn_token(m, grp, j);
-      const float x = t <= ic ? sacc[m][j] : kNegInf;
+      const float x = attn_token(m, grp, j) <= lim ? sacc[m][j] : kNegInf;
       sacc[m][j] = x;
       mx = fmaxf(mx, x);
     }

@@ -103,15 +103,34 @@ __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// Max / sum over the 4 lane groups that hold one tile column (lanes c, c+16, c+32, c+48).
-// Every lane of the column ends with the same, order-fixed result.
+// Max / sum over the 4 lane groups that hold one tile column (lanes c, c+16, c+32, c+48), on the
+// gfx950 lane-swap instructions (VALU, no LDS round trip). v_permlane16_swap(v, v) returns, in every
+// lane, the pair (value of the lower 16-lane row, value of the upper row) of its row pair, and
+// v_permlane32_swap(v, v) the pair (lower half, upper half); combining the two halves of the pair in
+// that order gives every lane of the column the same, order-fixed result.
+__device__ __forceinline__ void swap16(float v, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap32(float v, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
+}
 __device__ __forceinline__ float colgroup_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  return fmaxf(v, __shfl_xor(v, 32));
+  float a, b;
+  swap16(v, a, b);
+  v = fmaxf(a, b);
+  swap32(v, a, b);
+  return fmaxf(a, b);
 }
 __device__ __forceinline__ float colgroup_sum(float v) {
-  v += __shfl_xor(v, 16);
-  return v + __shfl_xor(v, 32);
+  float a, b;
+  swap16(v, a, b);
+  v = a + b;
+  swap32(v, a, b);
+  return a + b;
 }
 
 // LSE of scale * x over the NV values this lane holds for a column plus those of the column's
@@ -152,20 +171,43 @@ __device__ __forceinline__ float row_sum16(float v) {
   return v + dpp_rot<0x121>(v);  // row_ror:1
 }
 
-// Candidates c in [0, n) have scores s[c] (LDS, this wave's 64-entry slice) in ascending node order.
-// True for the lanes among the K best by (score descending, node ascending). n, K wave-uniform.
-__device__ __forceinline__ bool topk_keep_lds(const float* s, int n, int K) {
+// Wave-uniform read of lane c.
+__device__ __forceinline__ int readlane(int v, int c) { return __builtin_amdgcn_readlane(v, c); }
+__device__ __forceinline__ float readlane(float v, int c) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), c));
+}
+
+// Top-K ranking key of candidate c with score v: the order-preserving unsigned image of the float with
+// its 6 low bits replaced by 63 - c, so that a larger key means a higher score, and exactly equal
+// scores order by the lower index. Scores closer than 2^-17 relative also order by index; only such
+// near-ties can rank differently from an exact float comparison.
+__device__ __forceinline__ uint32_t topk_key(float v, int c) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (o & ~63u) | (uint32_t)(63 - c);
+}
+
+// Candidates c in [0, n) (ascending node order, one per lane) with scores `score`. True for the lanes
+// among the K best (score descending, index ascending). keys: this wave's 64-entry LDS slice. n, K are
+// wave-uniform.
+__device__ __forceinline__ bool topk_keep(float score, int n, int K, uint32_t* keys) {
   const int lane = lane_id();
-  const float mine = s[lane < n ? lane : 0];
+  const uint32_t mine = lane < n ? topk_key(score, lane) : 0u;
+  keys[lane] = mine;
+  __threadfence_block();
   int rank = 0;
   for (int c = 0; c < n; c += 4) {
-    const float4 v = *reinterpret_cast<const float4*>(s + c);
-    rank += (c + 0 < n) && (v.x > mine || (v.x == mine && c + 0 < lane));
-    rank += (c + 1 < n) && (v.y > mine || (v.y == mine && c + 1 < lane));
-    rank += (c + 2 < n) && (v.z > mine || (v.z == mine && c + 2 < lane));
-    rank += (c + 3 < n) && (v.w > mine || (v.w == mine && c + 3 < lane));
+    const uint4 v = *reinterpret_cast<const uint4*>(keys + c);
+    rank += (v.x > mine) + (v.y > mine) + (v.z > mine) + (v.w > mine);
   }
+  __threadfence_block();
   return lane < n && rank < K;
+}
+
+// Same, with the scores already in s[0, n) (LDS).
+__device__ __forceinline__ bool topk_keep_lds(const float* s, int n, int K, uint32_t* keys) {
+  const int lane = lane_id();
+  return topk_keep(s[lane < n ? lane : 0], n, K, keys);
 }
 
 // Stable compaction: lanes with keep move to [0, count) in lane order, the others after them.
@@ -209,11 +251,23 @@ struct PairRun {
   }
 };
 
-// Wave-uniform read of lane c.
-__device__ __forceinline__ int readlane(int v, int c) { return __builtin_amdgcn_readlane(v, c); }
-__device__ __forceinline__ float readlane(float v, int c) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), c));
+// Max / min over all 64 lanes of the wave (every lane gets the result): DPP row reductions, then the
+// four row results read back with readlane.
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_rot<0x128>(v));
+  v = fmaxf(v, dpp_rot<0x124>(v));
+  v = fmaxf(v, dpp_rot<0x122>(v));
+  v = fmaxf(v, dpp_rot<0x121>(v));
+  return fmaxf(fmaxf(readlane(v, 0), readlane(v, 16)), fmaxf(readlane(v, 32), readlane(v, 48)));
 }
+__device__ __forceinline__ float wave_min(float v) {
+  v = fminf(v, dpp_rot<0x128>(v));
+  v = fminf(v, dpp_rot<0x124>(v));
+  v = fminf(v, dpp_rot<0x122>(v));
+  v = fminf(v, dpp_rot<0x121>(v));
+  return fminf(fminf(readlane(v, 0), readlane(v, 16)), fminf(readlane(v, 32), readlane(v, 48)));
+}
+
 
 // Work-group index remapped so that consecutive logical indices run on the same XCD (dispatch
 // places work-group w on XCD w % 8), keeping each XCD's L2 on a contiguous slice of the work.

@@ -49,6 +49,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams<T> p) {
   constexpr int MO = D / 16;
   __shared__ __align__(16) unsigned char s_buf[UNION];
   __shared__ __align__(16) float s_sc[64];
+  __shared__ __align__(16) uint32_t s_key[64];
   __shared__ float s_ell[64][17];
   __shared__ int s_kept[64];
   __shared__ int s_sel[64];
@@ -155,7 +156,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams<T> p) {
         rows.base = reinterpret_cast<const T*>(s_buf);
         const int cn = lane < n_cand ? 2 * s_kept[lane >> 1] + (lane & 1) : -1;
         score_candidates<T, D, KM, StagedRows<T, D>>(rows, 0, qf, cn, n_cand, e_child, p.G, p.scale, s_sc);
-        const bool keep = topk_keep_lds(s_sc, n_cand, K);
+        const bool keep = topk_keep_lds(s_sc, n_cand, K, s_key);
         int cnt;
         const int nxt = compact_lanes(keep, cn, &cnt);
         s_kept[lane] = lane < cnt ? nxt : -1;
@@ -190,9 +191,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams<T> p) {
       float sc = 0.f;
       if (lane < n_cand)
         for (int h = 0; h < p.G; ++h) sc += s_ell[lane][h];
-      s_sc[lane] = sc;
-      __threadfence_block();
-      keep = topk_keep_lds(s_sc, n_cand, K);
+      keep = topk_keep(sc, n_cand, K, s_key);
     }
     int nsel;
     const int leaf = compact_lanes(keep, leaf_c, &nsel);

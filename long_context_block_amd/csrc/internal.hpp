@@ -26,6 +26,7 @@ struct PyrDims {
 
 struct SelDims {
   int B, Hq, Hkv, G, N, D, C, K, q_tile;
+  int chunk_log2;  // pairs are bucketed per position chunk of 2^chunk_log2 units (>= 10)
   float scale;
   bool bf16;
   Levels lv;
@@ -36,13 +37,15 @@ hipError_t launch_pool(const void* k, bool bf16, const PyrDims& pd, LensArg lens
 hipError_t launch_split_hilo(const float* mean, long long rows, int D, uint16_t* hilo, hipStream_t st);
 
 // Selection. `nodes` is the bf16 hi/lo pyramid (bf16 inputs) or the fp32 means (fp32 inputs).
-hipError_t launch_route(const SelDims& sd, const void* q, const void* k, const void* nodes, bool fused, int* kept,
-                        int* sel, float* sel_lse, hipStream_t st);
+hipError_t launch_route(const SelDims& sd, const void* q, const void* k, const void* nodes, const float* norms,
+                        bool fused, int* kept, int* sel, float* sel_lse, hipStream_t st);
+// |row| (Euclidean norm over d) of each fp32 pyramid row.
+hipError_t launch_row_norms(const float* mean, long long rows, int D, float* norms, hipStream_t st);
 
 // Bucket (unit, slot) pairs by node: node lists [U, K] (-1 = none) -> pairs sorted by
 // (b*Hkv + r, node), packed as (unit << 5) | slot. counts/offsets have n_buckets (+1) entries.
 hipError_t launch_regroup(const int* nodes, long long U, int K, int N, int buckets_per_head, int n_heads,
-                          int* counts, int* offsets, int* ranks, uint32_t* pairs, hipStream_t st);
+                          int chunk_log2, int* counts, int* offsets, int* ranks, uint32_t* pairs, hipStream_t st);
 
 hipError_t launch_leaf_lse(const SelDims& sd, const void* q, const void* k, const int* kept, const uint32_t* pairs,
                            const int* total, float* leaf_lse, hipStream_t st);

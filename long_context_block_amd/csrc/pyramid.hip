@@ -171,6 +171,22 @@ __global__ __launch_bounds__(256) void split_hilo_kernel(const float* __restrict
   }
 }
 
+// Euclidean norm of each fp32 row (one wave per row).
+__global__ __launch_bounds__(256) void row_norms_kernel(const float* __restrict__ mean, long long rows, int D,
+                                                       float* __restrict__ norms) {
+  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int lane = threadIdx.x & 63;
+  float s = 0.f;
+  for (int c = lane; c < D; c += 64) {
+    const float x = mean[row * D + c];
+    s += x * x;
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) s += __shfl_xor(s, o);
+  if (lane == 0) norms[row] = sqrtf(s);
+}
+
 // ------------------------------------------------------------------------------------------ host
 template <typename T, int D>
 static hipError_t launch_pool_t(const T* k, const PyrDims& pd, LensArg lens, int max_level, float* mean, float* sum,
@@ -197,6 +213,11 @@ hipError_t launch_pool(const void* k, bool bf16, const PyrDims& pd, LensArg lens
   }
   if (pd.D == 128) return launch_pool_t<float, 128>((const float*)k, pd, lens, max_level, mean, sum, st);
   return launch_pool_t<float, 64>((const float*)k, pd, lens, max_level, mean, sum, st);
+}
+
+hipError_t launch_row_norms(const float* mean, long long rows, int D, float* norms, hipStream_t st) {
+  hipLaunchKernelGGL(row_norms_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, mean, rows, D, norms);
+  return hipGetLastError();
 }
 
 hipError_t launch_split_hilo(const float* mean, long long rows, int D, uint16_t* hilo, hipStream_t st) {

@@ -33,6 +33,7 @@ struct RouteParams {
   const T* q;
   const T* k;
   const void* nodes;
+  const float* norms;  // |mean| per pyramid row (bf16 path)
   int B, Hq, Hkv, G, N, K, upw;
   float scale;
   Levels lv;
@@ -45,7 +46,7 @@ struct RouteParams {
 // (leaf 2*kept[slot] + bit); ell(c, h) gives its per-head LSE. The heads are summed in index order.
 template <typename F>
 __device__ __forceinline__ void leaf_topk_write(int n_cand, int leaf_c, int G, int K, long long u, long long qrow0,
-                                                long long qstride, F ell, int* sel, float* sel_lse, float* s_sc) {
+                                                long long qstride, F ell, int* sel, float* sel_lse, uint32_t* keys) {
   const int lane = lane_id();
   const bool need_rank = n_cand > K;
   bool keep = lane < n_cand;
@@ -53,10 +54,7 @@ __device__ __forceinline__ void leaf_topk_write(int n_cand, int leaf_c, int G, i
     float sc = 0.f;
     if (lane < n_cand)
       for (int h = 0; h < G; ++h) sc += ell(lane, h);
-    s_sc[lane] = sc;
-    __threadfence_block();
-    keep = topk_keep_lds(s_sc, n_cand, K);
-    __threadfence_block();
+    keep = topk_keep(sc, n_cand, K, keys);
   }
   int nsel;
   const int leaf_sel = compact_lanes(keep, leaf_c, &nsel);
@@ -74,6 +72,7 @@ __global__ __launch_bounds__(256, 2) void route_kernel(RouteParams<T> p) {
   constexpr int kLog2C = C == 64 ? 6 : 5;
   __shared__ float s_ell[FUSED ? 4 : 1][64][17];
   __shared__ __align__(16) float s_sc[4][64];
+  __shared__ __align__(16) uint32_t s_key[4][64];
   const int lane = lane_id(), wave = threadIdx.x >> 6, r16 = lane & 15, grp = lane >> 4;
   const long long U = (long long)p.B * p.Hkv * p.N;
   const int lb = xcd_logical_block(gridDim.x);
@@ -101,7 +100,30 @@ __global__ __launch_bounds__(256, 2) void route_kernel(RouteParams<T> p) {
     else
       rows.base = (const float*)p.nodes + bh * p.lv.nodes * D;
     int kept;
-    const int nk = walk_to_level1<T, D, KM>(rows, p.lv, qf, kLog2C, p.K, p.G, p.scale, (int)i, &kept, s_sc[wave]);
+    int nk;
+    if constexpr (sizeof(T) == 2) {
+      // sum over the group's heads of |q_h| (lane r16 = head holds its d/4 elements per lane group)
+      float sq = 0.f;
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = qf[s].get(e);
+          sq += x * x;
+        }
+      const float sq_all = colgroup_sum(sq);  // every lane takes part in the exchange
+      const float qn = row_sum16(hv ? sqrtf(sq_all) : 0.f);
+      const float* norms = p.norms + bh * p.lv.nodes;
+      nk = walk_to_level1<T, D, KM>(p.lv, kLog2C, p.K, (int)i, &kept, [&](int off, int cn, int n_cand, int e_child) {
+        return select_level_refine<D, KM>(rows, norms, off, qf, qn, cn, n_cand, e_child, p.G, p.scale, p.K, s_sc[wave],
+                                          s_key[wave]);
+      });
+    } else {
+      nk = walk_to_level1<T, D, KM>(p.lv, kLog2C, p.K, (int)i, &kept, [&](int off, int cn, int n_cand, int e_child) {
+        score_candidates<T, D, KM>(rows, off, qf, cn, n_cand, e_child, p.G, p.scale, s_sc[wave]);
+        return topk_keep_lds(s_sc[wave], n_cand, p.K, s_key[wave]);
+      });
+    }
     if constexpr (!FUSED) {
       if (lane < p.K) p.kept[u * p.K + lane] = lane < nk ? kept : -1;
     } else {
@@ -129,7 +151,7 @@ __global__ __launch_bounds__(256, 2) void route_kernel(RouteParams<T> p) {
       }
       leaf_topk_write(
           n_cand, leaf_c, p.G, p.K, u, qrow0, p.N, [&](int c, int h) { return s_ell[FUSED ? wave : 0][c][h]; }, p.sel,
-          p.sel_lse, s_sc[wave]);
+          p.sel_lse, s_key[wave]);
       __threadfence_block();
     }
   }
@@ -142,7 +164,7 @@ struct LeafParams {
   const int* kept;
   const uint32_t* pairs;
   const int* total;
-  int B, Hq, Hkv, G, N, K, q_tile, tasks;
+  int B, Hq, Hkv, G, N, K, q_tile, tasks, chunk_log2;
   float scale;
   float* leaf_lse;  // [U, K, 2, G]
 };
@@ -172,6 +194,7 @@ __global__ __launch_bounds__(256) void leaf_lse_kernel(LeafParams<T> p) {
   PairRun run;
   run.base = pos0;
   run.end = pos0 + kLeafTask < total ? pos0 + kLeafTask : total;
+  const long long nch = ((long long)p.N + (1LL << p.chunk_log2) - 1) >> p.chunk_log2;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
     const long long x = pos0 + 64 * w + lane;
@@ -181,7 +204,9 @@ __global__ __launch_bounds__(256) void leaf_lse_kernel(LeafParams<T> p) {
   for (int w = 0; w < 4; ++w) {
     const long long x = pos0 + 64 * w + lane;
     const long long u = run.pr[w] >> 5;
-    run.key[w] = x < run.end ? (u / p.N) * (1LL << 32) + p.kept[u * p.K + (run.pr[w] & 31)] : -1;
+    run.key[w] = x < run.end ? ((u / p.N) * nch + ((u % p.N) >> p.chunk_log2)) * (1LL << 32) +
+                                   p.kept[u * p.K + (run.pr[w] & 31)]
+                             : -1;
   }
   const int h = r16 % p.G;
   const int cols = p.q_tile * p.G;
@@ -191,7 +216,7 @@ __global__ __launch_bounds__(256) void leaf_lse_kernel(LeafParams<T> p) {
     const long long u0 = readlane((int)(pr0 >> 5), 0);
     const long long bh = u0 / p.N;
     const int node = p.kept[u0 * p.K + (readlane((int)pr0, 0) & 31)];
-    const long long seg = run.run_end(pos, bh * (1LL << 32) + node);
+    const long long seg = run.run_end(pos, (bh * nch + ((u0 % p.N) >> p.chunk_log2)) * (1LL << 32) + node);
     const T* kbh = p.k + bh * (long long)p.N * D;
     const long long t0 = 2LL * node * C;
     Frag<T> kf[C / 8][D / 32];
@@ -249,7 +274,7 @@ struct FinParams {
 };
 
 __global__ __launch_bounds__(256) void finalize_kernel(FinParams<float> p) {
-  __shared__ __align__(16) float s_sc[4][64];
+  __shared__ __align__(16) uint32_t s_key[4][64];
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const long long U = (long long)p.B * p.Hkv * p.N;
   const long long first = ((long long)xcd_logical_block(gridDim.x) * 4 + wave) * p.upw;
@@ -267,7 +292,7 @@ __global__ __launch_bounds__(256) void finalize_kernel(FinParams<float> p) {
     const float* ll = p.leaf_lse + u * p.K * 2 * p.G;
     leaf_topk_write(
         n_cand, leaf_c, p.G, p.K, u, qrow0, p.N, [&](int c, int h) { return ll[c * p.G + h]; }, p.sel, p.sel_lse,
-        s_sc[wave]);
+        s_key[wave]);
   }
 }
 
@@ -282,17 +307,22 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(int* x, long long n) {
 constexpr int kRegroupUnits = 1024;
 
 __global__ __launch_bounds__(256) void hist_kernel(const int* __restrict__ nodes, int K, int N, int nb, int chunks,
-                                                   int use_lds, int* __restrict__ counts, int* __restrict__ ranks) {
+                                                   int chunk_log2, int use_lds, int* __restrict__ counts,
+                                                   int* __restrict__ ranks) {
   extern __shared__ int lc[];  // nb local counts, then nb bases
   const int bh = blockIdx.x / chunks, ch = blockIdx.x % chunks;
-  const long long u0 = (long long)bh * N + (long long)ch * kRegroupUnits;
-  const long long u1 = (long long)bh * N + ((long long)(ch + 1) * kRegroupUnits < N ? (long long)(ch + 1) * kRegroupUnits : N);
+  const long long i0 = (long long)ch * kRegroupUnits;
+  const long long u0 = (long long)bh * N + i0;
+  const long long u1 = (long long)bh * N + (i0 + kRegroupUnits < N ? i0 + kRegroupUnits : N);
   const long long n_pairs = (u1 - u0) * K;
   const long long p0 = u0 * K;
+  // every unit of this work-group lies in one position chunk (chunk_log2 >= log2 kRegroupUnits)
+  const int nch = (int)(((long long)N + (1LL << chunk_log2) - 1) >> chunk_log2);
+  const long long bucket0 = ((long long)bh * nch + (i0 >> chunk_log2)) * nb;
   if (!use_lds) {
     for (long long x = threadIdx.x; x < n_pairs; x += blockDim.x) {
       const int nd = nodes[p0 + x];
-      if (nd >= 0 && nd < nb) ranks[p0 + x] = atomicAdd(&counts[(long long)bh * nb + nd], 1);
+      if (nd >= 0 && nd < nb) ranks[p0 + x] = atomicAdd(&counts[bucket0 + nd], 1);
     }
     return;
   }
@@ -305,7 +335,7 @@ __global__ __launch_bounds__(256) void hist_kernel(const int* __restrict__ nodes
   __syncthreads();
   for (int j = threadIdx.x; j < nb; j += blockDim.x) {
     const int c = lc[j];
-    lc[nb + j] = c ? atomicAdd(&counts[(long long)bh * nb + j], c) : 0;
+    lc[nb + j] = c ? atomicAdd(&counts[bucket0 + j], c) : 0;
   }
   __syncthreads();
   for (long long x = threadIdx.x; x < n_pairs; x += blockDim.x) {
@@ -338,44 +368,47 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ coun
 }
 
 __global__ __launch_bounds__(256) void scatter_kernel(const int* __restrict__ nodes, long long n_pairs, int K, int N,
-                                                      int nb, const int* __restrict__ offsets,
+                                                      int nb, int chunk_log2, const int* __restrict__ offsets,
                                                       const int* __restrict__ ranks, uint32_t* __restrict__ pairs) {
+  const int nch = (int)(((long long)N + (1LL << chunk_log2) - 1) >> chunk_log2);
   for (long long x = (long long)blockIdx.x * blockDim.x + threadIdx.x; x < n_pairs; x += (long long)gridDim.x * blockDim.x) {
     const int nd = nodes[x];
     if (nd < 0 || nd >= nb) continue;  // out-of-range entries are not attended
     const long long u = x / K;
     const int slot = (int)(x % K);
-    const long long bh = u / N;
-    pairs[offsets[bh * nb + nd] + ranks[x]] = (uint32_t)((u << 5) | slot);
+    const long long bh = u / N, i = u % N;
+    pairs[offsets[(bh * nch + (i >> chunk_log2)) * nb + nd] + ranks[x]] = (uint32_t)((u << 5) | slot);
   }
 }
 
-hipError_t launch_regroup(const int* nodes, long long U, int K, int N, int nb, int n_heads, int* counts, int* offsets,
-                          int* ranks, uint32_t* pairs, hipStream_t st) {
-  const long long NB = (long long)nb * n_heads;
+hipError_t launch_regroup(const int* nodes, long long U, int K, int N, int nb, int n_heads, int chunk_log2,
+                          int* counts, int* offsets, int* ranks, uint32_t* pairs, hipStream_t st) {
+  const int nch = (int)(((long long)N + (1LL << chunk_log2) - 1) >> chunk_log2);
+  const long long NB = (long long)nb * nch * n_heads;
   long long zb = (NB + 255) / 256;
   hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)(zb < 4096 ? zb : 4096)), dim3(256), 0, st, counts, NB);
   const int chunks = (N + kRegroupUnits - 1) / kRegroupUnits;
   const int use_lds = nb <= 8192;  // 2*nb ints of LDS, at most 64 KiB
   const size_t lds = use_lds ? (size_t)nb * 2 * sizeof(int) : 0;
-  hipLaunchKernelGGL(hist_kernel, dim3(n_heads * chunks), dim3(256), lds, st, nodes, K, N, nb, chunks, use_lds, counts,
-                     ranks);
+  hipLaunchKernelGGL(hist_kernel, dim3(n_heads * chunks), dim3(256), lds, st, nodes, K, N, nb, chunks, chunk_log2,
+                     use_lds, counts, ranks);
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, counts, NB, offsets);
   const long long n_pairs = U * K;
   long long sb = (n_pairs + 255) / 256;
   hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)(sb < 65536 ? sb : 65536)), dim3(256), 0, st, nodes, n_pairs, K, N,
-                     nb, offsets, ranks, pairs);
+                     nb, chunk_log2, offsets, ranks, pairs);
   return hipGetLastError();
 }
 
 // ------------------------------------------------------------------------------------------ launchers
 template <typename T, int D, int C, bool FUSED>
-static hipError_t route_t(const SelDims& sd, const void* q, const void* k, const void* nodes, int* kept, int* sel,
-                          float* sel_lse, hipStream_t st) {
+static hipError_t route_t(const SelDims& sd, const void* q, const void* k, const void* nodes, const float* norms,
+                          int* kept, int* sel, float* sel_lse, hipStream_t st) {
   RouteParams<T> p;
   p.q = (const T*)q;
   p.k = (const T*)k;
   p.nodes = nodes;
+  p.norms = norms;
   p.B = sd.B;
   p.Hq = sd.Hq;
   p.Hkv = sd.Hkv;
@@ -399,23 +432,23 @@ static hipError_t route_t(const SelDims& sd, const void* q, const void* k, const
 }
 
 template <typename T, bool FUSED>
-static hipError_t route_dc(const SelDims& sd, const void* q, const void* k, const void* nodes, int* kept, int* sel,
-                           float* sel_lse, hipStream_t st) {
+static hipError_t route_dc(const SelDims& sd, const void* q, const void* k, const void* nodes, const float* norms,
+                           int* kept, int* sel, float* sel_lse, hipStream_t st) {
   if (sd.D == 128) {
-    if (sd.C == 64) return route_t<T, 128, 64, FUSED>(sd, q, k, nodes, kept, sel, sel_lse, st);
-    return route_t<T, 128, 32, FUSED>(sd, q, k, nodes, kept, sel, sel_lse, st);
+    if (sd.C == 64) return route_t<T, 128, 64, FUSED>(sd, q, k, nodes, norms, kept, sel, sel_lse, st);
+    return route_t<T, 128, 32, FUSED>(sd, q, k, nodes, norms, kept, sel, sel_lse, st);
   }
-  if (sd.C == 64) return route_t<T, 64, 64, FUSED>(sd, q, k, nodes, kept, sel, sel_lse, st);
-  return route_t<T, 64, 32, FUSED>(sd, q, k, nodes, kept, sel, sel_lse, st);
+  if (sd.C == 64) return route_t<T, 64, 64, FUSED>(sd, q, k, nodes, norms, kept, sel, sel_lse, st);
+  return route_t<T, 64, 32, FUSED>(sd, q, k, nodes, norms, kept, sel, sel_lse, st);
 }
 
-hipError_t launch_route(const SelDims& sd, const void* q, const void* k, const void* nodes, bool fused, int* kept,
-                        int* sel, float* sel_lse, hipStream_t st) {
+hipError_t launch_route(const SelDims& sd, const void* q, const void* k, const void* nodes, const float* norms,
+                        bool fused, int* kept, int* sel, float* sel_lse, hipStream_t st) {
   if (sd.bf16)
-    return fused ? route_dc<uint16_t, true>(sd, q, k, nodes, kept, sel, sel_lse, st)
-                 : route_dc<uint16_t, false>(sd, q, k, nodes, kept, sel, sel_lse, st);
-  return fused ? route_dc<float, true>(sd, q, k, nodes, kept, sel, sel_lse, st)
-               : route_dc<float, false>(sd, q, k, nodes, kept, sel, sel_lse, st);
+    return fused ? route_dc<uint16_t, true>(sd, q, k, nodes, norms, kept, sel, sel_lse, st)
+                 : route_dc<uint16_t, false>(sd, q, k, nodes, norms, kept, sel, sel_lse, st);
+  return fused ? route_dc<float, true>(sd, q, k, nodes, norms, kept, sel, sel_lse, st)
+               : route_dc<float, false>(sd, q, k, nodes, norms, kept, sel, sel_lse, st);
 }
 
 template <typename T, int D, int C>
@@ -434,6 +467,7 @@ static hipError_t leaf_t(const SelDims& sd, const void* q, const void* k, const 
   p.N = sd.N;
   p.K = sd.K;
   p.q_tile = sd.q_tile;
+  p.chunk_log2 = sd.chunk_log2;
   p.scale = sd.scale;
   p.leaf_lse = leaf_lse;
   const long long max_pairs = (long long)sd.B * sd.Hkv * sd.N * sd.K;

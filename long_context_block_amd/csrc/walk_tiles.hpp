@@ -116,13 +116,110 @@ __device__ void score_candidates(const Rows& rows, int level_off, const Frag<T> 
   __threadfence_block();
 }
 
+// Relative bound on |q . (mean - hi)| / (|q| |mean|) for the bf16 hi plane: round-to-nearest-even to
+// bf16 errs by at most 2^-8 of the value, per element; the factor covers the fp32 accumulation.
+constexpr float kHiRelBound = 0.00391f * 1.05f;
+
+// One scored level on the bf16 path, in two passes over the <= 4K child rows. Pass 1 uses the hi plane
+// only; a candidate's score then lies within E_c = scale * kHiRelBound * sum_h |q_h| * max child |mean|
+// of its hi+lo score (LSE is 1-Lipschitz in the max norm, per head). With the Top-K of the hi scores
+// as the "in" group, a candidate is decided by pass 1 when its interval cannot cross the boundary (an
+// "in" candidate whose lower end is above every "out" upper end, or an "out" candidate whose upper end
+// is below every "in" lower end); the rest get the lo plane added (pass 2) and compete by their hi+lo
+// scores for the remaining places. The kept set is the one the hi+lo scores of every candidate give,
+// while only the lo rows of undecided candidates are read. Returns this lane's keep flag.
+template <int D, int KM>
+__device__ bool select_level_refine(const NodeRows<uint16_t, D>& rows, const float* norms, int level_off,
+                                    const Frag<uint16_t> (&qf)[D / 32], float qnorm_sum, int cn, int n_cand,
+                                    int e_child, int G, float scale, int K, float* s_sc, uint32_t* keys) {
+  const int lane = lane_id(), r16 = lane & 15, grp = lane >> 4;
+  const int MT = (2 * n_cand + 15) >> 4;
+  const bool last_two = 2 * readlane(cn, n_cand - 1) + 1 < e_child;
+  const int n_full = last_two ? n_cand : n_cand - 1;
+  int child[KM];
+  bool valid[KM];
+#pragma unroll
+  for (int m = 0; m < KM; ++m) {
+    const int row = 16 * m + r16;
+    const int cidx = row >> 1;
+    const int cnode = __shfl(cn, cidx & 63);
+    valid[m] = cidx < n_cand && ((row & 1) == 0 || cidx < n_full);
+    child[m] = valid[m] ? 2 * cnode + (row & 1) : 0;
+  }
+  // pass 1: hi plane
+  f32x4 acc[KM];
+#pragma unroll
+  for (int m = 0; m < KM; ++m) {
+    if (m < MT) {
+      Frag<uint16_t> hi[D / 32];
+      const uint16_t* p = rows.base + (unsigned)(level_off + child[m]) * (2 * D) + 8 * grp;
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s) hi[s].load(p + 32 * s);
+      acc[m] = zero4();
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s) mma(acc[m], hi[s], qf[s]);
+    }
+  }
+  auto cand_scores = [&](int m, unsigned long long only) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      const int c = 8 * m + 2 * grp + a;
+      const float x0 = scale * acc[m][2 * a], x1 = scale * acc[m][2 * a + 1];
+      float l = c < n_full ? lse2(x0, x1) : x0;
+      l = row_sum16(r16 < G ? l : 0.f);
+      if (r16 == 0 && ((only >> (c & 63)) & 1ull)) s_sc[c] = l;
+    }
+  };
+#pragma unroll
+  for (int m = 0; m < KM; ++m)
+    if (m < MT) cand_scores(m, ~0ull);
+  float e = 0.f;
+  if (lane < n_cand) {
+    const float n0 = norms[level_off + 2 * cn];
+    const float n1 = lane < n_full ? norms[level_off + 2 * cn + 1] : 0.f;
+    e = scale * kHiRelBound * qnorm_sum * fmaxf(n0, n1);
+  }
+  __threadfence_block();
+  const float sh = lane < n_cand ? s_sc[lane] : kNegInf;
+  const bool in = topk_keep_lds(s_sc, n_cand, K, keys);
+  const float lo_b = sh - e, hi_b = sh + e;
+  const float u_out = wave_max(!in && lane < n_cand ? hi_b : kNegInf);
+  const float l_in = wave_min(in ? lo_b : -kNegInf);
+  const bool refine = lane < n_cand && ((in && lo_b <= u_out) || (!in && hi_b >= l_in));
+  const unsigned long long rmask = __ballot(refine);
+  if (rmask == 0ull) return in;
+  // pass 2: lo plane of the undecided candidates' rows
+#pragma unroll
+  for (int m = 0; m < KM; ++m) {
+    const unsigned long long tile = (rmask >> (8 * m)) & 0xffull;
+    if (m < MT && tile) {
+      const int cidx = (16 * m + r16) >> 1;
+      const bool need = valid[m] && ((rmask >> cidx) & 1ull);
+      Frag<uint16_t> lo[D / 32];
+      const uint16_t* p = rows.base + (unsigned)(level_off + child[m]) * (2 * D) + D + 8 * grp;
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s) {
+        if (need)
+          lo[s].load(p + 32 * s);
+        else
+          lo[s].zero();
+      }
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s) mma(acc[m], lo[s], qf[s]);
+      cand_scores(m, rmask);
+    }
+  }
+  __threadfence_block();
+  const float key = refine ? s_sc[lane < n_cand ? lane : 0] : (in ? -kNegInf : kNegInf);
+  return topk_keep(key, n_cand, K, keys);
+}
+
 // Walk from the root to level 1 for query position i. Level l has e_l = (i >> (log2 C + l)) + 1
 // eligible nodes; levels with e_l <= K keep all of them, so the walk starts below the highest level
 // with more than K. Returns the number of kept level-1 nodes; lane c < n holds the c-th (ascending).
 // A pyramid of one leaf has the virtual level-1 node 0.
-template <typename T, int D, int KM>
-__device__ int walk_to_level1(const NodeRows<T, D>& rows, const Levels& lv, const Frag<T> (&qf)[D / 32], int log2c,
-                              int K, int G, float scale, int i, int* kept_out, float* s_sc) {
+template <typename T, int D, int KM, class LevelSelect>
+__device__ int walk_to_level1(const Levels& lv, int log2c, int K, int i, int* kept_out, LevelSelect&& level_select) {
   const int lane = lane_id();
   const int L = lv.n_levels - 1;
   int lstar = 0;
@@ -151,9 +248,7 @@ __device__ int walk_to_level1(const NodeRows<T, D>& rows, const Levels& lv, cons
       nk = n_cand;
       continue;
     }
-    score_candidates<T, D, KM>(rows, (int)lv.off[l - 1], qf, cn, n_cand, (i >> (log2c + l - 1)) + 1, G, scale, s_sc);
-    const bool keep = topk_keep_lds(s_sc, n_cand, K);
-    __threadfence_block();
+    const bool keep = level_select((int)lv.off[l - 1], cn, n_cand, (i >> (log2c + l - 1)) + 1);
     int cnt;
     const int nxt = compact_lanes(keep, cn, &cnt);
     kept = lane < cnt ? nxt : -1;
@@ -195,6 +290,9 @@ __device__ __forceinline__ void leaf_pair_lse(const Frag<T> (&kf)[C / 8][D / 32]
 #pragma unroll
     for (int m = 0; m < MT; ++m) mma(acc[m], kf[m][s], qf[s]);
   }
+  // causal mask on offsets within the tile: token t0 + o is visible iff o <= icol - t0
+  const long long lim64 = icol - t0;
+  const int lim = lim64 < 0 ? -1 : (lim64 > 2 * C ? 2 * C : (int)lim64);
 #pragma unroll
   for (int bit = 0; bit < 2; ++bit) {
     float x[ML * 4];
@@ -202,8 +300,8 @@ __device__ __forceinline__ void leaf_pair_lse(const Frag<T> (&kf)[C / 8][D / 32]
     for (int mm = 0; mm < ML; ++mm) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const long long t = t0 + 16 * (bit * ML + mm) + 4 * grp + j;
-        x[mm * 4 + j] = t <= icol ? acc[bit * ML + mm][j] : kNegInf;
+        const int o = 16 * (bit * ML + mm) + 4 * grp + j;
+        x[mm * 4 + j] = o <= lim ? acc[bit * ML + mm][j] : kNegInf;
       }
     }
     const float l = column_lse<ML * 4>(x, scale);
