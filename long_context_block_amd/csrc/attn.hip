@@ -131,16 +131,22 @@ __global__ __launch_bounds__(256) void attn_leaf_kernel(AttnParams<T> p) {
         if (grp == 0) p.part_lse[prow] = lse;
       }
     };
-    const long long ntiles = (seg - pos + tile_units - 1) / tile_units;
-    Tile X, Y;
-    fetch(X, pos);
-    if (ntiles > 1) fetch(Y, pos + tile_units);
-    for (long long t = 0; t < ntiles; t += 2) {
-      attend(X);
-      if (t + 2 < ntiles) fetch(X, pos + (t + 2) * tile_units);
-      if (t + 1 < ntiles) {
-        attend(Y);
-        if (t + 3 < ntiles) fetch(Y, pos + (t + 3) * tile_units);
+    const long long step = tile_units;
+    const long long ntiles = (seg - pos + step - 1) / step;
+    // ring of R tiles: the query fragments of tile t+R are requested as tile t finishes
+    // (bf16 tiles are small enough for R = 4 without spilling; fp32 keeps R = 2)
+    constexpr int R = sizeof(T) == 2 ? 4 : 2;
+    Tile X[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (r < ntiles) fetch(X[r], pos + r * step);
+    for (long long t = 0; t < ntiles; t += R) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        if (t + r < ntiles) {
+          attend(X[r]);
+          if (t + r + R < ntiles) fetch(X[r], pos + (t + r + R) * step);
+        }
       }
     }
     pos = seg;

@@ -68,15 +68,23 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams<T> p) {
     p.k_cache[((long long)bh * p.Nmax + pos) * D + tid] = kv;
     p.v_cache[((long long)bh * p.Nmax + pos) * D + tid] = p.v_new[(long long)bh * D + tid];
     const float kf = to_f32<T>(kv);
-    int j = pos >> LOG2C;
-    for (int l = 0; l < p.lv.n_levels; ++l, j >>= 1) {
-      const long long row = (head_row + p.lv.off[l] + j) * D + tid;
-      const float sm = p.pyr_sum[row] + kf;
-      p.pyr_sum[row] = sm;
-      const long long lo = (long long)j << (LOG2C + l);
-      const long long hi = (long long)(j + 1) << (LOG2C + l);
-      const float cnt = (float)((hi < len ? hi : (long long)len) - lo);
-      p.pyr_mean[row] = sm / cnt;
+    // all ancestor sums are read first (independent loads), then updated
+    float old_sum[kMaxLevels];
+#pragma unroll
+    for (int l = 0; l < kMaxLevels; ++l)
+      if (l < p.lv.n_levels) old_sum[l] = p.pyr_sum[(head_row + p.lv.off[l] + (pos >> (LOG2C + l))) * D + tid];
+#pragma unroll
+    for (int l = 0; l < kMaxLevels; ++l) {
+      if (l < p.lv.n_levels) {
+        const long long j = pos >> (LOG2C + l);
+        const long long row = (head_row + p.lv.off[l] + j) * D + tid;
+        const float sm = old_sum[l] + kf;
+        p.pyr_sum[row] = sm;
+        const long long lo = j << (LOG2C + l);
+        const long long hi = (j + 1) << (LOG2C + l);
+        const float cnt = (float)((hi < len ? hi : (long long)len) - lo);
+        p.pyr_mean[row] = sm / cnt;
+      }
     }
   }
   __threadfence();
@@ -130,13 +138,26 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams<T> p) {
       // stage child rows 2c + bit (child node 4 kept[c/2] + 2(c&1) + bit) of the level-(l-1) means
       const int n_rows = 2 * n_cand;
       const long long lvl_row = head_row + p.lv.off[l - 1];
-      for (int x = tid; x < n_rows * (D / 4); x += 256) {
+      // all of this thread's row loads are issued before any is used
+      constexpr int SPT = (16 * KM * (D / 4) + 255) / 256;  // staging items per thread
+      float4 mv[SPT];
+#pragma unroll
+      for (int it = 0; it < SPT; ++it) {
+        const int x = tid + 256 * it;
+        mv[it] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (x < n_rows * (D / 4)) {
+          const int rho = x / (D / 4), q4 = x % (D / 4);
+          const int c = rho >> 1, bit = rho & 1;
+          const int child = 4 * s_kept[c >> 1] + 2 * (c & 1) + bit;
+          if (bit == 0 || c < n_full) mv[it] = *reinterpret_cast<const float4*>(p.pyr_mean + (lvl_row + child) * D + 4 * q4);
+        }
+      }
+#pragma unroll
+      for (int it = 0; it < SPT; ++it) {
+        const int x = tid + 256 * it;
+        if (x >= n_rows * (D / 4)) continue;
         const int rho = x / (D / 4), q4 = x % (D / 4);
-        const int c = rho >> 1, bit = rho & 1;
-        const bool ok = bit == 0 || c < n_full;
-        const int child = 4 * s_kept[c >> 1] + 2 * (c & 1) + bit;
-        float4 m = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (ok) m = *reinterpret_cast<const float4*>(p.pyr_mean + (lvl_row + child) * D + 4 * q4);
+        const float4 m = mv[it];
         if constexpr (sizeof(T) == 2) {
           uint16_t* row = reinterpret_cast<uint16_t*>(s_buf) + rho * 2 * D + 4 * q4;
           const float v4[4] = {m.x, m.y, m.z, m.w};

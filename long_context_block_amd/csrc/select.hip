@@ -68,7 +68,7 @@ __device__ __forceinline__ void leaf_topk_write(int n_cand, int leaf_c, int G, i
 }
 
 template <typename T, int D, int C, bool FUSED, int KM>
-__global__ __launch_bounds__(256, 2) void route_kernel(RouteParams<T> p) {
+__global__ __launch_bounds__(256, FUSED ? 2 : 4) void route_kernel(RouteParams<T> p) {
   constexpr int kLog2C = C == 64 ? 6 : 5;
   __shared__ float s_ell[FUSED ? 4 : 1][64][17];
   __shared__ __align__(16) float s_sc[4][64];
@@ -248,16 +248,22 @@ __global__ __launch_bounds__(256) void leaf_lse_kernel(LeafParams<T> p) {
         dst[p.G] = l1;
       }
     };
-    const long long ntiles = (seg - pos + p.q_tile - 1) / p.q_tile;
-    LeafTile<T, D> X, Y;
-    fetch(X, pos);
-    if (ntiles > 1) fetch(Y, pos + p.q_tile);
-    for (long long t = 0; t < ntiles; t += 2) {
-      score(X);
-      if (t + 2 < ntiles) fetch(X, pos + (t + 2) * p.q_tile);
-      if (t + 1 < ntiles) {
-        score(Y);
-        if (t + 3 < ntiles) fetch(Y, pos + (t + 3) * p.q_tile);
+    const long long step = p.q_tile;
+    const long long ntiles = (seg - pos + step - 1) / step;
+    // ring of R tiles: the query fragments of tile t+R are requested as tile t finishes
+    // (bf16 tiles are small enough for R = 4 without spilling; fp32 keeps R = 2)
+    constexpr int R = sizeof(T) == 2 ? 4 : 2;
+    LeafTile<T, D> X[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (r < ntiles) fetch(X[r], pos + r * step);
+    for (long long t = 0; t < ntiles; t += R) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        if (t + r < ntiles) {
+          score(X[r]);
+          if (t + r + R < ntiles) fetch(X[r], pos + (t + r + R) * step);
+        }
       }
     }
     pos = seg;
