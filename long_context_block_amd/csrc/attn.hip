@@ -84,72 +84,202 @@ __global__ __launch_bounds__(256) void attn_leaf_kernel(AttnParams<T> p) {
       Frag<T> qf[D / 32];
       long long u;
       int slot;
-      bool valid;
     };
+    // A column past the run repeats the run's first pair: it computes that pair's result again and
+    // stores the same bytes to the same place. Loads and stores are therefore unconditional and the
+    // tile loop is straight-line code, which lets the query prefetch stay in flight across tiles.
     auto fetch = [&](Tile& t, long long tp) {
       const long long pi = tp + r16 / p.G;
-      t.valid = pi < seg;
-      const uint32_t pc = run.pair(t.valid ? pi : pos);
+      const uint32_t pc = run.pair(pi < seg ? pi : pos);
       t.u = pc >> 5;
       t.slot = pc & 31;
       const T* qrow = qhead + (t.u - ubase) * D;
 #pragma unroll
-      for (int s = 0; s < D / 32; ++s) {
-        if (t.valid)
-          t.qf[s].load(qrow + 32 * s);
-        else
-          t.qf[s].zero();
-      }
+      for (int s = 0; s < D / 32; ++s) t.qf[s].load(qrow + 32 * s);
     };
     auto attend = [&](const Tile& cur) {
       Frag<T> qf[D / 32];
 #pragma unroll
       for (int s = 0; s < D / 32; ++s) qf[s] = cur.qf[s];
-      const long long uc = cur.u;
-      const int slot = cur.slot;
-      const bool cv = cur.valid;
-      const long long ic = cv ? uc - ubase : -1;
       f32x4 oacc[MO];
       float lse, inv;
-      attend_tile<T, D, C>(kf, vf, qf, t0, ic, p.scale, oacc, lse, inv);
-      if (cv) {
-        const long long prow = (uc * p.K + slot) * p.G + h;
-        T* dst = p.part + prow * D;
+      attend_tile<T, D, C>(kf, vf, qf, t0, cur.u - ubase, p.scale, oacc, lse, inv);
+      const long long prow = (cur.u * p.K + cur.slot) * p.G + h;
+      // lane group grp holds dimensions 32 c + 8 grp .. +8 in oacc[2c], oacc[2c + 1]
+      T* dst = p.part + prow * D + 8 * grp;
+      if constexpr (sizeof(T) == 2) {
 #pragma unroll
-        for (int mt = 0; mt < MO; ++mt) {
-          const int n0 = 16 * mt + 4 * grp;
-          if constexpr (sizeof(T) == 2) {
-            uint2 w;
-            w.x = (uint32_t)f32_to_bf16(oacc[mt][0] * inv) | ((uint32_t)f32_to_bf16(oacc[mt][1] * inv) << 16);
-            w.y = (uint32_t)f32_to_bf16(oacc[mt][2] * inv) | ((uint32_t)f32_to_bf16(oacc[mt][3] * inv) << 16);
-            *reinterpret_cast<uint2*>((uint16_t*)dst + n0) = w;
-          } else {
-            *reinterpret_cast<float4*>((float*)dst + n0) =
-                make_float4(oacc[mt][0] * inv, oacc[mt][1] * inv, oacc[mt][2] * inv, oacc[mt][3] * inv);
-          }
+        for (int c = 0; c < MO / 2; ++c) {
+          uint4 w;
+          w.x = pack_bf16x2(oacc[2 * c][0] * inv, oacc[2 * c][1] * inv);
+          w.y = pack_bf16x2(oacc[2 * c][2] * inv, oacc[2 * c][3] * inv);
+          w.z = pack_bf16x2(oacc[2 * c + 1][0] * inv, oacc[2 * c + 1][1] * inv);
+          w.w = pack_bf16x2(oacc[2 * c + 1][2] * inv, oacc[2 * c + 1][3] * inv);
+          *reinterpret_cast<uint4*>((uint16_t*)dst + 32 * c) = w;
         }
-        if (grp == 0) p.part_lse[prow] = lse;
+      } else {
+#pragma unroll
+        for (int mt = 0; mt < MO; ++mt)
+          *reinterpret_cast<float4*>((float*)dst + 32 * (mt >> 1) + 4 * (mt & 1)) =
+              make_float4(oacc[mt][0] * inv, oacc[mt][1] * inv, oacc[mt][2] * inv, oacc[mt][3] * inv);
       }
+      p.part_lse[prow] = lse;  // the column's 4 lanes hold the same value
     };
+    // ring of R tiles in groups of R: the query fragments of tile t + R are requested as tile t
+    // finishes
+    constexpr int R = 2;
     const long long step = tile_units;
-    const long long ntiles = (seg - pos + step - 1) / step;
-    // ring of R tiles: the query fragments of tile t+R are requested as tile t finishes
-    // (bf16 tiles are small enough for R = 4 without spilling; fp32 keeps R = 2)
-    constexpr int R = sizeof(T) == 2 ? 4 : 2;
+    // the run length is wave-uniform; readfirstlane lets the compiler see it (a scalar loop)
+    const int run_len = __builtin_amdgcn_readfirstlane((int)(seg - pos));
+    const int ntiles = (run_len + tile_units - 1) / tile_units;
+    const int ngroups = (ntiles + R - 1) / R;
     Tile X[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r)
-      if (r < ntiles) fetch(X[r], pos + r * step);
-    for (long long t = 0; t < ntiles; t += R) {
+    for (int r = 0; r < R; ++r) fetch(X[r], pos + r * step);
+    for (int gi = 0; gi < ngroups; ++gi) {
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        if (t + r < ntiles) {
-          attend(X[r]);
-          if (t + r + R < ntiles) fetch(X[r], pos + (t + r + R) * step);
-        }
+        attend(X[r]);
+        fetch(X[r], pos + (long long)((gi + 1) * R + r) * step);
       }
     }
     pos = seg;
+  }
+}
+
+// bf16, work-group cooperative. A work-group task is kWgTask consecutive sorted pairs; its runs (one
+// leaf each) are found once. For each run the 256 threads stage the leaf's K (swizzled) and V^T into
+// LDS, then the four waves take the run's tiles of 16/G units x G heads round-robin, reading every
+// MFMA fragment of K and V^T from LDS. Sharing the tiles keeps registers low (three waves per SIMD
+// hide the query-gather latency) and loads each leaf's K/V once per work-group instead of per wave.
+constexpr int kWgTask = 1024;
+
+template <int D, int C>
+__global__ __launch_bounds__(256, 3) void attn_leaf_wg_kernel(AttnParams<uint16_t> p) {
+  constexpr int MO = D / 16;
+  __shared__ __align__(16) uint16_t s_k[C][D];
+  __shared__ __align__(16) uint16_t s_vt[D][C + 8];
+  __shared__ uint32_t s_pair[kWgTask];
+  __shared__ long long s_key[kWgTask];
+  __shared__ int s_run[kWgTask + 1];
+  __shared__ int s_wcount[4];
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6, r16 = lane & 15, grp = lane >> 4;
+  const long long total = *p.total;
+  const long long base = (long long)xcd_logical_block(gridDim.x) * kWgTask;
+  if (base >= total) return;  // whole work-group
+  const int n = (int)(total - base < kWgTask ? total - base : kWgTask);
+  const long long nch = ((long long)p.N + (1LL << p.chunk_log2) - 1) >> p.chunk_log2;
+  // ---- pairs and their bucket keys (KV head, position chunk, leaf)
+  for (int x = tid; x < n; x += 256) {
+    const uint32_t pr = p.pairs[base + x];
+    const long long u = pr >> 5;
+    s_pair[x] = pr;
+    s_key[x] = ((u / p.N) * nch + ((u % p.N) >> p.chunk_log2)) * (1LL << 32) + p.sel[u * p.K + (pr & 31)];
+  }
+  __syncthreads();
+  // ---- run starts, in order: wave w scans entries [256 w, 256 w + 256)
+  int cnt = 0;
+  uint64_t masks[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int x = wave * 256 + j * 64 + lane;
+    const bool start = x < n && (x == 0 || s_key[x] != s_key[x - 1]);
+    masks[j] = __ballot(start);
+    cnt += __popcll(masks[j]);
+  }
+  if (lane == 0) s_wcount[wave] = cnt;
+  __syncthreads();
+  int off = 0;
+  for (int w = 0; w < wave; ++w) off += s_wcount[w];
+  const int nrun = s_wcount[0] + s_wcount[1] + s_wcount[2] + s_wcount[3];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int x = wave * 256 + j * 64 + lane;
+    if ((masks[j] >> lane) & 1) s_run[off + __popcll(masks[j] & ((1ull << lane) - 1))] = x;
+    off += __popcll(masks[j]);
+  }
+  if (tid == 0) s_run[nrun] = n;
+  __syncthreads();
+  const int tile_units = 16 / p.G;
+  const int h = r16 % p.G;
+  for (int r = 0; r < nrun; ++r) {
+    const int a = s_run[r], b = s_run[r + 1];
+    const long long u0 = s_pair[a] >> 5;
+    const long long bh = u0 / p.N;
+    const int leaf = (int)(s_key[a] & 0xffffffffLL);
+    const long long t0 = (long long)leaf * C;
+    const uint16_t* kbh = p.k + bh * (long long)p.N * D;
+    const uint16_t* vbh = p.v + bh * (long long)p.N * D;
+    stage_kv_wg<D, C>(kbh, vbh, t0, p.N, s_k, s_vt);
+    __syncthreads();
+    const int bi = (int)(bh / p.Hkv), ri = (int)(bh % p.Hkv);
+    const uint16_t* qhead = p.q + (((long long)bi * p.Hq + (long long)ri * p.G + h) * p.N) * D + 8 * grp;
+    const long long ubase = bh * p.N;
+    const int ntiles = (b - a + tile_units - 1) / tile_units;
+    // The query fragments of tile t + 4 (this wave's next tile) are requested before tile t is
+    // computed. A column past the run, or past the wave's last tile, repeats the run's first pair:
+    // same result, same bytes, same place.
+    auto fetch = [&](int t, Frag<uint16_t> (&qf)[D / 32], uint32_t& pc) {
+      int x = a + t * tile_units + r16 / p.G;
+      x = (t < ntiles && x < b) ? x : a;
+      pc = s_pair[x];
+      const uint16_t* qrow = qhead + ((long long)(pc >> 5) - ubase) * D;
+#pragma unroll
+      for (int s2 = 0; s2 < D / 32; ++s2) qf[s2].load(qrow + 32 * s2);
+    };
+    auto opaque = [&](Frag<uint16_t> (&qf)[D / 32]) {
+#pragma unroll
+      for (int s2 = 0; s2 < D / 32; ++s2)
+        asm volatile("" : "+v"(qf[s2].u.x), "+v"(qf[s2].u.y), "+v"(qf[s2].u.z), "+v"(qf[s2].u.w));
+    };
+    struct Out {
+      f32x4 o[MO];
+      float lse, inv;
+      uint32_t pc;
+    };
+    auto attend = [&](const Frag<uint16_t> (&qf)[D / 32], uint32_t pc, Out& out) {
+      out.pc = pc;
+      attend_tile_kv<uint16_t, D, C, true>([&](int m, int s2) { return k_frag_wg<D>(s_k, m, s2); },
+                                           [&](int mt, int ks) { return vt_frag<C>(s_vt, mt, ks); }, qf, t0,
+                                           (long long)(pc >> 5) - ubase, p.scale, out.o, out.lse, out.inv);
+    };
+    auto store = [&](const Out& out) {
+      const long long prow = ((long long)(out.pc >> 5) * p.K + (out.pc & 31)) * p.G + h;
+      // lane group grp holds dimensions 32 c + 8 grp .. +8 in o[2c], o[2c + 1]
+      uint16_t* dst = p.part + prow * D + 8 * grp;
+      const float inv = out.inv;
+#pragma unroll
+      for (int c = 0; c < MO / 2; ++c) {
+        uint4 w;
+        w.x = pack_bf16x2(out.o[2 * c][0] * inv, out.o[2 * c][1] * inv);
+        w.y = pack_bf16x2(out.o[2 * c][2] * inv, out.o[2 * c][3] * inv);
+        w.z = pack_bf16x2(out.o[2 * c + 1][0] * inv, out.o[2 * c + 1][1] * inv);
+        w.w = pack_bf16x2(out.o[2 * c + 1][2] * inv, out.o[2 * c + 1][3] * inv);
+        *reinterpret_cast<uint4*>(dst + 32 * c) = w;
+      }
+      p.part_lse[prow] = out.lse;  // the column's 4 lanes hold the same value
+    };
+    if (wave < ntiles) {
+      // two register sets in turn: this wave's tiles t and t + 4 are computed while the queries of
+      // t + 8 and t + 12 are in flight (a tile past the end repeats the run's first pair); each
+      // prefetch is issued before the stores of the tile just computed
+      Frag<uint16_t> qa[D / 32], qb[D / 32];
+      uint32_t pa, pb;
+      fetch(wave, qa, pa);
+      fetch(wave + 4, qb, pb);
+      opaque(qa);
+      opaque(qb);
+      for (int t = wave; t < ntiles; t += 8) {
+        Out out;
+        attend(qa, pa, out);
+        fetch(t + 8, qa, pa);
+        store(out);
+        attend(qb, pb, out);
+        fetch(t + 12, qb, pb);
+        store(out);
+      }
+    }
+    __syncthreads();  // every wave is done with this leaf's tiles before they are restaged
   }
 }
 
@@ -223,9 +353,15 @@ static hipError_t attn_leaf_t(const SelDims& sd, const void* q, const void* k, c
   p.part = (T*)part;
   p.part_lse = part_lse;
   const long long max_pairs = (long long)sd.B * sd.Hkv * sd.N * sd.K;
-  const long long tasks = (max_pairs + kAttnTask - 1) / kAttnTask;
-  p.tasks = (int)tasks;
-  hipLaunchKernelGGL((attn_leaf_kernel<T, D, C>), dim3((unsigned)((tasks + 3) / 4)), dim3(256), 0, st, p);
+  if constexpr (sizeof(T) == 2) {
+    const long long wg = (max_pairs + kWgTask - 1) / kWgTask;
+    p.tasks = (int)wg;
+    hipLaunchKernelGGL((attn_leaf_wg_kernel<D, C>), dim3((unsigned)wg), dim3(256), 0, st, p);
+  } else {
+    const long long tasks = (max_pairs + kAttnTask - 1) / kAttnTask;
+    p.tasks = (int)tasks;
+    hipLaunchKernelGGL((attn_leaf_kernel<T, D, C>), dim3((unsigned)((tasks + 3) / 4)), dim3(256), 0, st, p);
+  }
   return hipGetLastError();
 }
 

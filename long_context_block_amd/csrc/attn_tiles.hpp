@@ -13,52 +13,91 @@ namespace pisa {
 // Token offset (within the leaf) of D-row 4*grp + j of M-tile m after the first MFMA.
 __device__ __forceinline__ int attn_token(int m, int grp, int j) { return 32 * (m >> 1) + 8 * grp + 4 * (m & 1) + j; }
 
-// K tile of the leaf starting at token t0, rows permuted (attn_token), zero past N.
+// Output dimension in D-row 4*grp + j of M-tile mt of O^T. The rows of V^T are permuted so that the
+// pair of M-tiles (2c, 2c + 1) gives lane group grp the 8 consecutive dimensions 32 c + 8 grp .. +8:
+// one 16-byte store per lane then covers 64 contiguous bytes of each output row per instruction.
+template <int D>
+__device__ __forceinline__ int attn_out_dim(int mt, int grp, int j) {
+  return 32 * (mt >> 1) + 8 * grp + 4 * (mt & 1) + j;
+}
+// Inverse: the V^T row (16 mt + 4 grp + j) that holds dimension d.
+template <int D>
+__device__ __forceinline__ int attn_vt_row(int d) {
+  const int mt = 2 * (d >> 5) + ((d >> 2) & 1), grp = (d >> 3) & 3, j = d & 3;
+  return 16 * mt + 4 * grp + j;
+}
+
+// K tile of the leaf starting at token t0, rows permuted (attn_token). Rows past N repeat row N - 1:
+// those tokens are later than every query, so the causal mask drops them before any use.
 template <typename T, int D, int C>
 __device__ __forceinline__ void load_attn_k(const T* kbh, long long t0, long long N, Frag<T> (&kf)[C / 16][D / 32]) {
   const int r16 = lane_id() & 15, grp = lane_id() >> 4;
 #pragma unroll
   for (int m = 0; m < C / 16; ++m) {
-    const long long t = t0 + attn_token(m, r16 >> 2, r16 & 3);
+    long long t = t0 + attn_token(m, r16 >> 2, r16 & 3);
+    t = t < N ? t : N - 1;
 #pragma unroll
-    for (int s = 0; s < D / 32; ++s) {
-      if (t < N)
-        kf[m][s].load(kbh + t * D + 32 * s + 8 * grp);
-      else
-        kf[m][s].zero();
-    }
+    for (int s = 0; s < D / 32; ++s) kf[m][s].load(kbh + t * D + 32 * s + 8 * grp);
   }
 }
 
-// V^T fragments: lane (row n = 16 mt + r16, grp) gets V[32 ks + 8 grp + e][n], e = 0..7. bf16 goes
-// through vt, this wave's [D][C + 8] LDS scratch.
+// Stage the bf16 V tile of the leaf at t0 transposed into vt, this wave's [D][C + 8] LDS scratch:
+// dimension d goes to row attn_vt_row(d). Tokens past N repeat token N - 1 (their probabilities are
+// exactly zero). Each lane writes (token 2tp, token 2tp + 1) pairs as 32-bit words.
+template <int D, int C>
+__device__ __forceinline__ void stage_attn_vt(const uint16_t* vbh, long long t0, long long N, uint16_t (*vt)[C + 8]) {
+  const int lane = lane_id();
+  constexpr int CHR = D / 8;               // 8-element chunks per V row
+  constexpr int NIT = (C / 2) * CHR / 64;  // token pairs x chunks per lane
+  static_assert(((C / 2) * CHR) % 64 == 0, "tile shape");
+  uint4 f0[NIT], f1[NIT];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int qd = it * 64 + lane;
+    const int tp = qd / CHR, c0 = (qd % CHR) * 8;
+    long long ta = t0 + 2 * tp, tb = ta + 1;
+    ta = ta < N ? ta : N - 1;
+    tb = tb < N ? tb : N - 1;
+    f0[it] = *reinterpret_cast<const uint4*>(vbh + ta * D + c0);
+    f1[it] = *reinterpret_cast<const uint4*>(vbh + tb * D + c0);
+  }
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int qd = it * 64 + lane;
+    const int tp = qd / CHR, c0 = (qd % CHR) * 8;
+    const uint32_t a[4] = {f0[it].x, f0[it].y, f0[it].z, f0[it].w};
+    const uint32_t b[4] = {f1[it].x, f1[it].y, f1[it].z, f1[it].w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t w = __builtin_amdgcn_perm(b[e >> 1], a[e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
+      *reinterpret_cast<uint32_t*>(&vt[attn_vt_row<D>(c0 + e)][2 * tp]) = w;
+    }
+  }
+  __threadfence_block();
+}
+
+// V^T A-fragment (M-tile mt, k step ks) from the staged tile: lane (row 16 mt + r16, grp) gets
+// V[32 ks + 8 grp + e][attn_out_dim(mt, r16 / 4, r16 % 4)], e = 0..7.
+template <int C>
+__device__ __forceinline__ Frag<uint16_t> vt_frag(const uint16_t (*vt)[C + 8], int mt, int ks) {
+  const int r16 = lane_id() & 15, grp = lane_id() >> 4;
+  Frag<uint16_t> f;
+  f.u = *reinterpret_cast<const uint4*>(&vt[16 * mt + r16][32 * ks + 8 * grp]);
+  return f;
+}
+
+// All V^T fragments in registers (bf16 staged through vt; fp32 loaded directly).
 template <typename T, int D, int C>
 __device__ __forceinline__ void load_attn_vt(const T* vbh, long long t0, long long N, uint16_t (*vt)[C + 8],
                                              Frag<T> (&vf)[D / 16][C / 32]) {
   constexpr int MO = D / 16, KS = C / 32;
   const int lane = lane_id(), r16 = lane & 15, grp = lane >> 4;
   if constexpr (sizeof(T) == 2) {
-    constexpr int CHR = D / 8;  // 8-element chunks per V row
-#pragma unroll
-    for (int it = 0; it < (C * CHR) / 64; ++it) {
-      const int qd = it * 64 + lane;
-      const int t = qd / CHR, c0 = (qd % CHR) * 8;
-      Frag<uint16_t> f;
-      if (t0 + t < N)
-        f.load((const uint16_t*)vbh + (t0 + t) * D + c0);
-      else
-        f.zero();
-      const uint32_t w[4] = {f.u.x, f.u.y, f.u.z, f.u.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) vt[c0 + e][t] = (uint16_t)((e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xffffu));
-    }
-    __threadfence_block();
+    stage_attn_vt<D, C>((const uint16_t*)vbh, t0, N, vt);
 #pragma unroll
     for (int mt = 0; mt < MO; ++mt)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        reinterpret_cast<Frag<uint16_t>&>(vf[mt][ks]).u =
-            *reinterpret_cast<const uint4*>(&vt[16 * mt + r16][32 * ks + 8 * grp]);
+      for (int ks = 0; ks < KS; ++ks) reinterpret_cast<Frag<uint16_t>&>(vf[mt][ks]) = vt_frag<C>(vt, mt, ks);
     __threadfence_block();
   } else {
 #pragma unroll
@@ -66,10 +105,12 @@ __device__ __forceinline__ void load_attn_vt(const T* vbh, long long t0, long lo
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         float e8[8];
+        const int d = attn_out_dim<D>(mt, r16 >> 2, r16 & 3);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const long long t = t0 + 32 * ks + 8 * grp + e;
-          e8[e] = t < N ? to_f32<T>(vbh[t * D + 16 * mt + r16]) : 0.f;
+          long long t = t0 + 32 * ks + 8 * grp + e;
+          t = t < N ? t : N - 1;
+          e8[e] = to_f32<T>(vbh[t * D + d]);
         }
         Frag<float>& f = reinterpret_cast<Frag<float>&>(vf[mt][ks]);
         f.a = make_float4(e8[0], e8[1], e8[2], e8[3]);
@@ -80,11 +121,15 @@ __device__ __forceinline__ void load_attn_vt(const T* vbh, long long t0, long lo
 
 // One leaf for the 16 columns whose query fragments are qf and whose positions are ic (-1: none):
 // oacc = sum_t p_t v_t with p_t = exp(s (x_t - m)) over t <= ic; lse = s m + ln l (-inf if empty),
-// inv = 1 / l. Lane (col, grp) gets O[col][16 mt + 4 grp + j] in oacc[mt][j].
-template <typename T, int D, int C>
-__device__ __forceinline__ void attend_tile(const Frag<T> (&kf)[C / 16][D / 32], const Frag<T> (&vf)[D / 16][C / 32],
-                                            const Frag<T> (&qf)[D / 32], long long t0, long long ic, float scale,
-                                            f32x4 (&oacc)[D / 16], float& lse, float& inv) {
+// inv = 1 / l. Lane (col, grp) gets O[col][attn_out_dim(mt, grp, j)] in oacc[mt][j].
+// kfrag(m, s) returns the K A-fragment of S M-tile m, k step s; vfrag(mt, ks) the V^T A-fragment of
+// O^T M-tile mt, k step ks.
+// kPhased: keep the scheduler from hoisting the V^T fragment reads above the softmax (LDS-sourced
+// fragments would otherwise all be live at once).
+template <typename T, int D, int C, bool kPhased = false, typename KFrag, typename VFrag>
+__device__ __forceinline__ void attend_tile_kv(KFrag kfrag, VFrag vfrag, const Frag<T> (&qf)[D / 32], long long t0,
+                                               long long ic, float scale, f32x4 (&oacc)[D / 16], float& lse,
+                                               float& inv) {
   constexpr int MS = C / 16, KS = C / 32, MO = D / 16;
   const int grp = lane_id() >> 4;
   f32x4 sacc[MS];
@@ -93,7 +138,7 @@ __device__ __forceinline__ void attend_tile(const Frag<T> (&kf)[C / 16][D / 32],
 #pragma unroll
   for (int s = 0; s < D / 32; ++s)
 #pragma unroll
-    for (int m = 0; m < MS; ++m) mma(sacc[m], kf[m][s], qf[s]);
+    for (int m = 0; m < MS; ++m) mma(sacc[m], kfrag(m, s), qf[s]);
   float mx = kNegInf;
   const long long lim64 = ic - t0;
   const int lim = lim64 < 0 ? -1 : (lim64 > C ? C : (int)lim64);
@@ -119,16 +164,17 @@ __device__ __forceinline__ void attend_tile(const Frag<T> (&kf)[C / 16][D / 32],
       lsum += e;
     }
   lsum = colgroup_sum(lsum);
+  if constexpr (kPhased) __builtin_amdgcn_sched_barrier(0);
   Frag<T> pf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     if constexpr (sizeof(T) == 2) {
       const f32x4 a = sacc[2 * ks], bb = sacc[2 * ks + 1];
       Frag<uint16_t>& f = reinterpret_cast<Frag<uint16_t>&>(pf[ks]);
-      f.u.x = (uint32_t)f32_to_bf16(a[0]) | ((uint32_t)f32_to_bf16(a[1]) << 16);
-      f.u.y = (uint32_t)f32_to_bf16(a[2]) | ((uint32_t)f32_to_bf16(a[3]) << 16);
-      f.u.z = (uint32_t)f32_to_bf16(bb[0]) | ((uint32_t)f32_to_bf16(bb[1]) << 16);
-      f.u.w = (uint32_t)f32_to_bf16(bb[2]) | ((uint32_t)f32_to_bf16(bb[3]) << 16);
+      f.u.x = pack_bf16x2(a[0], a[1]);
+      f.u.y = pack_bf16x2(a[2], a[3]);
+      f.u.z = pack_bf16x2(bb[0], bb[1]);
+      f.u.w = pack_bf16x2(bb[2], bb[3]);
     } else {
       Frag<float>& f = reinterpret_cast<Frag<float>&>(pf[ks]);
       f.a = make_float4(sacc[2 * ks][0], sacc[2 * ks][1], sacc[2 * ks][2], sacc[2 * ks][3]);
@@ -139,10 +185,86 @@ __device__ __forceinline__ void attend_tile(const Frag<T> (&kf)[C / 16][D / 32],
   for (int mt = 0; mt < MO; ++mt) {
     oacc[mt] = zero4();
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) mma(oacc[mt], vf[mt][ks], pf[ks]);
+    for (int ks = 0; ks < KS; ++ks) mma(oacc[mt], vfrag(mt, ks), pf[ks]);
   }
   inv = any ? 1.f / lsum : 0.f;
   lse = any ? scale * ms + kLn2 * fast_log2(lsum) : kNegInf;
+}
+
+template <typename T, int D, int C>
+__device__ __forceinline__ void attend_tile(const Frag<T> (&kf)[C / 16][D / 32], const Frag<T> (&vf)[D / 16][C / 32],
+                                            const Frag<T> (&qf)[D / 32], long long t0, long long ic, float scale,
+                                            f32x4 (&oacc)[D / 16], float& lse, float& inv) {
+  attend_tile_kv<T, D, C>([&](int m, int s) -> const Frag<T>& { return kf[m][s]; },
+                          [&](int mt, int ks) -> const Frag<T>& { return vf[mt][ks]; }, qf, t0, ic, scale, oacc, lse,
+                          inv);
+}
+
+// ---- work-group shared bf16 tiles (C x D keys, swizzled; D x (C + 8) transposed values)
+// 16-byte chunk c of key row t is stored at chunk c ^ kswz(t): the 16 rows that one K-fragment read
+// touches (attn_token of one M-tile) then fall on distinct chunk columns, so the read is free of
+// bank conflicts.
+template <int D>
+__device__ __forceinline__ int kswz(int t) {
+  return ((t & 3) | ((t >> 1) & 12)) & (D / 8 - 1);
+}
+
+// Cooperative staging by the work-group's 256 threads: K rows into sk (swizzled), V^T into svt.
+// Tokens past N repeat token N - 1 (masked for every query).
+template <int D, int C>
+__device__ __forceinline__ void stage_kv_wg(const uint16_t* kbh, const uint16_t* vbh, long long t0, long long N,
+                                            uint16_t (*sk)[D], uint16_t (*svt)[C + 8]) {
+  const int tid = threadIdx.x;
+  constexpr int CHR = D / 8;  // 16-byte chunks per row
+  // K: C * CHR chunks; V: (C / 2) * CHR (token pair, chunk) items
+  constexpr int KN = C * CHR, VN = (C / 2) * CHR;
+  constexpr int KIT = (KN + 255) / 256, VIT = (VN + 255) / 256;
+  uint4 kk[KIT], v0[VIT], v1[VIT];
+#pragma unroll
+  for (int it = 0; it < KIT; ++it) {
+    const int x = it * 256 + tid, t = x / CHR, c = x % CHR;
+    long long tt = t0 + t;
+    tt = tt < N ? tt : N - 1;
+    if (KN % 256 == 0 || x < KN) kk[it] = *reinterpret_cast<const uint4*>(kbh + tt * D + 8 * c);
+  }
+#pragma unroll
+  for (int it = 0; it < VIT; ++it) {
+    const int x = it * 256 + tid, tp = x / CHR, c0 = (x % CHR) * 8;
+    long long ta = t0 + 2 * tp, tb = ta + 1;
+    ta = ta < N ? ta : N - 1;
+    tb = tb < N ? tb : N - 1;
+    if (VN % 256 == 0 || x < VN) {
+      v0[it] = *reinterpret_cast<const uint4*>(vbh + ta * D + c0);
+      v1[it] = *reinterpret_cast<const uint4*>(vbh + tb * D + c0);
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < KIT; ++it) {
+    const int x = it * 256 + tid, t = x / CHR, c = x % CHR;
+    if (KN % 256 == 0 || x < KN) *reinterpret_cast<uint4*>(&sk[t][8 * (c ^ kswz<D>(t))]) = kk[it];
+  }
+#pragma unroll
+  for (int it = 0; it < VIT; ++it) {
+    const int x = it * 256 + tid, tp = x / CHR, c0 = (x % CHR) * 8;
+    if (VN % 256 != 0 && x >= VN) continue;
+    const uint32_t a[4] = {v0[it].x, v0[it].y, v0[it].z, v0[it].w};
+    const uint32_t b[4] = {v1[it].x, v1[it].y, v1[it].z, v1[it].w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t w = __builtin_amdgcn_perm(b[e >> 1], a[e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
+      *reinterpret_cast<uint32_t*>(&svt[attn_vt_row<D>(c0 + e)][2 * tp]) = w;
+    }
+  }
+}
+
+// K A-fragment (S M-tile m, k step s) from the swizzled shared tile.
+template <int D>
+__device__ __forceinline__ Frag<uint16_t> k_frag_wg(const uint16_t (*sk)[D], int m, int s) {
+  const int r16 = lane_id() & 15, grp = lane_id() >> 4;
+  const int t = attn_token(m, r16 >> 2, r16 & 3);
+  Frag<uint16_t> f;
+  f.u = *reinterpret_cast<const uint4*>(&sk[t][8 * ((4 * s + grp) ^ kswz<D>(t))]);
+  return f;
 }
 
 }  // namespace pisa

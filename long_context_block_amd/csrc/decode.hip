@@ -253,7 +253,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams<T> p) {
 #pragma unroll
   for (int mt = 0; mt < MO; ++mt)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) s_o[wave][r16][16 * mt + 4 * grp + j] = run_o[mt][j];
+    for (int j = 0; j < 4; ++j) s_o[wave][r16][attn_out_dim<D>(mt, grp, j)] = run_o[mt][j];
   if (grp == 0) s_lse[wave][r16] = run_lse;
   __syncthreads();
   for (int x = tid; x < p.G * D; x += 256) {
