@@ -13,6 +13,7 @@
 #include "attn_tiles.hpp"
 #include "common.hpp"
 #include "internal.hpp"
+#include "pair_runs.hpp"
 
 namespace pisa {
 
@@ -169,37 +170,14 @@ __global__ __launch_bounds__(256, 3) void attn_leaf_wg_kernel(AttnParams<uint16_
   if (base >= total) return;  // whole work-group
   const int n = (int)(total - base < kWgTask ? total - base : kWgTask);
   const long long nch = ((long long)p.N + (1LL << p.chunk_log2) - 1) >> p.chunk_log2;
-  // ---- pairs and their bucket keys (KV head, position chunk, leaf)
-  for (int x = tid; x < n; x += 256) {
-    const uint32_t pr = p.pairs[base + x];
-    const long long u = pr >> 5;
-    s_pair[x] = pr;
-    s_key[x] = ((u / p.N) * nch + ((u % p.N) >> p.chunk_log2)) * (1LL << 32) + p.sel[u * p.K + (pr & 31)];
-  }
-  __syncthreads();
-  // ---- run starts, in order: wave w scans entries [256 w, 256 w + 256)
-  int cnt = 0;
-  uint64_t masks[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int x = wave * 256 + j * 64 + lane;
-    const bool start = x < n && (x == 0 || s_key[x] != s_key[x - 1]);
-    masks[j] = __ballot(start);
-    cnt += __popcll(masks[j]);
-  }
-  if (lane == 0) s_wcount[wave] = cnt;
-  __syncthreads();
-  int off = 0;
-  for (int w = 0; w < wave; ++w) off += s_wcount[w];
-  const int nrun = s_wcount[0] + s_wcount[1] + s_wcount[2] + s_wcount[3];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int x = wave * 256 + j * 64 + lane;
-    if ((masks[j] >> lane) & 1) s_run[off + __popcll(masks[j] & ((1ull << lane) - 1))] = x;
-    off += __popcll(masks[j]);
-  }
-  if (tid == 0) s_run[nrun] = n;
-  __syncthreads();
+  // pairs, their bucket keys (KV head, position chunk, leaf) and the runs of equal keys
+  const int nrun = stage_pair_runs<kWgTask>(
+      p.pairs, base, n,
+      [&](uint32_t pr) {
+        const long long u = pr >> 5;
+        return ((u / p.N) * nch + ((u % p.N) >> p.chunk_log2)) * (1LL << 32) + p.sel[u * p.K + (pr & 31)];
+      },
+      s_pair, s_key, s_run, s_wcount);
   const int tile_units = 16 / p.G;
   const int h = r16 % p.G;
   for (int r = 0; r < nrun; ++r) {
@@ -226,11 +204,6 @@ __global__ __launch_bounds__(256, 3) void attn_leaf_wg_kernel(AttnParams<uint16_
       const uint16_t* qrow = qhead + ((long long)(pc >> 5) - ubase) * D;
 #pragma unroll
       for (int s2 = 0; s2 < D / 32; ++s2) qf[s2].load(qrow + 32 * s2);
-    };
-    auto opaque = [&](Frag<uint16_t> (&qf)[D / 32]) {
-#pragma unroll
-      for (int s2 = 0; s2 < D / 32; ++s2)
-        asm volatile("" : "+v"(qf[s2].u.x), "+v"(qf[s2].u.y), "+v"(qf[s2].u.z), "+v"(qf[s2].u.w));
     };
     struct Out {
       f32x4 o[MO];
@@ -267,8 +240,8 @@ __global__ __launch_bounds__(256, 3) void attn_leaf_wg_kernel(AttnParams<uint16_
       uint32_t pa, pb;
       fetch(wave, qa, pa);
       fetch(wave + 4, qb, pb);
-      opaque(qa);
-      opaque(qb);
+      opaque_frags(qa);
+      opaque_frags(qb);
       for (int t = wave; t < ntiles; t += 8) {
         Out out;
         attend(qa, pa, out);
@@ -293,42 +266,102 @@ struct MergeParams {
   float* o_lse;
 };
 
-// One wave per unit; lane e covers output columns e and e + 64 (D = 128) or e (D = 64).
+// Merge. A (unit, head) output row is one task, handled by DC = D / E lanes (E elements per 16-byte
+// chunk); a wave takes 64 / DC consecutive tasks, so for G >= 64 / DC its loads of one slot cover the
+// unit's G heads in one contiguous run. Per task: M = max_k lse_k, S = sum_k exp(lse_k - M),
+// o = sum_k (exp(lse_k - M) / S) partial_k, LSE = M + ln S. Slots k < nsel hold the selected leaves
+// (selections are left-packed), so only those partial rows are read.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(MergeParams<T> p) {
-  constexpr int PER = D / 64;
+  constexpr int E = 16 / (int)sizeof(T);  // elements per chunk
+  constexpr int DC = D / E;               // lanes per task
+  constexpr int KJ = (32 + DC - 1) / DC;  // lse registers per lane (K <= 32)
   const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int li = lane % DC, base = lane - li;
   const long long U = (long long)p.B * p.Hkv * p.N;
-  const long long u = (long long)xcd_logical_block(gridDim.x) * 4 + wave;
-  if (u >= U) return;
+  const long long task = ((long long)xcd_logical_block(gridDim.x) * 4 + wave) * (64 / DC) + lane / DC;
+  const bool live = task < U * p.G;
+  const long long u = live ? task / p.G : 0;
+  const int h = (int)(task % p.G);
+  // selected slots of u (left-packed)
+  int nsel = 0;
+#pragma unroll
+  for (int j = 0; j < KJ; ++j) {
+    const int kk = li + j * DC;
+    const bool has = live && kk < p.K && p.sel[u * p.K + kk] >= 0;
+    const uint64_t m = __ballot(has);
+    nsel += __popcll((m >> base) & (DC == 64 ? ~0ull : ((1ull << DC) - 1)));
+  }
+  float lv[KJ];
+  float mx = kNegInf;
+#pragma unroll
+  for (int j = 0; j < KJ; ++j) {
+    const int kk = li + j * DC;
+    lv[j] = kk < nsel ? p.part_lse[(u * p.K + kk) * p.G + h] : kNegInf;
+    mx = fmaxf(mx, lv[j]);
+  }
+#pragma unroll
+  for (int o = 1; o < DC; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  float ws = 0.f;
+#pragma unroll
+  for (int j = 0; j < KJ; ++j) {
+    lv[j] = lv[j] == kNegInf ? 0.f : fast_exp2((lv[j] - mx) * kLog2e);
+    ws += lv[j];
+  }
+#pragma unroll
+  for (int o = 1; o < DC; o <<= 1) ws += __shfl_xor(ws, o);
+  const float rs = ws > 0.f ? 1.f / ws : 0.f;
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  // the wave's tasks may have different nsel: loop to the wave's largest, lanes past theirs add 0
+  int nmax = nsel;
+#pragma unroll
+  for (int o = DC; o < 64; o <<= 1) nmax = max(nmax, __shfl_xor(nmax, o));
+  const T* src = p.part + (u * p.K * p.G + h) * (long long)D + li * E;
+  for (int kk = 0; kk < nmax; ++kk) {
+    const float w0 = __shfl(lv[0], base + (kk % DC));
+    float w = w0;
+#pragma unroll
+    for (int j = 1; j < KJ; ++j) {
+      const float wj = __shfl(lv[j], base + (kk % DC));
+      w = (kk / DC == j) ? wj : w;
+    }
+    if (kk < nsel) {
+      w *= rs;
+      if constexpr (sizeof(T) == 2) {
+        const uint4 x = *reinterpret_cast<const uint4*>(src + (long long)kk * p.G * D);
+        const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] += w * __uint_as_float(xs[e] << 16);
+          acc[2 * e + 1] += w * __uint_as_float(xs[e] & 0xffff0000u);
+        }
+      } else {
+        const float4 x = *reinterpret_cast<const float4*>(src + (long long)kk * p.G * D);
+        acc[0] += w * x.x;
+        acc[1] += w * x.y;
+        acc[2] += w * x.z;
+        acc[3] += w * x.w;
+      }
+    }
+  }
+  if (!live) return;
   const long long bh = u / p.N, i = u % p.N;
   const int b = (int)(bh / p.Hkv), r = (int)(bh % p.Hkv);
-  const bool has = lane < p.K && p.sel[u * p.K + lane] >= 0;
-  const int nsel = __popcll(__ballot(has));
-  for (int h = 0; h < p.G; ++h) {
-    const float pl = has ? p.part_lse[(u * p.K + lane) * p.G + h] : kNegInf;
-    float m = pl;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
-    const float w = has ? fast_exp2((pl - m) * kLog2e) : 0.f;
-    float ws = w;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) ws += __shfl_xor(ws, o);
-    const float lse = m + kLn2 * fast_log2(ws);
-    float acc[PER];
-#pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-    for (int kk = 0; kk < nsel; ++kk) {
-      const float wk = readlane(w, kk) / ws;
-      const T* src = p.part + ((u * p.K + kk) * p.G + h) * D;
-#pragma unroll
-      for (int e = 0; e < PER; ++e) acc[e] += wk * to_f32<T>(src[lane + 64 * e]);
-    }
-    const long long orow = ((long long)b * p.Hq + (long long)r * p.G + h) * p.N + i;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) p.o[orow * D + lane + 64 * e] = from_f32<T>(acc[e]);
-    if (p.o_lse && lane == 0) p.o_lse[orow] = lse;
+  const long long orow = ((long long)b * p.Hq + (long long)r * p.G + h) * p.N + i;
+  T* dst = p.o + orow * D + li * E;
+  if constexpr (sizeof(T) == 2) {
+    uint4 w;
+    w.x = pack_bf16x2(acc[0], acc[1]);
+    w.y = pack_bf16x2(acc[2], acc[3]);
+    w.z = pack_bf16x2(acc[4], acc[5]);
+    w.w = pack_bf16x2(acc[6], acc[7]);
+    *reinterpret_cast<uint4*>(dst) = w;
+  } else {
+    *reinterpret_cast<float4*>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
   }
+  if (p.o_lse && li == 0) p.o_lse[orow] = ws > 0.f ? mx + kLn2 * fast_log2(ws) : kNegInf;
 }
 
 // ------------------------------------------------------------------------------------------ launchers
@@ -400,8 +433,10 @@ static hipError_t merge_t(const SelDims& sd, const int* sel, const void* part, c
   p.K = sd.K;
   p.o = (T*)o;
   p.o_lse = o_lse;
-  const long long U = (long long)sd.B * sd.Hkv * sd.N;
-  hipLaunchKernelGGL((attn_merge_kernel<T, D>), dim3((unsigned)((U + 3) / 4)), dim3(256), 0, st, p);
+  const long long tasks = (long long)sd.B * sd.Hkv * sd.N * sd.G;
+  constexpr int per_wave = 64 / (D / (16 / (int)sizeof(T)));
+  const long long waves = (tasks + per_wave - 1) / per_wave;
+  hipLaunchKernelGGL((attn_merge_kernel<T, D>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 

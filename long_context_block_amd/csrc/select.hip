@@ -24,6 +24,7 @@
 // per-column arithmetic and sum the heads in the same order, so their outputs agree bit for bit.
 #include "common.hpp"
 #include "internal.hpp"
+#include "pair_runs.hpp"
 #include "walk_tiles.hpp"
 
 namespace pisa {
@@ -270,6 +271,96 @@ __global__ __launch_bounds__(256) void leaf_lse_kernel(LeafParams<T> p) {
   }
 }
 
+// bf16, work-group cooperative leaf stage: a work-group task is kLeafWgTask consecutive sorted pairs;
+// for each run (one KV head and level-1 node) the 256 threads stage the node's two leaves (2C keys)
+// into LDS, then the four waves take the run's tiles of q_tile units x G heads round-robin, reading
+// every K fragment from LDS. The per-column arithmetic (fragment values, MFMA order, LSE code) is the
+// unit-major leaf stage's, so both give the same bits.
+constexpr int kLeafWgTask = 1024;
+
+template <int D, int C>
+__global__ __launch_bounds__(256, 3) void leaf_lse_wg_kernel(LeafParams<uint16_t> p) {
+  __shared__ __align__(16) uint16_t s_k[2 * C][D];
+  __shared__ uint32_t s_pair[kLeafWgTask];
+  __shared__ long long s_key[kLeafWgTask];
+  __shared__ int s_run[kLeafWgTask + 1];
+  __shared__ int s_wcount[4];
+  const int lane = lane_id(), wave = threadIdx.x >> 6, r16 = lane & 15, grp = lane >> 4;
+  const long long total = *p.total;
+  const long long base = (long long)xcd_logical_block(gridDim.x) * kLeafWgTask;
+  if (base >= total) return;  // whole work-group
+  const int n = (int)(total - base < kLeafWgTask ? total - base : kLeafWgTask);
+  const long long nch = ((long long)p.N + (1LL << p.chunk_log2) - 1) >> p.chunk_log2;
+  const int nrun = stage_pair_runs<kLeafWgTask>(
+      p.pairs, base, n,
+      [&](uint32_t pr) {
+        const long long u = pr >> 5;
+        return ((u / p.N) * nch + ((u % p.N) >> p.chunk_log2)) * (1LL << 32) + p.kept[u * p.K + (pr & 31)];
+      },
+      s_pair, s_key, s_run, s_wcount);
+  const int h = r16 % p.G;
+  const int cols = p.q_tile * p.G;
+  for (int r = 0; r < nrun; ++r) {
+    const int a = s_run[r], b = s_run[r + 1];
+    const long long u0 = s_pair[a] >> 5;
+    const long long bh = u0 / p.N;
+    const int node = (int)(s_key[a] & 0xffffffffLL);
+    const long long t0 = 2LL * node * C;
+    const uint16_t* kbh = p.k + bh * (long long)p.N * D;
+    stage_leaf_pair_wg<D, C>(kbh, t0, p.N, s_k);
+    __syncthreads();
+    const int bi = (int)(bh / p.Hkv), ri = (int)(bh % p.Hkv);
+    const uint16_t* qhead = p.q + (((long long)bi * p.Hq + (long long)ri * p.G + h) * p.N) * D + 8 * grp;
+    const long long ubase = bh * p.N;
+    const int ntiles = (b - a + p.q_tile - 1) / p.q_tile;
+    // A column past the run, past the tile's q_tile units, or past the wave's last tile repeats the
+    // run's first pair: it computes that pair's values again and stores the same bits to the same place.
+    auto fetch = [&](int t, Frag<uint16_t> (&qf)[D / 32], uint32_t& pc) {
+      int x = a + t * p.q_tile + r16 / p.G;
+      x = (t < ntiles && r16 < cols && x < b) ? x : a;
+      pc = s_pair[x];
+      const uint16_t* qrow = qhead + ((long long)(pc >> 5) - ubase) * D;
+#pragma unroll
+      for (int s2 = 0; s2 < D / 32; ++s2) qf[s2].load(qrow + 32 * s2);
+    };
+    struct Out {
+      float l0, l1;
+      uint32_t pc;
+    };
+    auto score = [&](const Frag<uint16_t> (&qf)[D / 32], uint32_t pc, Out& out) {
+      out.pc = pc;
+      leaf_pair_lse_k<uint16_t, D, C, true>([&](int m, int s2) { return leaf_k_frag_wg<D>(s_k, m, s2); }, qf, t0,
+                                      (long long)(pc >> 5) - ubase, p.scale, out.l0, out.l1);
+    };
+    auto store = [&](const Out& out) {
+      // the column's 4 lanes hold the same values
+      float* dst = p.leaf_lse + ((long long)(out.pc >> 5) * p.K + (out.pc & 31)) * 2 * p.G + h;
+      dst[0] = out.l0;
+      dst[p.G] = out.l1;
+    };
+    if (wave < ntiles) {
+      // two register sets in turn: this wave's tiles t and t + 4 run while the queries of t + 8 and
+      // t + 12 are in flight
+      Frag<uint16_t> qa[D / 32], qb[D / 32];
+      uint32_t pa, pb;
+      fetch(wave, qa, pa);
+      fetch(wave + 4, qb, pb);
+      opaque_frags(qa);
+      opaque_frags(qb);
+      for (int t = wave; t < ntiles; t += 8) {
+        Out out;
+        score(qa, pa, out);
+        fetch(t + 8, qa, pa);
+        store(out);
+        score(qb, pb, out);
+        fetch(t + 12, qb, pb);
+        store(out);
+      }
+    }
+    __syncthreads();  // every wave is done with this node's keys before they are restaged
+  }
+}
+
 template <typename T>
 struct FinParams {
   const int* kept;
@@ -477,10 +568,16 @@ static hipError_t leaf_t(const SelDims& sd, const void* q, const void* k, const 
   p.scale = sd.scale;
   p.leaf_lse = leaf_lse;
   const long long max_pairs = (long long)sd.B * sd.Hkv * sd.N * sd.K;
-  const long long tasks = (max_pairs + kLeafTask - 1) / kLeafTask;
-  p.tasks = (int)tasks;
-  const long long blocks = (tasks + 3) / 4;
-  hipLaunchKernelGGL((leaf_lse_kernel<T, D, C>), dim3((unsigned)blocks), dim3(256), 0, st, p);
+  if constexpr (sizeof(T) == 2) {
+    const long long wg = (max_pairs + kLeafWgTask - 1) / kLeafWgTask;
+    p.tasks = (int)wg;
+    hipLaunchKernelGGL((leaf_lse_wg_kernel<D, C>), dim3((unsigned)wg), dim3(256), 0, st, p);
+  } else {
+    const long long tasks = (max_pairs + kLeafTask - 1) / kLeafTask;
+    p.tasks = (int)tasks;
+    const long long blocks = (tasks + 3) / 4;
+    hipLaunchKernelGGL((leaf_lse_kernel<T, D, C>), dim3((unsigned)blocks), dim3(256), 0, st, p);
+  }
   return hipGetLastError();
 }
 

@@ -276,9 +276,12 @@ __device__ __forceinline__ void load_leaf_pair(const T* kbh, long long t0, int N
 }
 
 // Per-column LSE over leaf 2p (lse0) and leaf 2p+1 (lse1) of scale * q_col . k_t for t <= icol.
-template <typename T, int D, int C>
-__device__ __forceinline__ void leaf_pair_lse(const Frag<T> (&kf)[C / 8][D / 32], const Frag<T> (&qf)[D / 32],
-                                              long long t0, long long icol, float scale, float& lse0, float& lse1) {
+// kfrag(m, s) returns the A-fragment of tokens t0 + 16 m + (0..15), k step s.
+// kPhased: a scheduling fence after each k step, so that LDS-sourced fragments of one step at a time
+// are live (the arithmetic is unchanged).
+template <typename T, int D, int C, bool kPhased = false, typename KFrag>
+__device__ __forceinline__ void leaf_pair_lse_k(KFrag kfrag, const Frag<T> (&qf)[D / 32], long long t0,
+                                                long long icol, float scale, float& lse0, float& lse1) {
   constexpr int MT = C / 8;
   constexpr int ML = C / 16;  // M-tiles per leaf
   const int grp = lane_id() >> 4;
@@ -288,7 +291,8 @@ __device__ __forceinline__ void leaf_pair_lse(const Frag<T> (&kf)[C / 8][D / 32]
 #pragma unroll
   for (int s = 0; s < D / 32; ++s) {
 #pragma unroll
-    for (int m = 0; m < MT; ++m) mma(acc[m], kf[m][s], qf[s]);
+    for (int m = 0; m < MT; ++m) mma(acc[m], kfrag(m, s), qf[s]);
+    if constexpr (kPhased) __builtin_amdgcn_sched_barrier(0);
   }
   // causal mask on offsets within the tile: token t0 + o is visible iff o <= icol - t0
   const long long lim64 = icol - t0;
@@ -310,6 +314,53 @@ __device__ __forceinline__ void leaf_pair_lse(const Frag<T> (&kf)[C / 8][D / 32]
     else
       lse1 = l;
   }
+}
+
+template <typename T, int D, int C>
+__device__ __forceinline__ void leaf_pair_lse(const Frag<T> (&kf)[C / 8][D / 32], const Frag<T> (&qf)[D / 32],
+                                              long long t0, long long icol, float scale, float& lse0, float& lse1) {
+  leaf_pair_lse_k<T, D, C>([&](int m, int s) -> const Frag<T>& { return kf[m][s]; }, qf, t0, icol, scale, lse0,
+                           lse1);
+}
+
+// ---- work-group shared bf16 key tile of a leaf pair (2C x D rows in LDS)
+// 16-byte chunk c of row t is stored at chunk c ^ (t mod D/8): the 16 consecutive rows that one
+// A-fragment read touches then fall on distinct chunk columns (no bank conflicts).
+template <int D>
+__device__ __forceinline__ int leaf_kswz(int t) {
+  return t & (D / 8 - 1);
+}
+
+// Cooperative staging by 256 threads of tokens t0 .. t0 + 2C - 1 (past N: token N - 1, which the
+// causal mask drops for every query).
+template <int D, int C>
+__device__ __forceinline__ void stage_leaf_pair_wg(const uint16_t* kbh, long long t0, long long N,
+                                                   uint16_t (*sk)[D]) {
+  constexpr int CHR = D / 8, NCH = 2 * C * CHR, IT = NCH / 256;
+  static_assert(NCH % 256 == 0, "tile shape");
+  const int tid = threadIdx.x;
+  uint4 kk[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int x = it * 256 + tid, t = x / CHR, c = x % CHR;
+    long long tt = t0 + t;
+    tt = tt < N ? tt : N - 1;
+    kk[it] = *reinterpret_cast<const uint4*>(kbh + tt * D + 8 * c);
+  }
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int x = it * 256 + tid, t = x / CHR, c = x % CHR;
+    *reinterpret_cast<uint4*>(&sk[t][8 * (c ^ leaf_kswz<D>(t))]) = kk[it];
+  }
+}
+
+template <int D>
+__device__ __forceinline__ Frag<uint16_t> leaf_k_frag_wg(const uint16_t (*sk)[D], int m, int s) {
+  const int r16 = lane_id() & 15, grp = lane_id() >> 4;
+  const int t = 16 * m + r16;
+  Frag<uint16_t> f;
+  f.u = *reinterpret_cast<const uint4*>(&sk[t][8 * ((4 * s + grp) ^ leaf_kswz<D>(t))]);
+  return f;
 }
 
 }  // namespace pisa
