@@ -39,7 +39,7 @@ hipError_t launch_split_hilo(const float* mean, long long rows, int D, uint16_t*
 // Selection. `nodes` is the bf16 hi/lo pyramid (bf16 inputs) or the fp32 means (fp32 inputs).
 hipError_t launch_route(const SelDims& sd, const void* q, const void* k, const void* nodes, const float* norms,
                         bool fused, int* kept, int* sel, float* sel_lse, hipStream_t st);
-// |row| (Euclidean norm over d) of each fp32 pyramid row.
+// Per-row bound b >= |q . lo| / |q| (plus accumulation slack) for the bf16 hi/lo planes of each row.
 hipError_t launch_row_norms(const float* mean, long long rows, int D, float* norms, hipStream_t st);
 
 // Bucket (unit, slot) pairs by node: node lists [U, K] (-1 = none) -> pairs sorted by

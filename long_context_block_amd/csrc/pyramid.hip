@@ -171,20 +171,29 @@ __global__ __launch_bounds__(256) void split_hilo_kernel(const float* __restrict
   }
 }
 
-// Euclidean norm of each fp32 row (one wave per row).
+// Per-row bound for the bf16 hi-plane score (one wave per row): b = 1.05 |lo| + 2^-16 |mean|, where
+// lo = rne(mean - rne(mean)) is the stored lo plane. For any q, |q . (hi + lo) - q . hi| = |q . lo|
+// <= |q| |lo| (Cauchy-Schwarz); the 2^-16 |mean| term covers the fp32 accumulation of 128-term dot
+// products (each order of summation errs by under 2^-17 |q| |mean|) and the 1.05 the rounding of the
+// norms themselves.
 __global__ __launch_bounds__(256) void row_norms_kernel(const float* __restrict__ mean, long long rows, int D,
                                                        float* __restrict__ norms) {
   const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
   const int lane = threadIdx.x & 63;
-  float s = 0.f;
+  float sm = 0.f, sl = 0.f;
   for (int c = lane; c < D; c += 64) {
     const float x = mean[row * D + c];
-    s += x * x;
+    const float lo = bf16_to_f32(f32_to_bf16(x - bf16_to_f32(f32_to_bf16(x))));
+    sm += x * x;
+    sl += lo * lo;
   }
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) s += __shfl_xor(s, o);
-  if (lane == 0) norms[row] = sqrtf(s);
+  for (int o = 1; o < 64; o <<= 1) {
+    sm += __shfl_xor(sm, o);
+    sl += __shfl_xor(sl, o);
+  }
+  if (lane == 0) norms[row] = 1.05f * sqrtf(sl) + 1.52587890625e-05f * sqrtf(sm);
 }
 
 // ------------------------------------------------------------------------------------------ host

@@ -34,7 +34,7 @@ struct RouteParams {
   const T* q;
   const T* k;
   const void* nodes;
-  const float* norms;  // |mean| per pyramid row (bf16 path)
+  const float* norms;  // hi-plane score bound per pyramid row (bf16 path)
   int B, Hq, Hkv, G, N, K, upw;
   float scale;
   Levels lv;

@@ -116,13 +116,10 @@ __device__ void score_candidates(const Rows& rows, int level_off, const Frag<T> 
   __threadfence_block();
 }
 
-// Relative bound on |q . (mean - hi)| / (|q| |mean|) for the bf16 hi plane: round-to-nearest-even to
-// bf16 errs by at most 2^-8 of the value, per element; the factor covers the fp32 accumulation.
-constexpr float kHiRelBound = 0.00391f * 1.05f;
-
 // One scored level on the bf16 path, in two passes over the <= 4K child rows. Pass 1 uses the hi plane
-// only; a candidate's score then lies within E_c = scale * kHiRelBound * sum_h |q_h| * max child |mean|
-// of its hi+lo score (LSE is 1-Lipschitz in the max norm, per head). With the Top-K of the hi scores
+// only; a candidate's score then lies within E_c = scale * sum_h |q_h| * max over its children of the
+// row bound b (b >= |q . lo| / |q| plus the accumulation slack, per row) of its hi+lo score (LSE is
+// 1-Lipschitz in the max norm, per head). With the Top-K of the hi scores
 // as the "in" group, a candidate is decided by pass 1 when its interval cannot cross the boundary (an
 // "in" candidate whose lower end is above every "out" upper end, or an "out" candidate whose upper end
 // is below every "in" lower end); the rest get the lo plane added (pass 2) and compete by their hi+lo
@@ -177,7 +174,7 @@ __device__ bool select_level_refine(const NodeRows<uint16_t, D>& rows, const flo
   if (lane < n_cand) {
     const float n0 = norms[level_off + 2 * cn];
     const float n1 = lane < n_full ? norms[level_off + 2 * cn + 1] : 0.f;
-    e = scale * kHiRelBound * qnorm_sum * fmaxf(n0, n1);
+    e = scale * qnorm_sum * fmaxf(n0, n1);
   }
   __threadfence_block();
   const float sh = lane < n_cand ? s_sc[lane] : kNegInf;
