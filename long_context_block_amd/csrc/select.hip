@@ -158,6 +158,69 @@ __global__ __launch_bounds__(256, FUSED ? 2 : 4) void route_kernel(RouteParams<T
   }
 }
 
+// bf16 routing with the upper pyramid levels in LDS. One work-group of 16 waves per CU and KV head
+// slice: the hi plane of pyramid rows [lds_first, nodes) of KV head bh (<= kRouteLdsBytes) is staged
+// into LDS once, then the waves walk units of that head (groups of kRouteUnits consecutive positions,
+// spread round-robin over the head's work-groups). Child rows of those levels are read from LDS; the
+// two largest levels and all lo rows come from global memory (L2). Same arithmetic as route_kernel.
+constexpr int kRouteLdsBytes = 128 * 1024;
+constexpr int kRouteUnits = 4;
+
+template <int D, int C, int KM>
+__global__ __launch_bounds__(1024) void route_lds_kernel(RouteParams<uint16_t> p, int lds_first, int wg_per_head) {
+  constexpr int kLog2C = C == 64 ? 6 : 5;
+  __shared__ __align__(16) uint16_t s_hi[kRouteLdsBytes / 2];
+  __shared__ __align__(16) float s_sc[16][64];
+  __shared__ __align__(16) uint32_t s_key[16][64];
+  const int lane = lane_id(), wave = threadIdx.x >> 6, r16 = lane & 15, grp = lane >> 4;
+  const int BH = p.B * p.Hkv;
+  const int bh = blockIdx.x % BH, w = blockIdx.x / BH;  // consecutive work-groups: different heads
+  LdsHiRows<D> rows;
+  rows.base = (const uint16_t*)p.nodes + (long long)bh * p.lv.nodes * 2 * D;
+  rows.lds = s_hi;
+  rows.first = lds_first;
+  stage_hi_rows<D>(rows.base, lds_first, (int)(p.lv.nodes - lds_first), s_hi);
+  __syncthreads();
+  const float* norms = p.norms + (long long)bh * p.lv.nodes;
+  const int b = bh / p.Hkv, r = bh % p.Hkv;
+  const bool hv = r16 < p.G;
+  const int groups = (p.N + kRouteUnits - 1) / kRouteUnits;
+  for (int gi = w * 16 + wave; gi < groups; gi += wg_per_head * 16) {
+    for (int it = 0; it < kRouteUnits; ++it) {
+      const int i = gi * kRouteUnits + it;
+      if (i >= p.N) break;
+      const long long u = (long long)bh * p.N + i;
+      Frag<uint16_t> qf[D / 32];
+      const long long qrow0 = ((long long)b * p.Hq + (long long)r * p.G) * p.N + i;
+      const uint16_t* qrow = p.q + (qrow0 + (long long)(hv ? r16 : 0) * p.N) * D + 8 * grp;
+#pragma unroll
+      for (int s2 = 0; s2 < D / 32; ++s2) {
+        if (hv)
+          qf[s2].load(qrow + 32 * s2);
+        else
+          qf[s2].zero();
+      }
+      float sq = 0.f;
+#pragma unroll
+      for (int s2 = 0; s2 < D / 32; ++s2)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = qf[s2].get(e);
+          sq += x * x;
+        }
+      const float sq_all = colgroup_sum(sq);  // every lane takes part in the exchange
+      const float qn = row_sum16(hv ? sqrtf(sq_all) : 0.f);
+      int kept;
+      const int nk =
+          walk_to_level1<uint16_t, D, KM>(p.lv, kLog2C, p.K, i, &kept, [&](int off, int cn, int n_cand, int e_child) {
+            return select_level_refine<D, KM>(rows, norms, off, qf, qn, cn, n_cand, e_child, p.G, p.scale, p.K,
+                                              s_sc[wave], s_key[wave]);
+          });
+      if (lane < p.K) p.kept[u * p.K + lane] = lane < nk ? kept : -1;
+    }
+  }
+}
+
 template <typename T>
 struct LeafParams {
   const T* q;
@@ -518,6 +581,24 @@ static hipError_t route_t(const SelDims& sd, const void* q, const void* k, const
   p.sel = sel;
   p.sel_lse = sel_lse;
   const long long U = (long long)sd.B * sd.Hkv * sd.N;
+  if constexpr (sizeof(T) == 2 && !FUSED) {
+    // LDS-resident upper levels: the smallest level whose rows up to the root fit in kRouteLdsBytes
+    int lcut = 0;
+    while (lcut < sd.lv.n_levels - 1 && (sd.lv.nodes - sd.lv.off[lcut]) * D * 2 > kRouteLdsBytes) ++lcut;
+    const int lds_first = (int)sd.lv.off[lcut];
+    const int BH = sd.B * sd.Hkv;
+    const long long groups = (sd.N + kRouteUnits - 1) / kRouteUnits;
+    long long wph = 256 / BH;  // about one work-group per CU
+    if (wph < 1) wph = 1;
+    if (wph > (groups + 15) / 16) wph = (groups + 15) / 16;
+    if (sd.K <= 16)
+      hipLaunchKernelGGL((route_lds_kernel<D, C, 4>), dim3((unsigned)(BH * wph)), dim3(1024), 0, st, p, lds_first,
+                         (int)wph);
+    else
+      hipLaunchKernelGGL((route_lds_kernel<D, C, 8>), dim3((unsigned)(BH * wph)), dim3(1024), 0, st, p, lds_first,
+                         (int)wph);
+    return hipGetLastError();
+  }
   p.upw = 4;
   const long long waves = (U + p.upw - 1) / p.upw;
   const long long blocks = (waves + 3) / 4;

@@ -31,7 +31,54 @@ struct NodeRows<uint16_t, D> {
       mma(acc, f.lo[s], qf[s]);
     }
   }
+  // hi or lo plane of pyramid row `node` alone (the two passes of the bf16 walk)
+  __device__ __forceinline__ void load_hi(Frag<uint16_t> (&hi)[D / 32], int node, int grp) const {
+    const uint16_t* p = base + (unsigned)node * (2 * D) + 8 * grp;
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) hi[s].load(p + 32 * s);
+  }
+  __device__ __forceinline__ void load_lo(Frag<uint16_t> (&lo)[D / 32], int node, int grp, bool need) const {
+    const uint16_t* p = base + (unsigned)node * (2 * D) + D + 8 * grp;
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) {
+      if (need)
+        lo[s].load(p + 32 * s);
+      else
+        lo[s].zero();
+    }
+  }
 };
+
+// bf16 walk with the hi plane of the upper pyramid rows (node >= first) resident in LDS: local row
+// r = node - first holds D hi values, 16-byte chunk c stored at chunk c ^ (r mod D/8), so the 4
+// consecutive rows of one kept node (its grandchildren) fall on distinct chunk columns. Lower rows and
+// every lo plane are read from global memory.
+template <int D>
+struct LdsHiRows : NodeRows<uint16_t, D> {
+  const uint16_t* lds;
+  int first;
+  __device__ __forceinline__ void load_hi(Frag<uint16_t> (&hi)[D / 32], int node, int grp) const {
+    if (node >= first) {
+      const int r = node - first;
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s)
+        hi[s].u = *reinterpret_cast<const uint4*>(lds + r * D + 8 * ((4 * s + grp) ^ (r & (D / 8 - 1))));
+    } else {
+      NodeRows<uint16_t, D>::load_hi(hi, node, grp);
+    }
+  }
+};
+
+// Cooperative copy of the hi planes of pyramid rows [first, first + n) into lds (layout above).
+template <int D>
+__device__ __forceinline__ void stage_hi_rows(const uint16_t* base, int first, int n, uint16_t* lds) {
+  constexpr int CHR = D / 8;
+  for (int x = threadIdx.x; x < n * CHR; x += blockDim.x) {
+    const int r = x / CHR, c = x % CHR;
+    *reinterpret_cast<uint4*>(lds + r * D + 8 * (c ^ (r & (CHR - 1)))) =
+        *reinterpret_cast<const uint4*>(base + (long long)(first + r) * (2 * D) + 8 * c);
+  }
+}
 
 // fp32 path: row r at base + r*D.
 template <int D>
@@ -125,8 +172,8 @@ __device__ void score_candidates(const Rows& rows, int level_off, const Frag<T> 
 // is below every "in" lower end); the rest get the lo plane added (pass 2) and compete by their hi+lo
 // scores for the remaining places. The kept set is the one the hi+lo scores of every candidate give,
 // while only the lo rows of undecided candidates are read. Returns this lane's keep flag.
-template <int D, int KM>
-__device__ bool select_level_refine(const NodeRows<uint16_t, D>& rows, const float* norms, int level_off,
+template <int D, int KM, class Rows>
+__device__ bool select_level_refine(const Rows& rows, const float* norms, int level_off,
                                     const Frag<uint16_t> (&qf)[D / 32], float qnorm_sum, int cn, int n_cand,
                                     int e_child, int G, float scale, int K, float* s_sc, uint32_t* keys) {
   const int lane = lane_id(), r16 = lane & 15, grp = lane >> 4;
@@ -149,9 +196,7 @@ __device__ bool select_level_refine(const NodeRows<uint16_t, D>& rows, const flo
   for (int m = 0; m < KM; ++m) {
     if (m < MT) {
       Frag<uint16_t> hi[D / 32];
-      const uint16_t* p = rows.base + (unsigned)(level_off + child[m]) * (2 * D) + 8 * grp;
-#pragma unroll
-      for (int s = 0; s < D / 32; ++s) hi[s].load(p + 32 * s);
+      rows.load_hi(hi, level_off + child[m], grp);
       acc[m] = zero4();
 #pragma unroll
       for (int s = 0; s < D / 32; ++s) mma(acc[m], hi[s], qf[s]);
@@ -193,14 +238,7 @@ __device__ bool select_level_refine(const NodeRows<uint16_t, D>& rows, const flo
       const int cidx = (16 * m + r16) >> 1;
       const bool need = valid[m] && ((rmask >> cidx) & 1ull);
       Frag<uint16_t> lo[D / 32];
-      const uint16_t* p = rows.base + (unsigned)(level_off + child[m]) * (2 * D) + D + 8 * grp;
-#pragma unroll
-      for (int s = 0; s < D / 32; ++s) {
-        if (need)
-          lo[s].load(p + 32 * s);
-        else
-          lo[s].zero();
-      }
+      rows.load_lo(lo, level_off + child[m], grp, need);
 #pragma unroll
       for (int s = 0; s < D / 32; ++s) mma(acc[m], lo[s], qf[s]);
       cand_scores(m, rmask);
