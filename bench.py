@@ -246,7 +246,7 @@ def main():
 
     sel_np = sel.cpu().numpy()
     w = work_counts(pf, sel_np)
-    sel_stage_names = ["pyramid", "split_hilo", "route", "regroup_select", "leaf_lse", "finalize", "route_fused_leaf"]
+    sel_stage_names = ["pyramid", "route_planes", "route", "regroup_select", "leaf_lse", "finalize", "route_fused_leaf"]
     selection_ms = sum(st_ms.get(n, 0.0) for n in sel_stage_names)
     attn_ms = sum(st_ms.get(n, 0.0) for n in ("regroup_attn", "attn_leaf", "attn_merge"))
     bsa_ms = st_ms.get("bsa_pool", 0.0) + st_ms.get("bsa_select", 0.0)

@@ -186,6 +186,8 @@ struct Carver {
 struct SelectWs {
   uint16_t* hilo;
   float* norms;
+  int* hexp;
+  float* part_max;
   int* kept;
   int* counts;
   int* offsets;
@@ -200,6 +202,8 @@ size_t carve_select(const Plan& p, void* ws, SelectWs* w) {
   if (p.sd.bf16) {
     x.hilo = (uint16_t*)c.take((size_t)p.BH * p.sd.lv.nodes * 2 * p.sd.D * 2);
     x.norms = (float*)c.take((size_t)p.BH * p.sd.lv.nodes * 4);
+    x.hexp = (int*)c.take((size_t)p.BH * 4);
+    x.part_max = (float*)c.take((size_t)p.BH * 64 * 4);
   }
   if (p.sd.q_tile > 1) {
     const size_t pairs = (size_t)p.U * p.sd.K;
@@ -365,23 +369,22 @@ pisa_status pisa_select(const pisa_shape* shape, const void* q, const void* k, c
   const void* nodes = pyr_mean;
   if (p.sd.bf16) {
     {
-      Stage sc(s, "split_hilo");
-      e = pisa::launch_split_hilo(pyr_mean, p.BH * p.sd.lv.nodes, p.sd.D, w.hilo, s);
-      if (e == hipSuccess) e = pisa::launch_row_norms(pyr_mean, p.BH * p.sd.lv.nodes, p.sd.D, w.norms, s);
+      Stage sc(s, "route_planes");
+      e = pisa::launch_route_planes(pyr_mean, p.BH, p.sd.lv.nodes, p.sd.D, w.part_max, w.hexp, w.hilo, w.norms, s);
     }
-    if (e != hipSuccess) return hip_status(e, "split_hilo");
+    if (e != hipSuccess) return hip_status(e, "route_planes");
     nodes = w.hilo;
   }
   if (p.sd.q_tile == 1) {
     {
       Stage sc(s, "route_fused_leaf");
-      e = pisa::launch_route(p.sd, q, k, nodes, w.norms, true, nullptr, sel, sel_lse, s);
+      e = pisa::launch_route(p.sd, q, k, nodes, w.norms, w.hexp, true, nullptr, sel, sel_lse, s);
     }
     return hip_status(e, "route (fused leaf stage)");
   }
   {
     Stage sc(s, "route");
-    e = pisa::launch_route(p.sd, q, k, nodes, w.norms, false, w.kept, nullptr, nullptr, s);
+    e = pisa::launch_route(p.sd, q, k, nodes, w.norms, w.hexp, false, w.kept, nullptr, nullptr, s);
   }
   if (e != hipSuccess) return hip_status(e, "route");
   {

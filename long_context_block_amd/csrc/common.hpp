@@ -96,6 +96,23 @@ __device__ __forceinline__ void mma(f32x4& acc, const Frag<uint16_t>& a, const F
                                                 acc, 0, 0, 0);
 }
 
+// fp16 operands held in Frag<uint16_t> bit patterns (routing planes and scaled queries).
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ void mma_f16(f32x4& acc, const Frag<uint16_t>& a, const Frag<uint16_t>& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a.u), __builtin_bit_cast(f16x8_t, b.u),
+                                               acc, 0, 0, 0);
+}
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float x) { return __builtin_bit_cast(uint16_t, (_Float16)x); }
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t x) { return (float)__builtin_bit_cast(_Float16, x); }
+
+// Exponent e with max * 2^e in [2^14, 2^15) for max > 0 (0 for max == 0): scaled values neither
+// overflow fp16 nor, for the ones that matter, fall below its normal range.
+__device__ __forceinline__ int f16_range_exp(float max_abs) {
+  int ex;
+  frexpf(max_abs, &ex);  // max_abs = f 2^ex, f in [0.5, 1)
+  return max_abs > 0.f ? 15 - ex : 0;
+}
+
 __device__ __forceinline__ void mma(f32x4& acc, const Frag<float>& a, const Frag<float>& b) {
   acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.a.x, b.a.x, acc, 0, 0, 0);
   acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.a.y, b.a.y, acc, 0, 0, 0);

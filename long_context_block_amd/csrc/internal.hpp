@@ -38,9 +38,12 @@ hipError_t launch_split_hilo(const float* mean, long long rows, int D, uint16_t*
 
 // Selection. `nodes` is the bf16 hi/lo pyramid (bf16 inputs) or the fp32 means (fp32 inputs).
 hipError_t launch_route(const SelDims& sd, const void* q, const void* k, const void* nodes, const float* norms,
-                        bool fused, int* kept, int* sel, float* sel_lse, hipStream_t st);
-// Per-row bound b >= |q . lo| / |q| (plus accumulation slack) for the bf16 hi/lo planes of each row.
-hipError_t launch_row_norms(const float* mean, long long rows, int D, float* norms, hipStream_t st);
+                        const int* hexp, bool fused, int* kept, int* sel, float* sel_lse, hipStream_t st);
+// Routing planes of a bf16 pyramid: per KV head an exponent hexp (max |mean| 2^hexp in [2^14, 2^15)),
+// per row the fp16 hi/lo planes of 2^hexp mean and the hi-plane score bound (unscaled units).
+// part_max: 64 floats of scratch per KV head.
+hipError_t launch_route_planes(const float* mean, long long heads, long long rows_per_head, int D, float* part_max,
+                               int* hexp, uint16_t* hilo, float* bound, hipStream_t st);
 
 // Bucket (unit, slot) pairs by node: node lists [U, K] (-1 = none) -> pairs sorted by
 // (b*Hkv + r, node), packed as (unit << 5) | slot. counts/offsets have n_buckets (+1) entries.

@@ -171,29 +171,63 @@ __global__ __launch_bounds__(256) void split_hilo_kernel(const float* __restrict
   }
 }
 
-// Per-row bound for the bf16 hi-plane score (one wave per row): b = 1.05 |lo| + 2^-16 |mean|, where
-// lo = rne(mean - rne(mean)) is the stored lo plane. For any q, |q . (hi + lo) - q . hi| = |q . lo|
-// <= |q| |lo| (Cauchy-Schwarz); the 2^-16 |mean| term covers the fp32 accumulation of 128-term dot
-// products (each order of summation errs by under 2^-17 |q| |mean|) and the 1.05 the rounding of the
-// norms themselves.
-__global__ __launch_bounds__(256) void row_norms_kernel(const float* __restrict__ mean, long long rows, int D,
-                                                       float* __restrict__ norms) {
+// Routing planes. Per KV head an exponent e (max |mean| 2^e in [2^14, 2^15), from 64 partial maxima);
+// per row the fp16
+// planes hi = rne(2^e mean), lo = rne(2^e mean - hi) (row r at r*2D: hi[D] then lo[D]), and the
+// hi-plane score bound b = 2^-e (1.05 |lo| + 2^-16 |2^e mean|): for any q, |q . (hi + lo) - q . hi| =
+// |q . lo| <= |q| |lo| (Cauchy-Schwarz); the 2^-16 term covers the fp32 accumulation of the dot
+// products (each order of summation errs by under 2^-17 |q| |2^e mean|) and the 1.05 the rounding of
+// the norms. 2^-e returns b to the units of the unscaled means.
+// Partial maxima of |mean|: kMaxParts work-groups per KV head, each over a contiguous slice.
+constexpr int kMaxParts = 64;
+__global__ __launch_bounds__(256) void head_max_kernel(const float* __restrict__ mean, long long rows_per_head, int D,
+                                                      float* __restrict__ part_max) {
+  __shared__ float s_m[4];
+  const int bh = blockIdx.x / kMaxParts, part = blockIdx.x % kMaxParts;
+  const long long n = rows_per_head * D;
+  const long long lo = n * part / kMaxParts, hi = n * (part + 1) / kMaxParts;
+  const float* m = mean + (long long)bh * n;
+  float mx = 0.f;
+  for (long long x = lo + threadIdx.x; x < hi; x += 256) mx = fmaxf(mx, fabsf(m[x]));
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  if ((threadIdx.x & 63) == 0) s_m[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  if (threadIdx.x == 0) part_max[blockIdx.x] = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+}
+
+// One wave per row.
+__global__ __launch_bounds__(256) void split_f16_kernel(const float* __restrict__ mean, long long rows,
+                                                       long long rows_per_head, int D,
+                                                       const float* __restrict__ part_max, int* __restrict__ hexp,
+                                                       uint16_t* __restrict__ hilo, float* __restrict__ bound) {
   const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
   const int lane = threadIdx.x & 63;
-  float sm = 0.f, sl = 0.f;
+  const long long bh = row / rows_per_head;
+  static_assert(kMaxParts == 64, "one partial per lane");
+  float mx = part_max[bh * kMaxParts + lane];
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  const int e = f16_range_exp(mx);
+  if (lane == 0 && row == bh * rows_per_head) hexp[bh] = e;
+  float sv = 0.f, sl = 0.f;
   for (int c = lane; c < D; c += 64) {
-    const float x = mean[row * D + c];
-    const float lo = bf16_to_f32(f32_to_bf16(x - bf16_to_f32(f32_to_bf16(x))));
-    sm += x * x;
-    sl += lo * lo;
+    const float v = ldexpf(mean[row * D + c], e);
+    const uint16_t hb = f32_to_f16_bits(v);
+    const uint16_t lb = f32_to_f16_bits(v - f16_bits_to_f32(hb));
+    hilo[row * 2 * D + c] = hb;
+    hilo[row * 2 * D + D + c] = lb;
+    const float l = f16_bits_to_f32(lb);
+    sv += v * v;
+    sl += l * l;
   }
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    sm += __shfl_xor(sm, o);
+    sv += __shfl_xor(sv, o);
     sl += __shfl_xor(sl, o);
   }
-  if (lane == 0) norms[row] = 1.05f * sqrtf(sl) + 1.52587890625e-05f * sqrtf(sm);
+  if (lane == 0) bound[row] = ldexpf(1.05f * sqrtf(sl) + 1.52587890625e-05f * sqrtf(sv), -e);
 }
 
 // ------------------------------------------------------------------------------------------ host
@@ -224,8 +258,13 @@ hipError_t launch_pool(const void* k, bool bf16, const PyrDims& pd, LensArg lens
   return launch_pool_t<float, 64>((const float*)k, pd, lens, max_level, mean, sum, st);
 }
 
-hipError_t launch_row_norms(const float* mean, long long rows, int D, float* norms, hipStream_t st) {
-  hipLaunchKernelGGL(row_norms_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, mean, rows, D, norms);
+hipError_t launch_route_planes(const float* mean, long long heads, long long rows_per_head, int D, float* part_max,
+                               int* hexp, uint16_t* hilo, float* bound, hipStream_t st) {
+  hipLaunchKernelGGL(head_max_kernel, dim3((unsigned)(heads * kMaxParts)), dim3(256), 0, st, mean, rows_per_head, D,
+                     part_max);
+  const long long rows = heads * rows_per_head;
+  hipLaunchKernelGGL(split_f16_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, mean, rows, rows_per_head,
+                     D, part_max, hexp, hilo, bound);
   return hipGetLastError();
 }
 

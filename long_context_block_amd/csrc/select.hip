@@ -34,7 +34,8 @@ struct RouteParams {
   const T* q;
   const T* k;
   const void* nodes;
-  const float* norms;  // hi-plane score bound per pyramid row (bf16 path)
+  const float* norms;  // hi-plane score bound per pyramid row (bf16 inputs)
+  const int* hexp;     // per KV head: the routing planes hold 2^hexp mean (bf16 inputs)
   int B, Hq, Hkv, G, N, K, upw;
   float scale;
   Levels lv;
@@ -115,8 +116,12 @@ __global__ __launch_bounds__(256, FUSED ? 2 : 4) void route_kernel(RouteParams<T
       const float sq_all = colgroup_sum(sq);  // every lane takes part in the exchange
       const float qn = row_sum16(hv ? sqrtf(sq_all) : 0.f);
       const float* norms = p.norms + bh * p.lv.nodes;
+      Frag<uint16_t> qh[D / 32];
+      const int te = route_q_f16<D>(qf, qh);
+      const float col_scale = ldexpf(p.scale, -(te + p.hexp[bh]));
       nk = walk_to_level1<T, D, KM>(p.lv, kLog2C, p.K, (int)i, &kept, [&](int off, int cn, int n_cand, int e_child) {
-        return select_level_refine<D, KM>(rows, norms, off, qf, qn, cn, n_cand, e_child, p.G, p.scale, p.K, s_sc[wave],
+        return select_level_refine<D, KM>(rows, norms, off, qh, qn, cn, n_cand, e_child, p.G, p.scale, col_scale, p.K,
+                                          s_sc[wave],
                                           s_key[wave]);
       });
     } else {
@@ -182,6 +187,7 @@ __global__ __launch_bounds__(1024) void route_lds_kernel(RouteParams<uint16_t> p
   stage_hi_rows<D>(rows.base, lds_first, (int)(p.lv.nodes - lds_first), s_hi);
   __syncthreads();
   const float* norms = p.norms + (long long)bh * p.lv.nodes;
+  const int hexp = p.hexp[bh];
   const int b = bh / p.Hkv, r = bh % p.Hkv;
   const bool hv = r16 < p.G;
   const int groups = (p.N + kRouteUnits - 1) / kRouteUnits;
@@ -210,11 +216,14 @@ __global__ __launch_bounds__(1024) void route_lds_kernel(RouteParams<uint16_t> p
         }
       const float sq_all = colgroup_sum(sq);  // every lane takes part in the exchange
       const float qn = row_sum16(hv ? sqrtf(sq_all) : 0.f);
+      Frag<uint16_t> qh[D / 32];
+      const int te = route_q_f16<D>(qf, qh);
+      const float col_scale = ldexpf(p.scale, -(te + hexp));
       int kept;
       const int nk =
           walk_to_level1<uint16_t, D, KM>(p.lv, kLog2C, p.K, i, &kept, [&](int off, int cn, int n_cand, int e_child) {
-            return select_level_refine<D, KM>(rows, norms, off, qf, qn, cn, n_cand, e_child, p.G, p.scale, p.K,
-                                              s_sc[wave], s_key[wave]);
+            return select_level_refine<D, KM>(rows, norms, off, qh, qn, cn, n_cand, e_child, p.G, p.scale, col_scale,
+                                              p.K, s_sc[wave], s_key[wave]);
           });
       if (lane < p.K) p.kept[u * p.K + lane] = lane < nk ? kept : -1;
     }
@@ -563,8 +572,9 @@ hipError_t launch_regroup(const int* nodes, long long U, int K, int N, int nb, i
 // ------------------------------------------------------------------------------------------ launchers
 template <typename T, int D, int C, bool FUSED>
 static hipError_t route_t(const SelDims& sd, const void* q, const void* k, const void* nodes, const float* norms,
-                          int* kept, int* sel, float* sel_lse, hipStream_t st) {
+                          const int* hexp, int* kept, int* sel, float* sel_lse, hipStream_t st) {
   RouteParams<T> p;
+  p.hexp = hexp;
   p.q = (const T*)q;
   p.k = (const T*)k;
   p.nodes = nodes;
@@ -611,22 +621,22 @@ static hipError_t route_t(const SelDims& sd, const void* q, const void* k, const
 
 template <typename T, bool FUSED>
 static hipError_t route_dc(const SelDims& sd, const void* q, const void* k, const void* nodes, const float* norms,
-                           int* kept, int* sel, float* sel_lse, hipStream_t st) {
+                           const int* hexp, int* kept, int* sel, float* sel_lse, hipStream_t st) {
   if (sd.D == 128) {
-    if (sd.C == 64) return route_t<T, 128, 64, FUSED>(sd, q, k, nodes, norms, kept, sel, sel_lse, st);
-    return route_t<T, 128, 32, FUSED>(sd, q, k, nodes, norms, kept, sel, sel_lse, st);
+    if (sd.C == 64) return route_t<T, 128, 64, FUSED>(sd, q, k, nodes, norms, hexp, kept, sel, sel_lse, st);
+    return route_t<T, 128, 32, FUSED>(sd, q, k, nodes, norms, hexp, kept, sel, sel_lse, st);
   }
-  if (sd.C == 64) return route_t<T, 64, 64, FUSED>(sd, q, k, nodes, norms, kept, sel, sel_lse, st);
-  return route_t<T, 64, 32, FUSED>(sd, q, k, nodes, norms, kept, sel, sel_lse, st);
+  if (sd.C == 64) return route_t<T, 64, 64, FUSED>(sd, q, k, nodes, norms, hexp, kept, sel, sel_lse, st);
+  return route_t<T, 64, 32, FUSED>(sd, q, k, nodes, norms, hexp, kept, sel, sel_lse, st);
 }
 
 hipError_t launch_route(const SelDims& sd, const void* q, const void* k, const void* nodes, const float* norms,
-                        bool fused, int* kept, int* sel, float* sel_lse, hipStream_t st) {
+                        const int* hexp, bool fused, int* kept, int* sel, float* sel_lse, hipStream_t st) {
   if (sd.bf16)
-    return fused ? route_dc<uint16_t, true>(sd, q, k, nodes, norms, kept, sel, sel_lse, st)
-                 : route_dc<uint16_t, false>(sd, q, k, nodes, norms, kept, sel, sel_lse, st);
-  return fused ? route_dc<float, true>(sd, q, k, nodes, norms, kept, sel, sel_lse, st)
-               : route_dc<float, false>(sd, q, k, nodes, norms, kept, sel, sel_lse, st);
+    return fused ? route_dc<uint16_t, true>(sd, q, k, nodes, norms, hexp, kept, sel, sel_lse, st)
+                 : route_dc<uint16_t, false>(sd, q, k, nodes, norms, hexp, kept, sel, sel_lse, st);
+  return fused ? route_dc<float, true>(sd, q, k, nodes, norms, hexp, kept, sel, sel_lse, st)
+               : route_dc<float, false>(sd, q, k, nodes, norms, hexp, kept, sel, sel_lse, st);
 }
 
 template <typename T, int D, int C>

@@ -31,7 +31,7 @@ struct NodeRows<uint16_t, D> {
       mma(acc, f.lo[s], qf[s]);
     }
   }
-  // hi or lo plane of pyramid row `node` alone (the two passes of the bf16 walk)
+  // hi or lo plane of row `node` alone (the two passes of the routing walk over the fp16 planes)
   __device__ __forceinline__ void load_hi(Frag<uint16_t> (&hi)[D / 32], int node, int grp) const {
     const uint16_t* p = base + (unsigned)node * (2 * D) + 8 * grp;
 #pragma unroll
@@ -49,7 +49,31 @@ struct NodeRows<uint16_t, D> {
   }
 };
 
-// bf16 walk with the hi plane of the upper pyramid rows (node >= first) resident in LDS: local row
+// The column's query (bf16 fragments qf) in fp16 scaled by 2^te, max |q| 2^te in [2^14, 2^15) over the
+// column (zero columns: te = 0): exact, since a bf16 value keeps its 8 significant bits in fp16 in that
+// range (values under 2^-14 after scaling, 2^-28 of the largest, may round: the routing bound's
+// accumulation slack covers them). Returns te.
+template <int D>
+__device__ __forceinline__ int route_q_f16(const Frag<uint16_t> (&qf)[D / 32], Frag<uint16_t> (&qh)[D / 32]) {
+  float mx = 0.f;
+#pragma unroll
+  for (int s = 0; s < D / 32; ++s)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(qf[s].get(e)));
+  const int te = f16_range_exp(colgroup_max(mx));
+#pragma unroll
+  for (int s = 0; s < D / 32; ++s) {
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = (uint32_t)f32_to_f16_bits(ldexpf(qf[s].get(2 * e), te)) |
+             ((uint32_t)f32_to_f16_bits(ldexpf(qf[s].get(2 * e + 1), te)) << 16);
+    qh[s].u = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  return te;
+}
+
+// Routing walk with the hi plane of the upper pyramid rows (node >= first) resident in LDS: local row
 // r = node - first holds D hi values, 16-byte chunk c stored at chunk c ^ (r mod D/8), so the 4
 // consecutive rows of one kept node (its grandchildren) fall on distinct chunk columns. Lower rows and
 // every lo plane are read from global memory.
@@ -163,19 +187,23 @@ __device__ void score_candidates(const Rows& rows, int level_off, const Frag<T> 
   __threadfence_block();
 }
 
-// One scored level on the bf16 path, in two passes over the <= 4K child rows. Pass 1 uses the hi plane
-// only; a candidate's score then lies within E_c = scale * sum_h |q_h| * max over its children of the
-// row bound b (b >= |q . lo| / |q| plus the accumulation slack, per row) of its hi+lo score (LSE is
-// 1-Lipschitz in the max norm, per head). With the Top-K of the hi scores
-// as the "in" group, a candidate is decided by pass 1 when its interval cannot cross the boundary (an
-// "in" candidate whose lower end is above every "out" upper end, or an "out" candidate whose upper end
-// is below every "in" lower end); the rest get the lo plane added (pass 2) and compete by their hi+lo
-// scores for the remaining places. The kept set is the one the hi+lo scores of every candidate give,
-// while only the lo rows of undecided candidates are read. Returns this lane's keep flag.
+// One scored level for bf16 inputs, in two passes over the <= 4K child rows of the fp16 routing planes
+// (hi = rne(2^hexp mean), lo = rne(2^hexp mean - hi)). Pass 1 uses the hi plane only; a candidate's
+// score then lies within E_c = scale * sum_h |q_h| * max over its children of the row bound b
+// (b >= |q . lo| / |q| plus the accumulation slack, in unscaled units) of its hi+lo score (LSE is
+// 1-Lipschitz in the max norm, per head). With the Top-K of the hi scores as the "in" group, a
+// candidate is decided by pass 1 when its interval cannot cross the boundary (an "in" candidate whose
+// lower end is above every "out" upper end, or an "out" candidate whose upper end is below every "in"
+// lower end); the rest get the lo plane added (pass 2) and compete by their hi+lo scores for the
+// remaining places. The kept set is the one the hi+lo scores of every candidate give, while only the
+// lo rows of undecided candidates are read. Returns this lane's keep flag.
+// qf: the column's query in fp16 scaled by 2^te (route_q_f16); col_scale = scale 2^-(te + hexp) returns
+// the dot products with the scaled planes to scale * q . mean.
 template <int D, int KM, class Rows>
 __device__ bool select_level_refine(const Rows& rows, const float* norms, int level_off,
                                     const Frag<uint16_t> (&qf)[D / 32], float qnorm_sum, int cn, int n_cand,
-                                    int e_child, int G, float scale, int K, float* s_sc, uint32_t* keys) {
+                                    int e_child, int G, float scale, float col_scale, int K, float* s_sc,
+                                    uint32_t* keys) {
   const int lane = lane_id(), r16 = lane & 15, grp = lane >> 4;
   const int MT = (2 * n_cand + 15) >> 4;
   const bool last_two = 2 * readlane(cn, n_cand - 1) + 1 < e_child;
@@ -199,14 +227,14 @@ __device__ bool select_level_refine(const Rows& rows, const float* norms, int le
       rows.load_hi(hi, level_off + child[m], grp);
       acc[m] = zero4();
 #pragma unroll
-      for (int s = 0; s < D / 32; ++s) mma(acc[m], hi[s], qf[s]);
+      for (int s = 0; s < D / 32; ++s) mma_f16(acc[m], hi[s], qf[s]);
     }
   }
   auto cand_scores = [&](int m, unsigned long long only) {
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
       const int c = 8 * m + 2 * grp + a;
-      const float x0 = scale * acc[m][2 * a], x1 = scale * acc[m][2 * a + 1];
+      const float x0 = col_scale * acc[m][2 * a], x1 = col_scale * acc[m][2 * a + 1];
       float l = c < n_full ? lse2(x0, x1) : x0;
       l = row_sum16(r16 < G ? l : 0.f);
       if (r16 == 0 && ((only >> (c & 63)) & 1ull)) s_sc[c] = l;
@@ -240,7 +268,7 @@ __device__ bool select_level_refine(const Rows& rows, const float* norms, int le
       Frag<uint16_t> lo[D / 32];
       rows.load_lo(lo, level_off + child[m], grp, need);
 #pragma unroll
-      for (int s = 0; s < D / 32; ++s) mma(acc[m], lo[s], qf[s]);
+      for (int s = 0; s < D / 32; ++s) mma_f16(acc[m], lo[s], qf[s]);
       cand_scores(m, rmask);
     }
   }
