@@ -70,6 +70,21 @@ def work_counts(pf, sel):
                 attended_keys=A, bsa_flops=bsa_flops, pyramid_read_bytes=pyr_bytes)
 
 
+def measured_traffic(workload):
+    """HBM bytes per launch and stage from the committed counter summary for this workload (FETCH_SIZE and
+    WRITE_SIZE, each scaled by a plain copy's reading), or None when there is none or the kernel sources
+    have changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    from long_context_block_amd.profile_summary import source_digest
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_digest") != source_digest():
+        return None
+    return {st: e["bytes"] for st, e in t["stages"].items()}
+
+
 def cpu_baseline(pf, seconds_target=15.0, seed=0):
     """The float64 oracle (as it stands) on a bounded random sample of units, one thread."""
     import oracle as O
@@ -264,6 +279,7 @@ def main():
     }
     dom = max(kern, key=lambda n: kern[n][2])
     bound, amount, ms = kern[dom]
+    traffic = measured_traffic(args.workload)
     if bound == "hbm":
         achieved, peak, unit = amount / (ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
     else:
@@ -272,12 +288,16 @@ def main():
     for n, (bd, amt, kms) in kern.items():
         if kms <= 0:
             continue
+        if traffic and n in traffic:
+            per_kernel.setdefault(n, {})["hbm_bytes_measured"] = round(traffic[n])
+            per_kernel[n]["hbm_GB/s_measured"] = round(traffic[n] / (kms * 1e-3) / 1e9, 1)
         if bd == "hbm":
-            per_kernel[n] = {"ms": round(kms, 4), "GB/s": round(amt / (kms * 1e-3) / 1e9, 1),
-                             "frac_hbm": round(amt / (kms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+            per_kernel.setdefault(n, {}).update({"ms": round(kms, 4), "GB/s": round(amt / (kms * 1e-3) / 1e9, 1),
+                                                 "frac_hbm": round(amt / (kms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)})
         else:
             tf = amt / (kms * 1e-3) / 1e12
-            per_kernel[n] = {"ms": round(kms, 4), "TFLOP/s": round(tf, 2), "frac_mfma": round(tf / peak_mma, 4)}
+            per_kernel.setdefault(n, {}).update({"ms": round(kms, 4), "TFLOP/s": round(tf, 2),
+                                                 "frac_mfma": round(tf / peak_mma, 4)})
 
     out = {
         "metric": METRIC,
@@ -303,7 +323,8 @@ def main():
         "kernels": per_kernel,
         "work": w,
         "roofline": {"kernel": dom, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-                     "frac": round(achieved / peak, 4), "traffic": None},
+                     "frac": round(achieved / peak, 4),
+                     "traffic": round(traffic[dom]) if traffic and dom in traffic else None},
     }
     if not args.no_decode:
         log("[bench] decode: generating the 8 x 128K cache and timing 256 steps")

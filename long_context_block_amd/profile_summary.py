@@ -1,0 +1,187 @@
+"""Summaries of rocprofv3 CSV output for the library's kernels.
+
+Reads the files rocprofv3 writes with ``--output-format csv`` (``*_kernel_stats.csv`` from a
+``--kernel-trace --stats`` run, ``*_counter_collection.csv`` from ``--pmc`` runs) and writes
+
+* a Markdown table of per-kernel launch statistics (``--stats``), and
+* HBM traffic per launch from a FETCH_SIZE run and a WRITE_SIZE run, each scaled by what the same
+  counter reads for a plain device copy of known size (``bench.py --copy-calibration BYTES``), as
+  Markdown plus a JSON file that ``bench.py`` reads. The JSON records a digest of the kernel sources;
+  ``bench.py`` ignores it once the sources have changed.
+
+Usage (from the repository root, on the host, after the GPU runs)::
+
+    python -m long_context_block_amd.profile_summary stats DIR --title T --command C --out profiles/x.md
+    python -m long_context_block_amd.profile_summary traffic --fetch DIR --write DIR --copy-fetch DIR \\
+        --copy-write DIR --copy-bytes N --title T --command C --out-md profiles/y.md --out-json profiles/y.json
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import re
+from collections import defaultdict
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# bench.py stage name -> kernel name fragments (the stage's launches)
+STAGE_KERNELS = {
+    "pyramid": ["pool_subtree_kernel", "pool_upper_kernel"],
+    "route_planes": ["head_max_kernel", "split_f16_kernel"],
+    "route": ["route_lds_kernel", "route_kernel"],
+    "regroup": ["hist_kernel", "scan_kernel", "scatter_kernel", "fill_zero_kernel"],
+    "leaf_lse": ["leaf_lse_wg_kernel", "leaf_lse_kernel"],
+    "finalize": ["finalize_kernel"],
+    "attn_leaf": ["attn_leaf_wg_kernel", "attn_leaf_kernel"],
+    "attn_merge": ["attn_merge_kernel"],
+    "bsa_select": ["bsa_kernel"],
+    "decode_step": ["decode_kernel"],
+}
+
+
+def source_digest(root: str = ROOT) -> str:
+    """SHA-256 over the kernel sources and the ABI header (sorted paths and contents)."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(root, "long_context_block_amd", "csrc", "*")) +
+                   glob.glob(os.path.join(root, "include", "*.h")))
+    for f in files:
+        h.update(os.path.relpath(f, root).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def short_name(name: str) -> str:
+    name = name.strip('"')
+    m = re.search(r"pisa::(\w+)(<[^(]*>)?", name)
+    if m:
+        return m.group(1) + (m.group(2) or "")
+    return name.split("(")[0].replace("void ", "")[:60]
+
+
+def stage_of(name: str) -> str | None:
+    for stage, frags in STAGE_KERNELS.items():
+        for f in frags:
+            if re.search(r"\b" + f + r"\b", name):
+                return stage
+    return None
+
+
+def _one(pattern: str) -> str:
+    files = glob.glob(pattern, recursive=True)
+    if not files:
+        raise SystemExit(f"no file matches {pattern}")
+    return sorted(files)[0]
+
+
+def kernel_stats(d: str) -> list[dict]:
+    rows = []
+    with open(_one(os.path.join(d, "**", "*kernel_stats.csv"))) as f:
+        for r in csv.DictReader(f):
+            rows.append({"name": short_name(r["Name"]), "calls": int(r["Calls"]),
+                         "avg_us": float(r["AverageNs"]) / 1e3, "total_us": float(r["TotalDurationNs"]) / 1e3,
+                         "pct": float(r["Percentage"])})
+    rows.sort(key=lambda x: -x["total_us"])
+    return rows
+
+
+def counter_per_launch(d: str, counter: str) -> dict[str, float]:
+    """Average over launches of the counter summed over its instances, per kernel short name."""
+    per = defaultdict(lambda: defaultdict(float))
+    with open(_one(os.path.join(d, "**", "*counter_collection.csv"))) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            per[short_name(r["Kernel_Name"])][r["Dispatch_Id"]] += float(r["Counter_Value"])
+    return {k: sum(v.values()) / len(v) for k, v in per.items()}
+
+
+def cmd_stats(a):
+    rows = kernel_stats(a.dir)
+    if a.filter:
+        rows = [r for r in rows if re.search(a.filter, r["name"])]
+    lines = [f"# Kernel statistics: {a.title}", "", "Command (run from the repository root on one MI355X):", "",
+             "```", a.command, "```", ""]
+    if a.note:
+        lines += [a.note, ""]
+    lines += ["| Kernel | Calls | Average (us) | Total (us) | Share % |", "|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| `{r['name']}` | {r['calls']} | {r['avg_us']:.1f} | {r['total_us']:.1f} | {r['pct']:.2f} |")
+    with open(a.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(f"wrote {a.out}")
+
+
+def cmd_traffic(a):
+    fetch = counter_per_launch(a.fetch, "FETCH_SIZE")
+    write = counter_per_launch(a.write, "WRITE_SIZE")
+    cf = counter_per_launch(a.copy_fetch, "FETCH_SIZE")
+    cw = counter_per_launch(a.copy_write, "WRITE_SIZE")
+    copy = [k for k in cf if "copyBuffer" in k or "copy" in k.lower()]
+    if not copy:
+        raise SystemExit("no copy kernel in the calibration runs")
+    ck = copy[0]
+    kib = a.copy_bytes / 1024.0
+    f_fac, w_fac = kib / cf[ck], kib / cw[ck]
+    kernels = {}
+    for k in sorted(set(fetch) | set(write)):
+        st = stage_of(k)
+        if st is None:
+            continue
+        fb = fetch.get(k, 0.0) * f_fac * 1024.0
+        wb = write.get(k, 0.0) * w_fac * 1024.0
+        e = kernels.setdefault(st, {"kernels": [], "fetch_bytes": 0.0, "write_bytes": 0.0})
+        e["kernels"].append(k)
+        e["fetch_bytes"] += fb
+        e["write_bytes"] += wb
+    for e in kernels.values():
+        e["bytes"] = e["fetch_bytes"] + e["write_bytes"]
+    out = {"source_digest": source_digest(), "copy_kernel": ck, "copy_bytes": a.copy_bytes,
+           "fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4), "workload": a.workload,
+           "command": a.command, "stages": kernels}
+    with open(a.out_json, "w") as f:
+        json.dump(out, f, indent=1)
+    lines = [f"# HBM traffic per launch: {a.title}", "", "Commands (run from the repository root on one MI355X):",
+             "", "```", a.command, "```", "",
+             f"Calibration: a plain device copy of {a.copy_bytes} bytes (`{ck}`) reads FETCH_SIZE = "
+             f"{cf[ck]:.0f} KiB and WRITE_SIZE = {cw[ck]:.0f} KiB per launch, so FETCH_SIZE is scaled by "
+             f"{f_fac:.3f} and WRITE_SIZE by {w_fac:.3f}. Source digest of the measured build: "
+             f"`{out['source_digest']}`.", "",
+             "| Stage | Kernels | Read (GB) | Written (GB) | Total (GB) |", "|---|---|---|---|---|"]
+    for st, e in sorted(kernels.items(), key=lambda kv: -kv[1]["bytes"]):
+        lines.append(f"| {st} | {', '.join('`' + k + '`' for k in e['kernels'])} | {e['fetch_bytes'] / 1e9:.3f} | "
+                     f"{e['write_bytes'] / 1e9:.3f} | {e['bytes'] / 1e9:.3f} |")
+    with open(a.out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(f"wrote {a.out_md} and {a.out_json}")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("dir")
+    s.add_argument("--title", required=True)
+    s.add_argument("--command", required=True)
+    s.add_argument("--note", default="")
+    s.add_argument("--filter", default="", help="regex: keep only the kernels whose name matches")
+    s.add_argument("--out", required=True)
+    t = sub.add_parser("traffic")
+    for k in ("fetch", "write", "copy_fetch", "copy_write"):
+        t.add_argument("--" + k.replace("_", "-"), dest=k, required=True)
+    t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--workload", default="prefill_64k")
+    t.add_argument("--title", required=True)
+    t.add_argument("--command", required=True)
+    t.add_argument("--out-md", required=True)
+    t.add_argument("--out-json", required=True)
+    a = ap.parse_args()
+    {"stats": cmd_stats, "traffic": cmd_traffic}[a.cmd](a)
+
+
+if __name__ == "__main__":
+    main()
