@@ -384,7 +384,10 @@ pisa_status pisa_select(const pisa_shape* shape, const void* q, const void* k, c
   }
   {
     Stage sc(s, "route");
-    e = pisa::launch_route(p.sd, q, k, nodes, w.norms, w.hexp, false, w.kept, nullptr, nullptr, s);
+    if (pisa::route_group_supported(p.sd))
+      e = pisa::launch_route_group(p.sd, q, nodes, w.norms, w.hexp, w.kept, s);
+    else
+      e = pisa::launch_route(p.sd, q, k, nodes, w.norms, w.hexp, false, w.kept, nullptr, nullptr, s);
   }
   if (e != hipSuccess) return hip_status(e, "route");
   {

@@ -39,6 +39,11 @@ hipError_t launch_split_hilo(const float* mean, long long rows, int D, uint16_t*
 // Selection. `nodes` is the bf16 hi/lo pyramid (bf16 inputs) or the fp32 means (fp32 inputs).
 hipError_t launch_route(const SelDims& sd, const void* q, const void* k, const void* nodes, const float* norms,
                         const int* hexp, bool fused, int* kept, int* sel, float* sel_lse, hipStream_t st);
+// Routing with 16 / G units per wave (bf16 inputs, G in {4, 8, 16}, K <= 32); same kept sets as
+// launch_route. Writes the kept level-1 nodes [U, K].
+bool route_group_supported(const SelDims& sd);
+hipError_t launch_route_group(const SelDims& sd, const void* q, const void* hilo, const float* norms, const int* hexp,
+                              int* kept, hipStream_t st);
 // Routing planes of a bf16 pyramid: per KV head an exponent hexp (max |mean| 2^hexp in [2^14, 2^15)),
 // per row the fp16 hi/lo planes of 2^hexp mean and the hi-plane score bound (unscaled units).
 // part_max: 64 floats of scratch per KV head.

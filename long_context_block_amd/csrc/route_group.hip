@@ -1,0 +1,413 @@
+// Pyramid Top-K routing for several query units per wave ("Block Sparse Attention with Log-Linear
+// Complexity" digest, 方法关键点: pyramid bullet -- coarse-to-fine walk keeping the Top-K of at most
+// g*K candidates per level and expanding only their children; scoring bullet -- an intermediate node
+// scores the LSE over its children's mean keys, summed over the GQA heads of the KV head).
+//
+// One work-group of 12 waves per CU serves one KV head: the fp16 hi plane (and row bounds) of the upper
+// pyramid levels is staged into LDS once, then each wave walks UG = 16 / G consecutive query positions
+// at once. Matrix column col = x G + h is head h of unit x, so all 16 columns carry data. At a scored
+// level, row 16 m + r of unit x's M-tile m is child (r & 1) of candidate 8 m + (r >> 1); all lanes load
+// and multiply every unit's rows, and the lanes of unit x keep the accumulators of their own M-tiles. A
+// lane (col, g) then holds both children of candidates 8 m + 2 g + {0, 1} for its head, so the per-head
+// LSE is lane-local and a butterfly over the unit's G columns (strides G/2 .. 1) sums the heads.
+// Candidate 8 m + 2 g + a is owned by the lane with h = m mod G, which ranks it against its unit's keys
+// in LDS and, if kept, places it in the unit's next kept list by a prefix count over an LDS bit mask.
+//
+// The arithmetic per candidate is the one-unit-per-wave walk's (same MFMA rows, k order, LSE, head-sum
+// order, bounds, keys and tie-break), so both give the same kept sets bit for bit.
+#include "common.hpp"
+#include "internal.hpp"
+#include "walk_tiles.hpp"
+
+namespace pisa {
+
+constexpr int kGroupWaves = 12;
+constexpr int kGroupLdsBytes = 128 * 1024;
+
+struct GroupRouteParams {
+  const uint16_t* q;
+  const uint16_t* hilo;  // [B*Hkv, nodes, 2D] fp16: hi plane then lo plane per row
+  const float* norms;    // per-row hi-plane bound
+  const int* hexp;       // per KV head: planes hold 2^hexp mean
+  int B, Hq, Hkv, N, K;
+  float scale;
+  Levels lv;
+  int* kept;  // [U, K]
+};
+
+template <int D, int C, int G, int KM>
+__global__ __launch_bounds__(kGroupWaves * 64) void route_group_kernel(GroupRouteParams p, int lds_first,
+                                                                      int wg_per_head) {
+  constexpr int UG = 16 / G;             // units per wave
+  constexpr int LOG2C = C == 64 ? 6 : 5;
+  constexpr int NS = D / 32;             // k steps
+  constexpr int OWN = (KM + G - 1) / G;  // owned M-tile slots per lane (x2 candidates)
+  constexpr int NC = 8 * KM;             // candidate slots per unit (>= 2K)
+  __shared__ __align__(16) uint16_t s_hi[kGroupLdsBytes / 2];
+  __shared__ float s_bound[kGroupLdsBytes / 128];
+  __shared__ int s_kept[kGroupWaves][2][UG][NC / 2];
+  __shared__ __align__(16) uint32_t s_key[kGroupWaves][UG][NC];
+  __shared__ unsigned long long s_mask[kGroupWaves][UG];
+  const int lane = lane_id(), wave = threadIdx.x >> 6, col = lane & 15, g = lane >> 4;
+  const int xo = col / G, h = col % G;  // this lane's unit and head
+  const int BH = p.B * p.Hkv;
+  const int bh = blockIdx.x % BH, w = blockIdx.x / BH;
+  const int K = p.K;
+  LdsHiRows<D> rows;
+  rows.base = p.hilo + (long long)bh * p.lv.nodes * 2 * D;
+  const float* norms = p.norms + (long long)bh * p.lv.nodes;
+  rows.lds = s_hi;
+  rows.lds_bound = s_bound;
+  rows.first = lds_first;
+  stage_hi_rows<D>(rows.base, norms, lds_first, (int)(p.lv.nodes - lds_first), s_hi, s_bound);
+  __syncthreads();
+  const int hexp = p.hexp[bh];
+  const int b = bh / p.Hkv, r = bh % p.Hkv;
+  const int L = p.lv.n_levels - 1;
+  const int groups = (p.N + UG - 1) / UG;
+  for (int gi = w * kGroupWaves + wave; gi < groups; gi += wg_per_head * kGroupWaves) {
+    // ---- units (positions) of this wave; past N: repeats of position N - 1, not stored
+    int ix[UG];
+#pragma unroll
+    for (int x = 0; x < UG; ++x) ix[x] = gi * UG + x < p.N ? gi * UG + x : p.N - 1;
+    int my_i = ix[0];
+#pragma unroll
+    for (int x = 1; x < UG; ++x) my_i = xo == x ? ix[x] : my_i;
+    // ---- the column's query (bf16, then exactly scaled fp16) and sum_h |q_h| of its unit
+    Frag<uint16_t> qf[NS], qh[NS];
+    {
+      const uint16_t* qrow = p.q + ((((long long)b * p.Hq + (long long)r * G + h) * p.N) + my_i) * D + 8 * g;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) qf[s].load(qrow + 32 * s);
+    }
+    float qn;
+    {
+      float sq = 0.f;
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float v = qf[s].get(e);
+          sq += v * v;
+        }
+      qn = sqrtf(colgroup_sum(sq));
+#pragma unroll
+      for (int o = G / 2; o >= 1; o >>= 1) qn += __shfl_xor(qn, o);
+    }
+    const int te = route_q_f16<D>(qf, qh);
+    const float col_scale = ldexpf(p.scale, -(te + hexp));
+    // ---- top of the walk: below the highest level where some unit has more than K eligible nodes
+    int lw = 0;
+#pragma unroll
+    for (int x = 0; x < UG; ++x)
+      for (int l = L; l > lw; --l)
+        if ((ix[x] >> (LOG2C + l)) + 1 > K) {
+          lw = l;
+          break;
+        }
+    int nk[UG];
+    int cur = 0;
+#pragma unroll
+    for (int x = 0; x < UG; ++x) {
+      nk[x] = (ix[x] >> (LOG2C + lw + 1)) + 1;  // all eligible nodes of level lw + 1 (<= K when lw > 0)
+      if (lane < nk[x]) s_kept[wave][0][x][lane] = lane;
+    }
+    __threadfence_block();
+    for (int l = lw; l >= 1; --l) {
+      const int off = (int)p.lv.off[l - 1];
+      int n_cand[UG], n_full[UG];
+      bool any_scored = false;
+#pragma unroll
+      for (int x = 0; x < UG; ++x) {
+        const int e_l = (ix[x] >> (LOG2C + l)) + 1, ec = (ix[x] >> (LOG2C + l - 1)) + 1;
+        const int klast = s_kept[wave][cur][x][nk[x] - 1];
+        n_cand[x] = 2 * nk[x] - (2 * klast + 1 >= e_l ? 1 : 0);
+        const int cn_last = 2 * s_kept[wave][cur][x][(n_cand[x] - 1) >> 1] + ((n_cand[x] - 1) & 1);
+        n_full[x] = 2 * cn_last + 1 < ec ? n_cand[x] : n_cand[x] - 1;
+        any_scored |= n_cand[x] > K;
+      }
+      int my_nc = n_cand[0], my_nf = n_full[0], my_nk = nk[0];
+#pragma unroll
+      for (int x = 1; x < UG; ++x) {
+        my_nc = xo == x ? n_cand[x] : my_nc;
+        my_nf = xo == x ? n_full[x] : my_nf;
+        my_nk = xo == x ? nk[x] : my_nk;
+      }
+      const bool my_scored = my_nc > K;
+      // candidate c: node 2 kept[c >> 1] + (c & 1) at level l
+      auto cand_node = [&](int c) {
+        const int kj = c >> 1;
+        return 2 * s_kept[wave][cur][xo][kj < my_nk ? kj : 0] + (c & 1);
+      };
+      bool keep[OWN][2];
+      if (any_scored) {
+        // ---- pass 1 (hi) for every scored unit; lanes keep their own unit's accumulators
+        f32x4 acc_own[KM];
+#pragma unroll
+        for (int m = 0; m < KM; ++m) acc_own[m] = zero4();
+#pragma unroll
+        for (int x = 0; x < UG; ++x) {
+          if (n_cand[x] <= K) continue;
+          const int mt = (2 * n_cand[x] + 15) >> 4;
+#pragma unroll
+          for (int m = 0; m < KM; ++m) {
+            if (m >= mt) break;
+            const int kj = 4 * m + (col >> 2), c = kj * 2 + ((col >> 1) & 1);
+            const bool valid = c < n_cand[x] && ((col & 1) == 0 || c < n_full[x]);
+            const int kn = s_kept[wave][cur][x][kj < nk[x] ? kj : 0];
+            Frag<uint16_t> hi[NS];
+            rows.load_hi(hi, off + (valid ? 4 * kn + (col & 3) : 0), g);
+            f32x4 a = zero4();
+#pragma unroll
+            for (int s = 0; s < NS; ++s) mma_f16(a, hi[s], qh[s]);
+            if (xo == x) acc_own[m] = a;
+          }
+          __builtin_amdgcn_sched_barrier(0);  // one unit's rows in flight at a time (register budget)
+        }
+        // ---- per-head candidate scores, summed over the unit's heads (strides G/2 .. 1)
+        auto head_scores = [&](float (&sc)[KM][2]) {
+#pragma unroll
+          for (int m = 0; m < KM; ++m)
+#pragma unroll
+            for (int a = 0; a < 2; ++a) {
+              const int c = 8 * m + 2 * g + a;
+              const float x0 = col_scale * acc_own[m][2 * a], x1 = col_scale * acc_own[m][2 * a + 1];
+              float v = c < my_nf ? lse2(x0, x1) : x0;
+#pragma unroll
+              for (int o = G / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+              sc[m][a] = v;
+            }
+        };
+        float sc[KM][2];
+        head_scores(sc);
+        // ---- owned candidates: hi score, bound, hi Top-K
+        float own_s[OWN][2], own_e[OWN][2];
+        bool own_v[OWN][2], in[OWN][2];
+#pragma unroll
+        for (int j = 0; j < OWN; ++j)
+#pragma unroll
+          for (int a = 0; a < 2; ++a) {
+            const int m = h + j * G;
+            float s = 0.f;
+#pragma unroll
+            for (int mm = 0; mm < KM; ++mm) s = mm == m ? sc[mm][a] : s;
+            const int c = 8 * m + 2 * g + a;
+            own_v[j][a] = m < KM && c < my_nc;
+            own_s[j][a] = s;
+            float e = 0.f;
+            if (own_v[j][a] && my_scored) {
+              const int r0 = off + 2 * cand_node(c);
+              const float n0 = rows.bound(norms, r0), n1 = c < my_nf ? rows.bound(norms, r0 + 1) : 0.f;
+              e = p.scale * qn * fmaxf(n0, n1);
+            }
+            own_e[j][a] = e;
+            if (own_v[j][a]) s_key[wave][xo][c] = topk_key(s, c);
+          }
+        __threadfence_block();
+        auto rank_of = [&](uint32_t key) {
+          int rank = 0;
+          for (int c = 0; c < my_nc; c += 4) {
+            const uint4 v = *reinterpret_cast<const uint4*>(&s_key[wave][xo][c]);
+            rank += (v.x > key) + (c + 1 < my_nc && v.y > key) + (c + 2 < my_nc && v.z > key) +
+                    (c + 3 < my_nc && v.w > key);
+          }
+          return rank;
+        };
+        float u_out = kNegInf, l_in = -kNegInf;
+#pragma unroll
+        for (int j = 0; j < OWN; ++j)
+#pragma unroll
+          for (int a = 0; a < 2; ++a) {
+            const int c = 8 * (h + j * G) + 2 * g + a;
+            in[j][a] = own_v[j][a] && rank_of(topk_key(own_s[j][a], c)) < K;
+            if (own_v[j][a] && !in[j][a]) u_out = fmaxf(u_out, own_s[j][a] + own_e[j][a]);
+            if (in[j][a]) l_in = fminf(l_in, own_s[j][a] - own_e[j][a]);
+          }
+        // over the unit's lanes (its G columns in each of the 4 lane groups)
+#pragma unroll
+        for (int o = 1; o < G; o <<= 1) {
+          u_out = fmaxf(u_out, __shfl_xor(u_out, o));
+          l_in = fminf(l_in, __shfl_xor(l_in, o));
+        }
+        u_out = colgroup_max(u_out);
+        l_in = -colgroup_max(-l_in);
+        bool refine[OWN][2];
+        bool any_ref = false;
+#pragma unroll
+        for (int j = 0; j < OWN; ++j)
+#pragma unroll
+          for (int a = 0; a < 2; ++a) {
+            const float lo_b = own_s[j][a] - own_e[j][a], hi_b = own_s[j][a] + own_e[j][a];
+            refine[j][a] = my_scored && own_v[j][a] && ((in[j][a] && lo_b <= u_out) || (!in[j][a] && hi_b >= l_in));
+            any_ref |= refine[j][a];
+          }
+        const unsigned long long ref_lanes = __ballot(any_ref);
+        if (ref_lanes) {
+          // ---- pass 2 (lo) on the M-tiles holding undecided candidates; a row is read only if its
+          // candidate is undecided. The owners publish the flags in their key slots.
+#pragma unroll
+          for (int j = 0; j < OWN; ++j)
+#pragma unroll
+            for (int a = 0; a < 2; ++a) {
+              const int c = 8 * (h + j * G) + 2 * g + a;
+              if (own_v[j][a]) s_key[wave][xo][c] = refine[j][a] ? 1u : 0u;
+            }
+          __threadfence_block();
+#pragma unroll
+          for (int x = 0; x < UG; ++x) {
+            // lanes of unit x: columns xG .. xG+G-1 in every lane group
+            const unsigned long long xl = (((1ull << G) - 1) << (x * G)) * 0x0001000100010001ull;
+            if (n_cand[x] <= K || !(ref_lanes & xl)) continue;
+            const int mt = (2 * n_cand[x] + 15) >> 4;
+#pragma unroll
+            for (int m = 0; m < KM; ++m) {
+              if (m >= mt) break;
+              // the M-tile's 8 candidates: skip it when none is undecided (uniform)
+              const uint4 f0 = *reinterpret_cast<const uint4*>(&s_key[wave][x][8 * m]);
+              const uint4 f1 = *reinterpret_cast<const uint4*>(&s_key[wave][x][8 * m + 4]);
+              const bool tile = (8 * m + 0 < n_cand[x] && f0.x) || (8 * m + 1 < n_cand[x] && f0.y) ||
+                                (8 * m + 2 < n_cand[x] && f0.z) || (8 * m + 3 < n_cand[x] && f0.w) ||
+                                (8 * m + 4 < n_cand[x] && f1.x) || (8 * m + 5 < n_cand[x] && f1.y) ||
+                                (8 * m + 6 < n_cand[x] && f1.z) || (8 * m + 7 < n_cand[x] && f1.w);
+              if (!tile) continue;
+              const int kj = 4 * m + (col >> 2), c = kj * 2 + ((col >> 1) & 1);
+              const bool valid = c < n_cand[x] && ((col & 1) == 0 || c < n_full[x]);
+              const bool need = valid && s_key[wave][x][c] != 0u;
+              const int kn = s_kept[wave][cur][x][kj < nk[x] ? kj : 0];
+              Frag<uint16_t> lo[NS];
+              rows.load_lo(lo, off + (need ? 4 * kn + (col & 3) : 0), g, need);
+              f32x4 a = xo == x ? acc_own[m] : zero4();
+#pragma unroll
+              for (int s = 0; s < NS; ++s) mma_f16(a, lo[s], qh[s]);
+              if (xo == x) acc_own[m] = a;
+            }
+          }
+          head_scores(sc);
+          __threadfence_block();
+          // final keys: undecided -> hi+lo score, decided in -> +inf, decided out -> -inf
+#pragma unroll
+          for (int j = 0; j < OWN; ++j)
+#pragma unroll
+            for (int a = 0; a < 2; ++a) {
+              const int m = h + j * G;
+              float s = 0.f;
+#pragma unroll
+              for (int mm = 0; mm < KM; ++mm) s = mm == m ? sc[mm][a] : s;
+              own_s[j][a] = refine[j][a] ? s : (in[j][a] ? -kNegInf : kNegInf);
+              const int c = 8 * m + 2 * g + a;
+              if (own_v[j][a]) s_key[wave][xo][c] = topk_key(own_s[j][a], c);
+            }
+          __threadfence_block();
+#pragma unroll
+          for (int j = 0; j < OWN; ++j)
+#pragma unroll
+            for (int a = 0; a < 2; ++a) {
+              const int c = 8 * (h + j * G) + 2 * g + a;
+              in[j][a] = own_v[j][a] && rank_of(topk_key(own_s[j][a], c)) < K;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < OWN; ++j)
+#pragma unroll
+          for (int a = 0; a < 2; ++a) keep[j][a] = my_scored ? in[j][a] : own_v[j][a];
+      } else {
+#pragma unroll
+        for (int j = 0; j < OWN; ++j)
+#pragma unroll
+          for (int a = 0; a < 2; ++a) {
+            const int m = h + j * G;
+            keep[j][a] = m < KM && 8 * m + 2 * g + a < my_nc;
+          }
+      }
+      // ---- next kept lists: kept candidates in ascending order
+      if (lane < UG) s_mask[wave][lane] = 0ull;
+      __threadfence_block();
+#pragma unroll
+      for (int j = 0; j < OWN; ++j)
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+          const int c = 8 * (h + j * G) + 2 * g + a;
+          if (keep[j][a]) atomicOr(&s_mask[wave][xo], 1ull << c);
+        }
+      __threadfence_block();
+      const unsigned long long my_mask = s_mask[wave][xo];
+#pragma unroll
+      for (int j = 0; j < OWN; ++j)
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+          const int c = 8 * (h + j * G) + 2 * g + a;
+          if (keep[j][a]) s_kept[wave][cur ^ 1][xo][__popcll(my_mask & ((1ull << c) - 1))] = cand_node(c);
+        }
+      __threadfence_block();
+#pragma unroll
+      for (int x = 0; x < UG; ++x) nk[x] = __popcll(s_mask[wave][x]);
+      cur ^= 1;
+    }
+    // ---- level-1 kept nodes (ascending), -1 past the count
+#pragma unroll
+    for (int x = 0; x < UG; ++x) {
+      if (gi * UG + x >= p.N) break;
+      const long long u = (long long)bh * p.N + gi * UG + x;
+      if (lane < K) p.kept[u * K + lane] = lane < nk[x] ? s_kept[wave][cur][x][lane] : -1;
+    }
+    __threadfence_block();  // the next group rewrites this wave's LDS lists
+  }
+}
+
+template <int D, int C, int G, int KM>
+static hipError_t route_group_t(const SelDims& sd, const void* q, const void* hilo, const float* norms,
+                                const int* hexp, int* kept, hipStream_t st) {
+  GroupRouteParams p;
+  p.q = (const uint16_t*)q;
+  p.hilo = (const uint16_t*)hilo;
+  p.norms = norms;
+  p.hexp = hexp;
+  p.B = sd.B;
+  p.Hq = sd.Hq;
+  p.Hkv = sd.Hkv;
+  p.N = sd.N;
+  p.K = sd.K;
+  p.scale = sd.scale;
+  p.lv = sd.lv;
+  p.kept = kept;
+  // LDS-resident upper levels: the smallest level whose rows up to the root fit
+  int lcut = 0;
+  while (lcut < sd.lv.n_levels - 1 && (sd.lv.nodes - sd.lv.off[lcut]) * D * 2 > kGroupLdsBytes) ++lcut;
+  const int BH = sd.B * sd.Hkv;
+  const long long groups = (sd.N + 16 / G - 1) / (16 / G);
+  long long wph = 256 / BH;  // about one work-group per CU
+  if (wph < 1) wph = 1;
+  if (wph > (groups + kGroupWaves - 1) / kGroupWaves) wph = (groups + kGroupWaves - 1) / kGroupWaves;
+  hipLaunchKernelGGL((route_group_kernel<D, C, G, KM>), dim3((unsigned)(BH * wph)), dim3(kGroupWaves * 64), 0, st, p,
+                     (int)sd.lv.off[lcut], (int)wph);
+  return hipGetLastError();
+}
+
+template <int D, int C, int KM>
+static hipError_t route_group_g(const SelDims& sd, const void* q, const void* hilo, const float* norms,
+                                const int* hexp, int* kept, hipStream_t st) {
+  if (sd.G == 4) return route_group_t<D, C, 4, KM>(sd, q, hilo, norms, hexp, kept, st);
+  if (sd.G == 8) return route_group_t<D, C, 8, KM>(sd, q, hilo, norms, hexp, kept, st);
+  return route_group_t<D, C, 16, KM>(sd, q, hilo, norms, hexp, kept, st);
+}
+
+bool route_group_supported(const SelDims& sd) {
+  return sd.bf16 && (sd.G == 4 || sd.G == 8 || sd.G == 16) && sd.K <= 32;
+}
+
+hipError_t launch_route_group(const SelDims& sd, const void* q, const void* hilo, const float* norms, const int* hexp,
+                              int* kept, hipStream_t st) {
+  if (!route_group_supported(sd)) return hipErrorInvalidValue;
+#define PISA_RG(D, C)                                                             \
+  return sd.K <= 16 ? route_group_g<D, C, 4>(sd, q, hilo, norms, hexp, kept, st) \
+                    : route_group_g<D, C, 8>(sd, q, hilo, norms, hexp, kept, st)
+  if (sd.D == 128) {
+    if (sd.C == 64) PISA_RG(128, 64);
+    PISA_RG(128, 32);
+  }
+  if (sd.C == 64) PISA_RG(64, 64);
+  PISA_RG(64, 32);
+#undef PISA_RG
+}
+
+}  // namespace pisa

@@ -175,6 +175,7 @@ template <int D, int C, int KM>
 __global__ __launch_bounds__(1024) void route_lds_kernel(RouteParams<uint16_t> p, int lds_first, int wg_per_head) {
   constexpr int kLog2C = C == 64 ? 6 : 5;
   __shared__ __align__(16) uint16_t s_hi[kRouteLdsBytes / 2];
+  __shared__ float s_bound[kRouteLdsBytes / 128];  // one per staged row (rows of >= 64 values)
   __shared__ __align__(16) float s_sc[16][64];
   __shared__ __align__(16) uint32_t s_key[16][64];
   const int lane = lane_id(), wave = threadIdx.x >> 6, r16 = lane & 15, grp = lane >> 4;
@@ -182,11 +183,12 @@ __global__ __launch_bounds__(1024) void route_lds_kernel(RouteParams<uint16_t> p
   const int bh = blockIdx.x % BH, w = blockIdx.x / BH;  // consecutive work-groups: different heads
   LdsHiRows<D> rows;
   rows.base = (const uint16_t*)p.nodes + (long long)bh * p.lv.nodes * 2 * D;
-  rows.lds = s_hi;
-  rows.first = lds_first;
-  stage_hi_rows<D>(rows.base, lds_first, (int)(p.lv.nodes - lds_first), s_hi);
-  __syncthreads();
   const float* norms = p.norms + (long long)bh * p.lv.nodes;
+  rows.lds = s_hi;
+  rows.lds_bound = s_bound;
+  rows.first = lds_first;
+  stage_hi_rows<D>(rows.base, norms, lds_first, (int)(p.lv.nodes - lds_first), s_hi, s_bound);
+  __syncthreads();
   const int hexp = p.hexp[bh];
   const int b = bh / p.Hkv, r = bh % p.Hkv;
   const bool hv = r16 < p.G;

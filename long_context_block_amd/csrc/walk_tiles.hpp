@@ -37,6 +37,8 @@ struct NodeRows<uint16_t, D> {
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) hi[s].load(p + 32 * s);
   }
+  // the row's hi-plane score bound
+  __device__ __forceinline__ float bound(const float* norms, int node) const { return norms[node]; }
   __device__ __forceinline__ void load_lo(Frag<uint16_t> (&lo)[D / 32], int node, int grp, bool need) const {
     const uint16_t* p = base + (unsigned)node * (2 * D) + D + 8 * grp;
 #pragma unroll
@@ -80,7 +82,11 @@ __device__ __forceinline__ int route_q_f16(const Frag<uint16_t> (&qf)[D / 32], F
 template <int D>
 struct LdsHiRows : NodeRows<uint16_t, D> {
   const uint16_t* lds;
+  const float* lds_bound;  // the same rows' hi-plane bounds
   int first;
+  __device__ __forceinline__ float bound(const float* norms, int node) const {
+    return node >= first ? lds_bound[node - first] : norms[node];
+  }
   __device__ __forceinline__ void load_hi(Frag<uint16_t> (&hi)[D / 32], int node, int grp) const {
     if (node >= first) {
       const int r = node - first;
@@ -93,10 +99,13 @@ struct LdsHiRows : NodeRows<uint16_t, D> {
   }
 };
 
-// Cooperative copy of the hi planes of pyramid rows [first, first + n) into lds (layout above).
+// Cooperative copy of the hi planes of pyramid rows [first, first + n) into lds (layout above) and of
+// their bounds into lds_bound.
 template <int D>
-__device__ __forceinline__ void stage_hi_rows(const uint16_t* base, int first, int n, uint16_t* lds) {
+__device__ __forceinline__ void stage_hi_rows(const uint16_t* base, const float* norms, int first, int n,
+                                              uint16_t* lds, float* lds_bound) {
   constexpr int CHR = D / 8;
+  for (int x = threadIdx.x; x < n; x += blockDim.x) lds_bound[x] = norms[first + x];
   for (int x = threadIdx.x; x < n * CHR; x += blockDim.x) {
     const int r = x / CHR, c = x % CHR;
     *reinterpret_cast<uint4*>(lds + r * D + 8 * (c ^ (r & (CHR - 1)))) =
@@ -208,6 +217,12 @@ __device__ bool select_level_refine(const Rows& rows, const float* norms, int le
   const int MT = (2 * n_cand + 15) >> 4;
   const bool last_two = 2 * readlane(cn, n_cand - 1) + 1 < e_child;
   const int n_full = last_two ? n_cand : n_cand - 1;
+  // the candidates' child-row bounds, requested ahead of the row loads
+  float nb0 = 0.f, nb1 = 0.f;
+  if (lane < n_cand) {
+    nb0 = rows.bound(norms, level_off + 2 * cn);
+    nb1 = lane < n_full ? rows.bound(norms, level_off + 2 * cn + 1) : 0.f;
+  }
   int child[KM];
   bool valid[KM];
 #pragma unroll
@@ -243,12 +258,7 @@ __device__ bool select_level_refine(const Rows& rows, const float* norms, int le
 #pragma unroll
   for (int m = 0; m < KM; ++m)
     if (m < MT) cand_scores(m, ~0ull);
-  float e = 0.f;
-  if (lane < n_cand) {
-    const float n0 = norms[level_off + 2 * cn];
-    const float n1 = lane < n_full ? norms[level_off + 2 * cn + 1] : 0.f;
-    e = scale * qnorm_sum * fmaxf(n0, n1);
-  }
+  const float e = lane < n_cand ? scale * qnorm_sum * fmaxf(nb0, nb1) : 0.f;
   __threadfence_block();
   const float sh = lane < n_cand ? s_sc[lane] : kNegInf;
   const bool in = topk_keep_lds(s_sc, n_cand, K, keys);
