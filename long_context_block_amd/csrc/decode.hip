@@ -3,18 +3,18 @@
 // token's ancestor path, amortised O(log N) per step, and one kernel covers every level so that no
 // further launches are paid).
 //
-// One work-group (4 waves) per (sequence b, KV head r), i.e. per decode unit; p = cached length:
+// One work-group (8 waves) per (sequence b, KV head r), i.e. per decode unit; p = cached length:
 //   1. append k_new, v_new at position p; add k_new to the sum of each ancestor of leaf p / C (every
 //      level of the capacity layout) and refresh that node's mean = sum / tokens held;
-//   2. walk the levels for query i = p: per scored level all 256 threads stage the candidates'
-//      child means into LDS (bf16 hi/lo, or fp32 for fp32 inputs), then wave 0 scores them on MFMA
-//      and keeps the Top-K;
-//   3. leaf stage: the kept level-1 nodes' leaf pairs are spread over the 4 waves (exact per-head
+//   2. walk the levels for query i = p: per scored level all threads stage the candidates' child
+//      means into LDS (bf16 hi/lo, or fp32 for fp32 inputs), each wave scores one M-tile on MFMA
+//      (8 candidates), and wave 0 keeps the Top-K;
+//   3. leaf stage: the kept level-1 nodes' leaf pairs are spread over the 8 waves (exact per-head
 //      LSE with the causal mask), wave 0 takes the leaf Top-K;
 //   4. attention: the selected leaves are spread over the waves; each wave merges its leaves'
-//      partial outputs with running LSE weights, and the 4 wave results are merged at the end.
-// The update lands before the walk reads it: writes are fenced and the work-group synchronises,
-// and a work-group only reads its own (b, r) cache and pyramid.
+//      partial outputs with running LSE weights, and the 8 wave results are merged at the end.
+// The update lands before the walk reads it: writes are fenced (work-group scope) and the work-group
+// synchronises, and a work-group only reads its own (b, r) cache and pyramid.
 #include "attn_tiles.hpp"
 #include "common.hpp"
 #include "internal.hpp"
@@ -39,14 +39,20 @@ struct DecodeParams {
   LensArg lens;
 };
 
+constexpr int kDecodeWaves = 8;
+
 template <typename T, int D, int C, int KM>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeParams<T> p) {
+__global__ __launch_bounds__(kDecodeWaves * 64) void decode_kernel(DecodeParams<T> p) {
+  constexpr int NW = kDecodeWaves;
+  constexpr int NT = NW * 64;
   constexpr int LOG2C = C == 64 ? 6 : 5;
   constexpr int ROWB = sizeof(T) == 2 ? 2 * D * 2 : D * 4;  // bytes per staged child row
   constexpr int STAGE = 16 * KM * ROWB;                     // 2K candidates x 2 children
-  constexpr int VTB = 4 * D * (C + 8) * 2;
-  constexpr int UNION = STAGE > VTB ? STAGE : VTB;
+  constexpr int VTB = NW * D * (C + 8) * 2;                 // per-wave transposed V tiles
+  constexpr int OB = NW * 16 * D * 4;                       // per-wave outputs for the final merge
+  constexpr int UNION = STAGE > VTB ? (STAGE > OB ? STAGE : OB) : (VTB > OB ? VTB : OB);
   constexpr int MO = D / 16;
+  static_assert(KM <= NW, "one M-tile per wave");
   __shared__ __align__(16) unsigned char s_buf[UNION];
   __shared__ __align__(16) float s_sc[64];
   __shared__ __align__(16) uint32_t s_key[64];
@@ -54,8 +60,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams<T> p) {
   __shared__ int s_kept[64];
   __shared__ int s_sel[64];
   __shared__ int s_n[2];
-  __shared__ __align__(16) float s_o[4][16][D];
-  __shared__ float s_lse[4][16];
+  __shared__ float s_lse[NW][16];
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6, r16 = lane & 15, grp = lane >> 4;
   const int bh = blockIdx.x;
   const int b = bh / p.Hkv, r = bh % p.Hkv;
@@ -87,7 +92,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams<T> p) {
       }
     }
   }
-  __threadfence();
+  // Only this work-group reads these writes during the step (its own cache rows and pyramid path),
+  // so a work-group-scope fence orders them before the barrier; the next step is a new launch.
+  __threadfence_block();
   __syncthreads();
   // query fragments: columns = the group's heads
   Frag<T> qf[D / 32];
@@ -139,11 +146,11 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams<T> p) {
       const int n_rows = 2 * n_cand;
       const long long lvl_row = head_row + p.lv.off[l - 1];
       // all of this thread's row loads are issued before any is used
-      constexpr int SPT = (16 * KM * (D / 4) + 255) / 256;  // staging items per thread
+      constexpr int SPT = (16 * KM * (D / 4) + NT - 1) / NT;  // staging items per thread
       float4 mv[SPT];
 #pragma unroll
       for (int it = 0; it < SPT; ++it) {
-        const int x = tid + 256 * it;
+        const int x = tid + NT * it;
         mv[it] = make_float4(0.f, 0.f, 0.f, 0.f);
         if (x < n_rows * (D / 4)) {
           const int rho = x / (D / 4), q4 = x % (D / 4);
@@ -154,7 +161,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams<T> p) {
       }
 #pragma unroll
       for (int it = 0; it < SPT; ++it) {
-        const int x = tid + 256 * it;
+        const int x = tid + NT * it;
         if (x >= n_rows * (D / 4)) continue;
         const int rho = x / (D / 4), q4 = x % (D / 4);
         const float4 m = mv[it];
@@ -172,11 +179,14 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams<T> p) {
         }
       }
       __syncthreads();
-      if (wave == 0) {
+      if (wave < (2 * n_cand + 15) >> 4) {  // one M-tile (8 candidates) per wave
         StagedRows<T, D> rows;
         rows.base = reinterpret_cast<const T*>(s_buf);
+        score_staged_mtile<T, D>(rows, qf, wave, n_full, p.G, p.scale, s_sc);
+      }
+      __syncthreads();
+      if (wave == 0) {
         const int cn = lane < n_cand ? 2 * s_kept[lane >> 1] + (lane & 1) : -1;
-        score_candidates<T, D, KM, StagedRows<T, D>>(rows, 0, qf, cn, n_cand, e_child, p.G, p.scale, s_sc);
         const bool keep = topk_keep_lds(s_sc, n_cand, K, s_key);
         int cnt;
         const int nxt = compact_lanes(keep, cn, &cnt);
@@ -191,7 +201,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams<T> p) {
   // ---- 3. leaf stage: pairs of leaves under the kept level-1 nodes
   const T* kbh = p.k_cache + (long long)bh * p.Nmax * D;
   const T* vbh = p.v_cache + (long long)bh * p.Nmax * D;
-  for (int slot = wave; slot < nk; slot += 4) {
+  for (int slot = wave; slot < nk; slot += NW) {
     const long long pn = s_kept[slot];
     Frag<T> kf[C / 8][D / 32];
     load_leaf_pair<T, D, C>(kbh, 2 * pn * C, len, kf);
@@ -228,7 +238,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams<T> p) {
   for (int mt = 0; mt < MO; ++mt) run_o[mt] = zero4();
   float run_lse = kNegInf;
   uint16_t(*vt)[C + 8] = reinterpret_cast<uint16_t(*)[C + 8]>(s_buf) + wave * D;
-  for (int k = wave; k < nsel; k += 4) {
+  for (int k = wave; k < nsel; k += NW) {
     const long long t0 = (long long)s_sel[k] * C;
     Frag<T> kf[C / 16][D / 32];
     load_attn_k<T, D, C>(kbh, t0, len, kf);
@@ -250,20 +260,22 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams<T> p) {
       run_lse = m + kLn2 * fast_log2(den);
     }
   }
+  __syncthreads();  // every wave is done with its transposed V tiles: s_buf now holds the outputs
+  float(*s_o)[16][D] = reinterpret_cast<float(*)[16][D]>(s_buf);
 #pragma unroll
   for (int mt = 0; mt < MO; ++mt)
 #pragma unroll
     for (int j = 0; j < 4; ++j) s_o[wave][r16][attn_out_dim<D>(mt, grp, j)] = run_o[mt][j];
   if (grp == 0) s_lse[wave][r16] = run_lse;
   __syncthreads();
-  for (int x = tid; x < p.G * D; x += 256) {
+  for (int x = tid; x < p.G * D; x += NT) {
     const int h = x / D, d = x % D;
     float m = kNegInf;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) m = fmaxf(m, s_lse[w][h]);
+    for (int w = 0; w < NW; ++w) m = fmaxf(m, s_lse[w][h]);
     float num = 0.f, den = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float lw = s_lse[w][h];
       const float wt = lw == kNegInf ? 0.f : fast_exp2((lw - m) * kLog2e);
       num += wt * s_o[w][h][d];
@@ -298,9 +310,9 @@ static hipError_t decode_t(const DecodeArgs& da, const void* q_new, const void* 
   p.lens = da.lens;
   const int grid = da.B * da.Hkv;
   if (da.K <= 16)
-    hipLaunchKernelGGL((decode_kernel<T, D, C, 4>), dim3(grid), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((decode_kernel<T, D, C, 4>), dim3(grid), dim3(kDecodeWaves * 64), 0, st, p);
   else
-    hipLaunchKernelGGL((decode_kernel<T, D, C, 8>), dim3(grid), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((decode_kernel<T, D, C, 8>), dim3(grid), dim3(kDecodeWaves * 64), 0, st, p);
   return hipGetLastError();
 }
 

@@ -196,6 +196,27 @@ __device__ void score_candidates(const Rows& rows, int level_off, const Frag<T> 
   __threadfence_block();
 }
 
+// One M-tile (candidates 8 m .. 8 m + 7) of score_candidates over rows already staged in MFMA-row
+// order (local row 16 m + r = child r & 1 of candidate 8 m + r / 2): the same per-candidate arithmetic,
+// so a level's M-tiles can be scored by different waves. n_full = candidates with two eligible children.
+template <typename T, int D>
+__device__ __forceinline__ void score_staged_mtile(const StagedRows<T, D>& rows, const Frag<T> (&qf)[D / 32], int m,
+                                                   int n_full, int G, float scale, float* s_sc) {
+  const int r16 = lane_id() & 15, grp = lane_id() >> 4;
+  typename NodeRows<T, D>::Row f;
+  rows.load(f, 16 * m + r16, grp);
+  f32x4 acc = zero4();
+  rows.dot(acc, f, qf);
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    const int c = 8 * m + 2 * grp + a;
+    const float x0 = scale * acc[2 * a], x1 = scale * acc[2 * a + 1];
+    float l = c < n_full ? lse2(x0, x1) : x0;
+    l = row_sum16(r16 < G ? l : 0.f);
+    if (r16 == 0) s_sc[c] = l;
+  }
+}
+
 // One scored level for bf16 inputs, in two passes over the <= 4K child rows of the fp16 routing planes
 // (hi = rne(2^hexp mean), lo = rne(2^hexp mean - hi)). Pass 1 uses the hi plane only; a candidate's
 // score then lies within E_c = scale * sum_h |q_h| * max over its children of the row bound b
@@ -331,20 +352,18 @@ __device__ int walk_to_level1(const Levels& lv, int log2c, int K, int i, int* ke
   return nk;
 }
 
-// Key tile of leaves 2p and 2p+1: rows = tokens t0 .. t0+2C-1 of one KV head (zero past N).
+// Key tile of leaves 2p and 2p+1: rows = tokens t0 .. t0+2C-1 of one KV head. Rows past N repeat token
+// N - 1: those tokens are later than every query, so the causal mask drops them before any use (the
+// loads stay unconditional, so all of them are in flight together).
 template <typename T, int D, int C>
 __device__ __forceinline__ void load_leaf_pair(const T* kbh, long long t0, int N, Frag<T> (&kf)[C / 8][D / 32]) {
   const int r16 = lane_id() & 15, grp = lane_id() >> 4;
 #pragma unroll
   for (int m = 0; m < C / 8; ++m) {
-    const long long t = t0 + 16 * m + r16;
+    long long t = t0 + 16 * m + r16;
+    t = t < N ? t : N - 1;
 #pragma unroll
-    for (int s = 0; s < D / 32; ++s) {
-      if (t < N)
-        kf[m][s].load(kbh + t * D + 32 * s + 8 * grp);
-      else
-        kf[m][s].zero();
-    }
+    for (int s = 0; s < D / 32; ++s) kf[m][s].load(kbh + t * D + 32 * s + 8 * grp);
   }
 }
 
