@@ -74,6 +74,34 @@ def test_determinism_and_qtile_identity_64k_slice():
     assert_report(rep, "bf16")
 
 
+# Pyramids too large for the routing kernels' LDS-resident levels: the lower levels' rows are gathered
+# from global memory. One case per routing variant (GQA 2 runs the one-unit walk with LDS levels,
+# GQA 4/8/16 the several-units-per-wave walk; K = 32 doubles the candidate tiles; d = 64 halves the
+# rows).
+LDS_SPILL = {
+    "g2_64k": dict(B=1, Hq=4, Hkv=2, N=65536, d=128, C=64, K=16),
+    "g8_64k": dict(B=1, Hq=16, Hkv=2, N=65536, d=128, C=64, K=16),
+    "g16_32k": dict(B=1, Hq=16, Hkv=1, N=32768, d=128, C=64, K=16),
+    "k32_64k": dict(B=1, Hq=8, Hkv=2, N=65536, d=128, C=64, K=32),
+    "d64_c32_64k": dict(B=1, Hq=8, Hkv=2, N=65536, d=64, C=32, K=16),
+}
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", sorted(LDS_SPILL))
+def test_routing_beyond_lds_levels(name):
+    spec = LDS_SPILL[name]
+    say(f"[lds-spill] {name} {spec}")
+    pf = I.make_prefill(seed=0, workload_id=102, dtype="bf16", keys="ar1", **spec)
+    qt = _max_qtile(pf.G)
+    g1 = run_gpu(pf, 1, attn=False)
+    gt = run_gpu(pf, qt) if qt > 1 else run_gpu(pf, 1)
+    assert np.array_equal(g1.sel, gt.sel)
+    assert np.array_equal(g1.sel_lse.view(np.uint32), gt.sel_lse.view(np.uint32))
+    rep = compare(pf, gt, units_sample(pf, 150, seed=3))
+    assert_report(rep, pf.dtype)
+
+
 def _full(name, q_tiles, n_sample, extra_units=(), check_bsa=True):
     say(f"[full] generating {name}")
     pf = I.make_workload(name)
