@@ -259,6 +259,26 @@ def main():
     log(f"[bench] step {step_ms:.3f} ms (wall {wall / args.steps * 1e3:.3f} ms); stages " +
         ", ".join(f"{n}={v:.3f}" for n, v in sorted(st_ms.items())))
 
+    # the same selection with q_tile 1 (one unit per leaf-stage tile), for the q_tile comparison
+    sel_q1_ms = None
+    if qt > 1:
+        s1 = P.make_shape(batch=pf.B, seq_len=pf.N, n_q_heads=pf.Hq, n_kv_heads=pf.Hkv, head_dim=pf.d, block=pf.C,
+                          top_k=pf.K, q_tile=1, dtype=pf.dtype)
+        ws1 = P.alloc_workspace(s1, P.PISA_OP_SELECT)
+        sel1 = torch.empty_like(sel)
+        for _ in range(2):
+            P.pisa_select(s1, q, k, pyr, sel1, None, ws1)
+        torch.cuda.synchronize()
+        P.pisa_stage_timing(True)
+        n1 = max(2, args.steps // 2)
+        for _ in range(n1):
+            P.pisa_build_pyramid(s1, k, pyr)
+            P.pisa_select(s1, q, k, pyr, sel1, None, ws1)
+        torch.cuda.synchronize()
+        st1 = P.pisa_stage_times()
+        P.pisa_stage_timing(False)
+        sel_q1_ms = sum(tot / cnt for name, (tot, cnt) in st1.items())
+        del ws1, sel1
     sel_np = sel.cpu().numpy()
     w = work_counts(pf, sel_np)
     sel_stage_names = ["pyramid", "route_planes", "route", "regroup_select", "leaf_lse", "finalize", "route_fused_leaf"]
@@ -315,6 +335,7 @@ def main():
         "config": {"workload": args.workload, "batch": pf.B, "seq_len": pf.N, "n_q_heads": pf.Hq,
                    "n_kv_heads": pf.Hkv, "head_dim": pf.d, "block": pf.C, "top_k": pf.K, "branch": 2, "q_tile": qt},
         "selection_ms": round(selection_ms, 4),
+        "selection_ms_q_tile_1": round(sel_q1_ms, 4) if sel_q1_ms else None,
         "sparse_attn_ms": round(attn_ms, 4),
         "sparse_attn_tflops": round(w["attn_flops"] / (attn_ms * 1e-3) / 1e12, 2) if attn_ms else None,
         "bsa_select_ms": round(bsa_ms, 4),

@@ -32,7 +32,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 STAGE_KERNELS = {
     "pyramid": ["pool_subtree_kernel", "pool_upper_kernel"],
     "route_planes": ["head_max_kernel", "split_f16_kernel"],
-    "route": ["route_lds_kernel", "route_kernel"],
+    "route_fused_leaf": [],  # route_kernel<..., true, ...>: the q_tile 1 walk with its own leaf stage
+    "route": ["route_group_kernel", "route_lds_kernel", "route_kernel"],
     "regroup": ["hist_kernel", "scan_kernel", "scatter_kernel", "fill_zero_kernel"],
     "leaf_lse": ["leaf_lse_wg_kernel", "leaf_lse_kernel"],
     "finalize": ["finalize_kernel"],
@@ -64,6 +65,8 @@ def short_name(name: str) -> str:
 
 
 def stage_of(name: str) -> str | None:
+    if re.search(r"\broute_kernel<[^>]*\btrue\b", name):
+        return "route_fused_leaf"
     for stage, frags in STAGE_KERNELS.items():
         for f in frags:
             if re.search(r"\b" + f + r"\b", name):
