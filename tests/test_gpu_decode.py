@@ -122,6 +122,15 @@ def test_decode_small_every_step(dtype, d, C, K, G):
     _run_decode(dec, units)
 
 
+@pytest.mark.parametrize("K,G,C", [(32, 16, 32), (32, 4, 64)])
+def test_decode_large_k(K, G, C):
+    # K = 32 doubles the candidate tiles; the caches are long enough for levels with more than K nodes
+    Hkv = 2
+    dec = I.make_decode(B=2, Hq=G * Hkv, Hkv=Hkv, N0=[2500, 4200], d=128, C=C, K=K, steps=40, Nmax=4300,
+                        dtype="bf16", seed=0, workload_id=302)
+    _run_decode(dec, [(b, r) for b in range(2) for r in range(Hkv)])
+
+
 def test_decode_from_tiny_cache():
     # the cache starts with one token: the tree grows from a single leaf
     dec = I.make_decode(B=1, Hq=4, Hkv=1, N0=1, d=128, C=64, K=4, steps=300, Nmax=512, dtype="bf16", seed=0,
