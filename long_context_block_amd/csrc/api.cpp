@@ -235,9 +235,9 @@ size_t carve_attn(const Plan& p, void* ws, AttnWs* w) {
   const size_t NB = (size_t)p.BH * p.nch * p.sd.lv.n[0];
   x.counts = (int*)c.take(NB * 4);
   x.offsets = (int*)c.take((NB + 1) * 4);
-  x.ranks = (int*)c.take(pairs * 4);
+  x.ranks = (int*)c.take(pairs * 4);  // after the regroup: each pair's index in the sorted list
   x.pairs = (uint32_t*)c.take(pairs * 4);
-  x.part = c.take(pairs * p.sd.G * p.sd.D * p.elem);
+  x.part = c.take(pairs * p.sd.G * p.sd.D * p.elem);  // rows in sorted-pair order
   x.part_lse = (float*)c.take(pairs * p.sd.G * 4);
   if (w) *w = x;
   return c.off;
@@ -393,7 +393,7 @@ pisa_status pisa_select(const pisa_shape* shape, const void* q, const void* k, c
   {
     Stage sc(s, "regroup_select");
     e = pisa::launch_regroup(w.kept, p.U, p.sd.K, p.sd.N, p.n1_buckets, (int)p.BH, p.sd.chunk_log2, w.counts,
-                             w.offsets, w.ranks, w.pairs, s);
+                             w.offsets, w.ranks, false, w.pairs, s);
   }
   if (e != hipSuccess) return hip_status(e, "regroup");
   const int* total = w.offsets + p.BH * p.nch * p.n1_buckets;
@@ -430,7 +430,7 @@ pisa_status pisa_sparse_attn(const pisa_shape* shape, const void* q, const void*
   {
     Stage sc(s, "regroup_attn");
     e = pisa::launch_regroup(sel, p.U, p.sd.K, p.sd.N, p.sd.lv.n[0], (int)p.BH, p.sd.chunk_log2, w.counts,
-                             w.offsets, w.ranks, w.pairs, s);
+                             w.offsets, w.ranks, true, w.pairs, s);
   }
   if (e != hipSuccess) return hip_status(e, "regroup");
   const int* total = w.offsets + p.BH * p.nch * p.sd.lv.n[0];
@@ -441,7 +441,7 @@ pisa_status pisa_sparse_attn(const pisa_shape* shape, const void* q, const void*
   if (e != hipSuccess) return hip_status(e, "attn_leaf");
   {
     Stage sc(s, "attn_merge");
-    e = pisa::launch_attn_merge(p.sd, sel, w.part, w.part_lse, o, o_lse, s);
+    e = pisa::launch_attn_merge(p.sd, sel, w.ranks, w.part, w.part_lse, o, o_lse, s);
   }
   return hip_status(e, "attn_merge");
 }

@@ -9,6 +9,8 @@
 //   O^T = V^T P (MFMA, P in the input type) ; partial = O / l, lse = s m + ln l.
 // The K tile rows are permuted so that after the first MFMA each lane group holds 8 consecutive
 // tokens per 32-token step, which is exactly the B operand the second MFMA needs (no shuffle).
+// Partial rows are stored in sorted-pair order (pair x owns rows x G .. x G + G - 1), so a work-group
+// writes one contiguous range; the regroup leaves each pair's sorted index in pos[u K + slot].
 // attn_merge combines a unit's K partials with weights exp(lse_k - LSE), LSE = LSE_k lse_k.
 #include "attn_tiles.hpp"
 #include "common.hpp"
@@ -27,8 +29,8 @@ struct AttnParams {
   const int* total;
   int B, Hq, Hkv, G, N, K, tasks, chunk_log2;
   float scale;
-  T* part;         // [U, K, G, D]
-  float* part_lse; // [U, K, G]
+  T* part;         // [pairs, G, D], rows in sorted-pair order
+  float* part_lse; // [pairs, G]
 };
 
 constexpr int kAttnTask = 256;
@@ -83,17 +85,16 @@ __global__ __launch_bounds__(256) void attn_leaf_kernel(AttnParams<T> p) {
     const long long ubase = bh * p.N;
     struct Tile {
       Frag<T> qf[D / 32];
-      long long u;
-      int slot;
+      long long u, at;  // unit, sorted index of the pair
     };
     // A column past the run repeats the run's first pair: it computes that pair's result again and
     // stores the same bytes to the same place. Loads and stores are therefore unconditional and the
     // tile loop is straight-line code, which lets the query prefetch stay in flight across tiles.
     auto fetch = [&](Tile& t, long long tp) {
       const long long pi = tp + r16 / p.G;
-      const uint32_t pc = run.pair(pi < seg ? pi : pos);
+      t.at = pi < seg ? pi : pos;
+      const uint32_t pc = run.pair(t.at);
       t.u = pc >> 5;
-      t.slot = pc & 31;
       const T* qrow = qhead + (t.u - ubase) * D;
 #pragma unroll
       for (int s = 0; s < D / 32; ++s) t.qf[s].load(qrow + 32 * s);
@@ -105,7 +106,7 @@ __global__ __launch_bounds__(256) void attn_leaf_kernel(AttnParams<T> p) {
       f32x4 oacc[MO];
       float lse, inv;
       attend_tile<T, D, C>(kf, vf, qf, t0, cur.u - ubase, p.scale, oacc, lse, inv);
-      const long long prow = (cur.u * p.K + cur.slot) * p.G + h;
+      const long long prow = cur.at * p.G + h;
       // lane group grp holds dimensions 32 c + 8 grp .. +8 in oacc[2c], oacc[2c + 1]
       T* dst = p.part + prow * D + 8 * grp;
       if constexpr (sizeof(T) == 2) {
@@ -191,33 +192,39 @@ __global__ __launch_bounds__(256, 3) void attn_leaf_wg_kernel(AttnParams<uint16_
     stage_kv_wg<D, C>(kbh, vbh, t0, p.N, s_k, s_vt);
     __syncthreads();
     const int bi = (int)(bh / p.Hkv), ri = (int)(bh % p.Hkv);
-    const uint16_t* qhead = p.q + (((long long)bi * p.Hq + (long long)ri * p.G + h) * p.N) * D + 8 * grp;
+    const int qr = quad_row(), hq = qr % p.G;
+    const uint16_t* qhead = p.q + (((long long)bi * p.Hq + (long long)ri * p.G + hq) * p.N) * D + 8 * quad_chunk();
     const long long ubase = bh * p.N;
     const int ntiles = (b - a + tile_units - 1) / tile_units;
     // The query fragments of tile t + 4 (this wave's next tile) are requested before tile t is
     // computed. A column past the run, or past the wave's last tile, repeats the run's first pair:
-    // same result, same bytes, same place.
-    auto fetch = [&](int t, Frag<uint16_t> (&qf)[D / 32], uint32_t& pc) {
-      int x = a + t * tile_units + r16 / p.G;
-      x = (t < ntiles && x < b) ? x : a;
-      pc = s_pair[x];
-      const uint16_t* qrow = qhead + ((long long)(pc >> 5) - ubase) * D;
+    // same result, same bytes, same place. The loads are quad-coalesced (lane 4 r + g reads row r);
+    // quad_rows_to_mfma() before use.
+    // xc is the column's pair (its index in the task)
+    auto fetch = [&](int t, Frag<uint16_t> (&qf)[D / 32], int& xc) {
+      int xl = a + t * tile_units + qr / p.G;
+      xl = (t < ntiles && xl < b) ? xl : a;
+      const uint16_t* qrow = qhead + ((long long)(s_pair[xl] >> 5) - ubase) * D;
 #pragma unroll
       for (int s2 = 0; s2 < D / 32; ++s2) qf[s2].load(qrow + 32 * s2);
+      const int x = a + t * tile_units + r16 / p.G;
+      xc = (t < ntiles && x < b) ? x : a;
     };
     struct Out {
       f32x4 o[MO];
       float lse, inv;
-      uint32_t pc;
+      int xc;
     };
-    auto attend = [&](const Frag<uint16_t> (&qf)[D / 32], uint32_t pc, Out& out) {
-      out.pc = pc;
+    auto attend = [&](Frag<uint16_t> (&qf)[D / 32], int xc, Out& out) {
+      out.xc = xc;
+      quad_rows_to_mfma(qf);
       attend_tile_kv<uint16_t, D, C, true>([&](int m, int s2) { return k_frag_wg<D>(s_k, m, s2); },
                                            [&](int mt, int ks) { return vt_frag<C>(s_vt, mt, ks); }, qf, t0,
-                                           (long long)(pc >> 5) - ubase, p.scale, out.o, out.lse, out.inv);
+                                           (long long)(s_pair[xc] >> 5) - ubase, p.scale, out.o, out.lse, out.inv);
     };
+    // partial rows in sorted-pair order: a tile's rows are contiguous
     auto store = [&](const Out& out) {
-      const long long prow = ((long long)(out.pc >> 5) * p.K + (out.pc & 31)) * p.G + h;
+      const long long prow = (base + out.xc) * p.G + h;
       // lane group grp holds dimensions 32 c + 8 grp .. +8 in o[2c], o[2c + 1]
       uint16_t* dst = p.part + prow * D + 8 * grp;
       const float inv = out.inv;
@@ -237,7 +244,7 @@ __global__ __launch_bounds__(256, 3) void attn_leaf_wg_kernel(AttnParams<uint16_
       // t + 8 and t + 12 are in flight (a tile past the end repeats the run's first pair); each
       // prefetch is issued before the stores of the tile just computed
       Frag<uint16_t> qa[D / 32], qb[D / 32];
-      uint32_t pa, pb;
+      int pa, pb;
       fetch(wave, qa, pa);
       fetch(wave + 4, qb, pb);
       opaque_frags(qa);
@@ -259,6 +266,7 @@ __global__ __launch_bounds__(256, 3) void attn_leaf_wg_kernel(AttnParams<uint16_
 template <typename T>
 struct MergeParams {
   const int* sel;
+  const int* pos;  // [U, K]: sorted index of the pair (u, slot), the row block of its partials
   const T* part;
   const float* part_lse;
   int B, Hq, Hkv, G, N, K;
@@ -270,7 +278,7 @@ struct MergeParams {
 // chunk); a wave takes 64 / DC consecutive tasks, so for G >= 64 / DC its loads of one slot cover the
 // unit's G heads in one contiguous run. Per task: M = max_k lse_k, S = sum_k exp(lse_k - M),
 // o = sum_k (exp(lse_k - M) / S) partial_k, LSE = M + ln S. Slots k < nsel hold the selected leaves
-// (selections are left-packed), so only those partial rows are read.
+// (selections are left-packed), so only those partial rows are read, found through pos.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(MergeParams<T> p) {
   constexpr int E = 16 / (int)sizeof(T);  // elements per chunk
@@ -293,11 +301,13 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeParams<T> p) {
     nsel += __popcll((m >> base) & (DC == 64 ? ~0ull : ((1ull << DC) - 1)));
   }
   float lv[KJ];
+  int at[KJ];
   float mx = kNegInf;
 #pragma unroll
   for (int j = 0; j < KJ; ++j) {
     const int kk = li + j * DC;
-    lv[j] = kk < nsel ? p.part_lse[(u * p.K + kk) * p.G + h] : kNegInf;
+    at[j] = kk < nsel ? p.pos[u * p.K + kk] : 0;
+    lv[j] = kk < nsel ? p.part_lse[(long long)at[j] * p.G + h] : kNegInf;
     mx = fmaxf(mx, lv[j]);
   }
 #pragma unroll
@@ -318,19 +328,22 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeParams<T> p) {
   int nmax = nsel;
 #pragma unroll
   for (int o = DC; o < 64; o <<= 1) nmax = max(nmax, __shfl_xor(nmax, o));
-  const T* src = p.part + (u * p.K * p.G + h) * (long long)D + li * E;
+  const T* src = p.part + (long long)h * D + li * E;
   for (int kk = 0; kk < nmax; ++kk) {
-    const float w0 = __shfl(lv[0], base + (kk % DC));
-    float w = w0;
+    float w = __shfl(lv[0], base + (kk % DC));
+    int ak = __shfl(at[0], base + (kk % DC));
 #pragma unroll
     for (int j = 1; j < KJ; ++j) {
       const float wj = __shfl(lv[j], base + (kk % DC));
+      const int aj = __shfl(at[j], base + (kk % DC));
       w = (kk / DC == j) ? wj : w;
+      ak = (kk / DC == j) ? aj : ak;
     }
     if (kk < nsel) {
       w *= rs;
+      const T* row = src + (long long)ak * p.G * D;
       if constexpr (sizeof(T) == 2) {
-        const uint4 x = *reinterpret_cast<const uint4*>(src + (long long)kk * p.G * D);
+        const uint4 x = *reinterpret_cast<const uint4*>(row);
         const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -338,7 +351,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeParams<T> p) {
           acc[2 * e + 1] += w * __uint_as_float(xs[e] & 0xffff0000u);
         }
       } else {
-        const float4 x = *reinterpret_cast<const float4*>(src + (long long)kk * p.G * D);
+        const float4 x = *reinterpret_cast<const float4*>(row);
         acc[0] += w * x.x;
         acc[1] += w * x.y;
         acc[2] += w * x.z;
@@ -419,10 +432,11 @@ hipError_t launch_attn_leaf(const SelDims& sd, const void* q, const void* k, con
 }
 
 template <typename T, int D>
-static hipError_t merge_t(const SelDims& sd, const int* sel, const void* part, const float* part_lse, void* o,
-                          float* o_lse, hipStream_t st) {
+static hipError_t merge_t(const SelDims& sd, const int* sel, const int* pos, const void* part,
+                          const float* part_lse, void* o, float* o_lse, hipStream_t st) {
   MergeParams<T> p;
   p.sel = sel;
+  p.pos = pos;
   p.part = (const T*)part;
   p.part_lse = part_lse;
   p.B = sd.B;
@@ -440,12 +454,12 @@ static hipError_t merge_t(const SelDims& sd, const int* sel, const void* part, c
   return hipGetLastError();
 }
 
-hipError_t launch_attn_merge(const SelDims& sd, const int* sel, const void* part, const float* part_lse, void* o,
-                             float* o_lse, hipStream_t st) {
-  if (sd.bf16) return sd.D == 128 ? merge_t<uint16_t, 128>(sd, sel, part, part_lse, o, o_lse, st)
-                                  : merge_t<uint16_t, 64>(sd, sel, part, part_lse, o, o_lse, st);
-  return sd.D == 128 ? merge_t<float, 128>(sd, sel, part, part_lse, o, o_lse, st)
-                     : merge_t<float, 64>(sd, sel, part, part_lse, o, o_lse, st);
+hipError_t launch_attn_merge(const SelDims& sd, const int* sel, const int* pos, const void* part,
+                             const float* part_lse, void* o, float* o_lse, hipStream_t st) {
+  if (sd.bf16) return sd.D == 128 ? merge_t<uint16_t, 128>(sd, sel, pos, part, part_lse, o, o_lse, st)
+                                  : merge_t<uint16_t, 64>(sd, sel, pos, part, part_lse, o, o_lse, st);
+  return sd.D == 128 ? merge_t<float, 128>(sd, sel, pos, part, part_lse, o, o_lse, st)
+                     : merge_t<float, 64>(sd, sel, pos, part, part_lse, o, o_lse, st);
 }
 
 }  // namespace pisa

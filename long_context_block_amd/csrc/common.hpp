@@ -96,6 +96,25 @@ __device__ __forceinline__ void mma(f32x4& acc, const Frag<uint16_t>& a, const F
                                                 acc, 0, 0, 0);
 }
 
+// Quad-coalesced gathers of a 16-row operand tile. In the MFMA operand layout lane r + 16 g holds
+// row r, so the four lanes of a quad would read four rows (four cache lines per quad). Instead lane
+// 4 r + g loads row r's chunks 4 s + g (s = 0 .. NS-1; each quad reads one contiguous 64-byte piece of
+// one row per load), and quad_rows_to_mfma() moves every lane's chunks to lane r + 16 g.
+__device__ __forceinline__ int quad_row() { return lane_id() >> 2; }
+__device__ __forceinline__ int quad_chunk() { return lane_id() & 3; }
+template <int NS>
+__device__ __forceinline__ void quad_rows_to_mfma(Frag<uint16_t> (&f)[NS]) {
+  const int lane = lane_id();
+  const int src = ((lane & 15) * 4 + (lane >> 4)) * 4;  // byte address of the source lane
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    f[s].u.x = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)f[s].u.x);
+    f[s].u.y = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)f[s].u.y);
+    f[s].u.z = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)f[s].u.z);
+    f[s].u.w = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)f[s].u.w);
+  }
+}
+
 // fp16 operands held in Frag<uint16_t> bit patterns (routing planes and scaled queries).
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ void mma_f16(f32x4& acc, const Frag<uint16_t>& a, const Frag<uint16_t>& b) {

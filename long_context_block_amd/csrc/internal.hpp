@@ -51,20 +51,23 @@ hipError_t launch_route_planes(const float* mean, long long heads, long long row
                                int* hexp, uint16_t* hilo, float* bound, hipStream_t st);
 
 // Bucket (unit, slot) pairs by node: node lists [U, K] (-1 = none) -> pairs sorted by
-// (b*Hkv + r, node), packed as (unit << 5) | slot. counts/offsets have n_buckets (+1) entries.
+// (b*Hkv + r, node), packed as (unit << 5) | slot. counts/offsets have n_buckets (+1) entries. With
+// ranks_to_positions, ranks[u * K + slot] ends as the pair's index in the sorted list.
 hipError_t launch_regroup(const int* nodes, long long U, int K, int N, int buckets_per_head, int n_heads,
-                          int chunk_log2, int* counts, int* offsets, int* ranks, uint32_t* pairs, hipStream_t st);
+                          int chunk_log2, int* counts, int* offsets, int* ranks, bool ranks_to_positions,
+                          uint32_t* pairs, hipStream_t st);
 
 hipError_t launch_leaf_lse(const SelDims& sd, const void* q, const void* k, const int* kept, const uint32_t* pairs,
                            const int* total, float* leaf_lse, hipStream_t st);
 hipError_t launch_finalize(const SelDims& sd, const int* kept, const float* leaf_lse, int* sel, float* sel_lse,
                            hipStream_t st);
 
-// Attention over selected leaves.
+// Attention over selected leaves. The partial rows of sorted pair x are part[(x G + h) D ..] and
+// part_lse[x G + h]; pos[u K + slot] is the sorted index of the pair (u, slot).
 hipError_t launch_attn_leaf(const SelDims& sd, const void* q, const void* k, const void* v, const int* sel,
                             const uint32_t* pairs, const int* total, void* part, float* part_lse, hipStream_t st);
-hipError_t launch_attn_merge(const SelDims& sd, const int* sel, const void* part, const float* part_lse, void* o,
-                             float* o_lse, hipStream_t st);
+hipError_t launch_attn_merge(const SelDims& sd, const int* sel, const int* pos, const void* part,
+                             const float* part_lse, void* o, float* o_lse, hipStream_t st);
 
 // Flat block selection.
 hipError_t launch_bsa(const SelDims& sd, const void* q, const float* leaf_mean, const uint16_t* leaf_hilo, int* sel,

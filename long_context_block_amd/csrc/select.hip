@@ -538,22 +538,32 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ coun
   if (threadIdx.x == 1023) offsets[n] = (int)s_part[1023];
 }
 
+// With to_positions, ranks[x] is replaced by the pair's index in the sorted list (its row in the
+// leaf-major attention's partial outputs); entries that are not attended get 0, an index that exists,
+// so a reader that trusts a malformed selection still stays inside the partial buffer.
 __global__ __launch_bounds__(256) void scatter_kernel(const int* __restrict__ nodes, long long n_pairs, int K, int N,
                                                       int nb, int chunk_log2, const int* __restrict__ offsets,
-                                                      const int* __restrict__ ranks, uint32_t* __restrict__ pairs) {
+                                                      int* __restrict__ ranks, int to_positions,
+                                                      uint32_t* __restrict__ pairs) {
   const int nch = (int)(((long long)N + (1LL << chunk_log2) - 1) >> chunk_log2);
   for (long long x = (long long)blockIdx.x * blockDim.x + threadIdx.x; x < n_pairs; x += (long long)gridDim.x * blockDim.x) {
     const int nd = nodes[x];
-    if (nd < 0 || nd >= nb) continue;  // out-of-range entries are not attended
+    if (nd < 0 || nd >= nb) {  // out-of-range entries are not attended
+      if (to_positions) ranks[x] = 0;
+      continue;
+    }
     const long long u = x / K;
     const int slot = (int)(x % K);
     const long long bh = u / N, i = u % N;
-    pairs[offsets[(bh * nch + (i >> chunk_log2)) * nb + nd] + ranks[x]] = (uint32_t)((u << 5) | slot);
+    const int at = offsets[(bh * nch + (i >> chunk_log2)) * nb + nd] + ranks[x];
+    pairs[at] = (uint32_t)((u << 5) | slot);
+    if (to_positions) ranks[x] = at;
   }
 }
 
 hipError_t launch_regroup(const int* nodes, long long U, int K, int N, int nb, int n_heads, int chunk_log2,
-                          int* counts, int* offsets, int* ranks, uint32_t* pairs, hipStream_t st) {
+                          int* counts, int* offsets, int* ranks, bool ranks_to_positions, uint32_t* pairs,
+                          hipStream_t st) {
   const int nch = (int)(((long long)N + (1LL << chunk_log2) - 1) >> chunk_log2);
   const long long NB = (long long)nb * nch * n_heads;
   long long zb = (NB + 255) / 256;
@@ -567,7 +577,7 @@ hipError_t launch_regroup(const int* nodes, long long U, int K, int N, int nb, i
   const long long n_pairs = U * K;
   long long sb = (n_pairs + 255) / 256;
   hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)(sb < 65536 ? sb : 65536)), dim3(256), 0, st, nodes, n_pairs, K, N,
-                     nb, chunk_log2, offsets, ranks, pairs);
+                     nb, chunk_log2, offsets, ranks, ranks_to_positions ? 1 : 0, pairs);
   return hipGetLastError();
 }
 
