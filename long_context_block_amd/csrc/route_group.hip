@@ -119,10 +119,12 @@ __global__ __launch_bounds__(kGroupWaves * 64) void route_group_kernel(GroupRout
       bool any_scored = false;
 #pragma unroll
       for (int x = 0; x < UG; ++x) {
+        // wave-uniform values (every lane reads the same LDS word), made scalar for uniform branches
         const int e_l = (ix[x] >> (LOG2C + l)) + 1, ec = (ix[x] >> (LOG2C + l - 1)) + 1;
-        const int klast = s_kept[wave][cur][x][nk[x] - 1];
+        const int klast = __builtin_amdgcn_readfirstlane(s_kept[wave][cur][x][nk[x] - 1]);
         n_cand[x] = 2 * nk[x] - (2 * klast + 1 >= e_l ? 1 : 0);
-        const int cn_last = 2 * s_kept[wave][cur][x][(n_cand[x] - 1) >> 1] + ((n_cand[x] - 1) & 1);
+        const int cn_last =
+            2 * __builtin_amdgcn_readfirstlane(s_kept[wave][cur][x][(n_cand[x] - 1) >> 1]) + ((n_cand[x] - 1) & 1);
         n_full[x] = 2 * cn_last + 1 < ec ? n_cand[x] : n_cand[x] - 1;
         any_scored |= n_cand[x] > K;
       }
@@ -141,29 +143,48 @@ __global__ __launch_bounds__(kGroupWaves * 64) void route_group_kernel(GroupRout
       };
       bool keep[OWN][2];
       if (any_scored) {
-        // ---- pass 1 (hi) for every scored unit; lanes keep their own unit's accumulators
+        // ---- pass 1 (hi) for every scored unit; lanes keep their own unit's accumulators. The level
+        // is LDS-resident or not as a whole: one scalar branch picks the loader.
         f32x4 acc_own[KM];
+        float own_e[OWN][2];
 #pragma unroll
         for (int m = 0; m < KM; ++m) acc_own[m] = zero4();
+        for_level_rows(rows, off, [&](const auto& ld) {
 #pragma unroll
-        for (int x = 0; x < UG; ++x) {
-          if (n_cand[x] <= K) continue;
-          const int mt = (2 * n_cand[x] + 15) >> 4;
+          for (int x = 0; x < UG; ++x) {
+            if (n_cand[x] <= K) continue;
+            // every M-tile is loaded (rows past the unit's candidates read row `off`, and their sums
+            // are never used), so no branch separates the tiles' loads
 #pragma unroll
-          for (int m = 0; m < KM; ++m) {
-            if (m >= mt) break;
-            const int kj = 4 * m + (col >> 2), c = kj * 2 + ((col >> 1) & 1);
-            const bool valid = c < n_cand[x] && ((col & 1) == 0 || c < n_full[x]);
-            const int kn = s_kept[wave][cur][x][kj < nk[x] ? kj : 0];
-            Frag<uint16_t> hi[NS];
-            rows.load_hi(hi, off + (valid ? 4 * kn + (col & 3) : 0), g);
-            f32x4 a = zero4();
+            for (int m = 0; m < KM; ++m) {
+              const int kj = 4 * m + (col >> 2), c = kj * 2 + ((col >> 1) & 1);
+              const bool valid = c < n_cand[x] && ((col & 1) == 0 || c < n_full[x]);
+              const int kn = s_kept[wave][cur][x][kj < nk[x] ? kj : 0];
+              Frag<uint16_t> hi[NS];
+              ld.load_hi(hi, off + (valid ? 4 * kn + (col & 3) : 0), g);
+              f32x4 a = zero4();
 #pragma unroll
-            for (int s = 0; s < NS; ++s) mma_f16(a, hi[s], qh[s]);
-            if (xo == x) acc_own[m] = a;
+              for (int s = 0; s < NS; ++s) mma_f16(a, hi[s], qh[s]);
+              if (xo == x) acc_own[m] = a;
+            }
+            __builtin_amdgcn_sched_barrier(0);  // one unit's rows in flight at a time (register budget)
           }
-          __builtin_amdgcn_sched_barrier(0);  // one unit's rows in flight at a time (register budget)
-        }
+          // the owned candidates' bounds: E = scale * sum_h |q_h| * max over the two children
+#pragma unroll
+          for (int j = 0; j < OWN; ++j)
+#pragma unroll
+            for (int a = 0; a < 2; ++a) {
+              const int m = h + j * G;
+              const int c = 8 * m + 2 * g + a;
+              float e = 0.f;
+              if (m < KM && c < my_nc && my_scored) {
+                const int r0 = off + 2 * cand_node(c);
+                const float n0 = ld.bound(norms, r0), n1 = c < my_nf ? ld.bound(norms, r0 + 1) : 0.f;
+                e = p.scale * qn * fmaxf(n0, n1);
+              }
+              own_e[j][a] = e;
+            }
+        });
         // ---- per-head candidate scores, summed over the unit's heads (strides G/2 .. 1)
         auto head_scores = [&](float (&sc)[KM][2]) {
 #pragma unroll
@@ -180,8 +201,8 @@ __global__ __launch_bounds__(kGroupWaves * 64) void route_group_kernel(GroupRout
         };
         float sc[KM][2];
         head_scores(sc);
-        // ---- owned candidates: hi score, bound, hi Top-K
-        float own_s[OWN][2], own_e[OWN][2];
+        // ---- owned candidates: hi score, hi Top-K
+        float own_s[OWN][2];
         bool own_v[OWN][2], in[OWN][2];
 #pragma unroll
         for (int j = 0; j < OWN; ++j)
@@ -194,13 +215,6 @@ __global__ __launch_bounds__(kGroupWaves * 64) void route_group_kernel(GroupRout
             const int c = 8 * m + 2 * g + a;
             own_v[j][a] = m < KM && c < my_nc;
             own_s[j][a] = s;
-            float e = 0.f;
-            if (own_v[j][a] && my_scored) {
-              const int r0 = off + 2 * cand_node(c);
-              const float n0 = rows.bound(norms, r0), n1 = c < my_nf ? rows.bound(norms, r0 + 1) : 0.f;
-              e = p.scale * qn * fmaxf(n0, n1);
-            }
-            own_e[j][a] = e;
             if (own_v[j][a]) s_key[wave][xo][c] = topk_key(s, c);
           }
         __threadfence_block();
@@ -269,7 +283,7 @@ __global__ __launch_bounds__(kGroupWaves * 64) void route_group_kernel(GroupRout
                                 (8 * m + 2 < n_cand[x] && f0.z) || (8 * m + 3 < n_cand[x] && f0.w) ||
                                 (8 * m + 4 < n_cand[x] && f1.x) || (8 * m + 5 < n_cand[x] && f1.y) ||
                                 (8 * m + 6 < n_cand[x] && f1.z) || (8 * m + 7 < n_cand[x] && f1.w);
-              if (!tile) continue;
+              if (!__builtin_amdgcn_readfirstlane((int)tile)) continue;  // same LDS words for every lane
               const int kj = 4 * m + (col >> 2), c = kj * 2 + ((col >> 1) & 1);
               const bool valid = c < n_cand[x] && ((col & 1) == 0 || c < n_full[x]);
               const bool need = valid && s_key[wave][x][c] != 0u;
@@ -340,7 +354,7 @@ __global__ __launch_bounds__(kGroupWaves * 64) void route_group_kernel(GroupRout
         }
       __threadfence_block();
 #pragma unroll
-      for (int x = 0; x < UG; ++x) nk[x] = __popcll(s_mask[wave][x]);
+      for (int x = 0; x < UG; ++x) nk[x] = __builtin_amdgcn_readfirstlane(__popcll(s_mask[wave][x]));
       cur ^= 1;
     }
     // ---- level-1 kept nodes (ascending), -1 past the count

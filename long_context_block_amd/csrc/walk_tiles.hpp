@@ -39,14 +39,16 @@ struct NodeRows<uint16_t, D> {
   }
   // the row's hi-plane score bound
   __device__ __forceinline__ float bound(const float* norms, int node) const { return norms[node]; }
+  // lo plane of row `node`, zero where !need. `node` must be a valid row either way: the load is
+  // unconditional and its value dropped afterwards, because a load under a lane condition makes the
+  // compiler wait for it before issuing the next one.
   __device__ __forceinline__ void load_lo(Frag<uint16_t> (&lo)[D / 32], int node, int grp, bool need) const {
     const uint16_t* p = base + (unsigned)node * (2 * D) + D + 8 * grp;
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) {
-      if (need)
-        lo[s].load(p + 32 * s);
-      else
-        lo[s].zero();
+      Frag<uint16_t> v;
+      v.load(p + 32 * s);
+      lo[s].u = need ? v.u : make_uint4(0u, 0u, 0u, 0u);
     }
   }
 };
@@ -98,6 +100,43 @@ struct LdsHiRows : NodeRows<uint16_t, D> {
     }
   }
 };
+
+// Level-uniform row access. All rows of one pyramid level are either LDS-resident or not, so the choice
+// is made once per level (a scalar branch) and each path issues plain LDS or plain global loads that can
+// be in flight together; a per-lane choice compiles to flat loads, each waited for before its MFMA.
+template <int D>
+struct GlobalHiLoader {
+  const NodeRows<uint16_t, D>* rows;
+  __device__ __forceinline__ void load_hi(Frag<uint16_t> (&hi)[D / 32], int node, int grp) const {
+    rows->load_hi(hi, node, grp);
+  }
+  __device__ __forceinline__ float bound(const float* norms, int node) const { return norms[node]; }
+};
+template <int D>
+struct LdsHiLoader {
+  const uint16_t* lds;
+  const float* lds_bound;
+  int first;
+  __device__ __forceinline__ void load_hi(Frag<uint16_t> (&hi)[D / 32], int node, int grp) const {
+    const int r = node - first;
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s)
+      hi[s].u = *reinterpret_cast<const uint4*>(lds + r * D + 8 * ((4 * s + grp) ^ (r & (D / 8 - 1))));
+  }
+  __device__ __forceinline__ float bound(const float*, int node) const { return lds_bound[node - first]; }
+};
+// f(loader) for the level whose rows start at level_off (wave-uniform)
+template <int D, class F>
+__device__ __forceinline__ void for_level_rows(const NodeRows<uint16_t, D>& rows, int, F&& f) {
+  f(GlobalHiLoader<D>{&rows});
+}
+template <int D, class F>
+__device__ __forceinline__ void for_level_rows(const LdsHiRows<D>& rows, int level_off, F&& f) {
+  if (__builtin_amdgcn_readfirstlane(level_off) >= rows.first)
+    f(LdsHiLoader<D>{rows.lds, rows.lds_bound, rows.first});
+  else
+    f(GlobalHiLoader<D>{&rows});
+}
 
 // Cooperative copy of the hi planes of pyramid rows [first, first + n) into lds (layout above) and of
 // their bounds into lds_bound.
@@ -235,15 +274,10 @@ __device__ bool select_level_refine(const Rows& rows, const float* norms, int le
                                     int e_child, int G, float scale, float col_scale, int K, float* s_sc,
                                     uint32_t* keys) {
   const int lane = lane_id(), r16 = lane & 15, grp = lane >> 4;
+  n_cand = __builtin_amdgcn_readfirstlane(n_cand);
   const int MT = (2 * n_cand + 15) >> 4;
   const bool last_two = 2 * readlane(cn, n_cand - 1) + 1 < e_child;
   const int n_full = last_two ? n_cand : n_cand - 1;
-  // the candidates' child-row bounds, requested ahead of the row loads
-  float nb0 = 0.f, nb1 = 0.f;
-  if (lane < n_cand) {
-    nb0 = rows.bound(norms, level_off + 2 * cn);
-    nb1 = lane < n_full ? rows.bound(norms, level_off + 2 * cn + 1) : 0.f;
-  }
   int child[KM];
   bool valid[KM];
 #pragma unroll
@@ -254,18 +288,25 @@ __device__ bool select_level_refine(const Rows& rows, const float* norms, int le
     valid[m] = cidx < n_cand && ((row & 1) == 0 || cidx < n_full);
     child[m] = valid[m] ? 2 * cnode + (row & 1) : 0;
   }
-  // pass 1: hi plane
+  // pass 1: hi plane, after the candidates' child-row bounds are requested
   f32x4 acc[KM];
+  float nb0 = 0.f, nb1 = 0.f;
+  for_level_rows(rows, level_off, [&](const auto& ld) {
+    if (lane < n_cand) {
+      nb0 = ld.bound(norms, level_off + 2 * cn);
+      nb1 = lane < n_full ? ld.bound(norms, level_off + 2 * cn + 1) : 0.f;
+    }
+    // every M-tile is loaded (invalid rows read row level_off; tiles past MT are never scored), so no
+    // branch separates the tiles' loads
 #pragma unroll
-  for (int m = 0; m < KM; ++m) {
-    if (m < MT) {
+    for (int m = 0; m < KM; ++m) {
       Frag<uint16_t> hi[D / 32];
-      rows.load_hi(hi, level_off + child[m], grp);
+      ld.load_hi(hi, level_off + child[m], grp);
       acc[m] = zero4();
 #pragma unroll
       for (int s = 0; s < D / 32; ++s) mma_f16(acc[m], hi[s], qf[s]);
     }
-  }
+  });
   auto cand_scores = [&](int m, unsigned long long only) {
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
@@ -297,7 +338,7 @@ __device__ bool select_level_refine(const Rows& rows, const float* norms, int le
       const int cidx = (16 * m + r16) >> 1;
       const bool need = valid[m] && ((rmask >> cidx) & 1ull);
       Frag<uint16_t> lo[D / 32];
-      rows.load_lo(lo, level_off + child[m], grp, need);
+      rows.load_lo(lo, level_off + (need ? child[m] : 0), grp, need);
 #pragma unroll
       for (int s = 0; s < D / 32; ++s) mma_f16(acc[m], lo[s], qf[s]);
       cand_scores(m, rmask);
