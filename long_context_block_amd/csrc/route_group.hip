@@ -218,22 +218,38 @@ __global__ __launch_bounds__(kGroupWaves * 64) void route_group_kernel(GroupRout
             if (own_v[j][a]) s_key[wave][xo][c] = topk_key(s, c);
           }
         __threadfence_block();
-        auto rank_of = [&](uint32_t key) {
-          int rank = 0;
+        // in-flags of the owned candidates (fewer than K of the unit's keys above theirs), all owned
+        // keys ranked in one pass over the unit's keys in LDS
+        auto owned_in = [&]() {
+          uint32_t key[OWN][2];
+          int rank[OWN][2];
+#pragma unroll
+          for (int j = 0; j < OWN; ++j)
+#pragma unroll
+            for (int a = 0; a < 2; ++a) {
+              key[j][a] = topk_key(own_s[j][a], 8 * (h + j * G) + 2 * g + a);
+              rank[j][a] = 0;
+            }
           for (int c = 0; c < my_nc; c += 4) {
             const uint4 v = *reinterpret_cast<const uint4*>(&s_key[wave][xo][c]);
-            rank += (v.x > key) + (c + 1 < my_nc && v.y > key) + (c + 2 < my_nc && v.z > key) +
-                    (c + 3 < my_nc && v.w > key);
+#pragma unroll
+            for (int j = 0; j < OWN; ++j)
+#pragma unroll
+              for (int a = 0; a < 2; ++a)
+                rank[j][a] += (v.x > key[j][a]) + (c + 1 < my_nc && v.y > key[j][a]) +
+                              (c + 2 < my_nc && v.z > key[j][a]) + (c + 3 < my_nc && v.w > key[j][a]);
           }
-          return rank;
+#pragma unroll
+          for (int j = 0; j < OWN; ++j)
+#pragma unroll
+            for (int a = 0; a < 2; ++a) in[j][a] = own_v[j][a] && rank[j][a] < K;
         };
+        owned_in();
         float u_out = kNegInf, l_in = -kNegInf;
 #pragma unroll
         for (int j = 0; j < OWN; ++j)
 #pragma unroll
           for (int a = 0; a < 2; ++a) {
-            const int c = 8 * (h + j * G) + 2 * g + a;
-            in[j][a] = own_v[j][a] && rank_of(topk_key(own_s[j][a], c)) < K;
             if (own_v[j][a] && !in[j][a]) u_out = fmaxf(u_out, own_s[j][a] + own_e[j][a]);
             if (in[j][a]) l_in = fminf(l_in, own_s[j][a] - own_e[j][a]);
           }
@@ -246,47 +262,33 @@ __global__ __launch_bounds__(kGroupWaves * 64) void route_group_kernel(GroupRout
         u_out = colgroup_max(u_out);
         l_in = -colgroup_max(-l_in);
         bool refine[OWN][2];
-        bool any_ref = false;
+        unsigned long long rb[OWN][2];  // wave-uniform: bit (x G + h) + 16 g = owner lane's flag
+        unsigned long long ref_lanes = 0ull;
 #pragma unroll
         for (int j = 0; j < OWN; ++j)
 #pragma unroll
           for (int a = 0; a < 2; ++a) {
             const float lo_b = own_s[j][a] - own_e[j][a], hi_b = own_s[j][a] + own_e[j][a];
             refine[j][a] = my_scored && own_v[j][a] && ((in[j][a] && lo_b <= u_out) || (!in[j][a] && hi_b >= l_in));
-            any_ref |= refine[j][a];
+            rb[j][a] = __ballot(refine[j][a]);
+            ref_lanes |= rb[j][a];
           }
-        const unsigned long long ref_lanes = __ballot(any_ref);
         if (ref_lanes) {
           // ---- pass 2 (lo) on the M-tiles holding undecided candidates; a row is read only if its
-          // candidate is undecided. The owners publish the flags in their key slots.
-#pragma unroll
-          for (int j = 0; j < OWN; ++j)
-#pragma unroll
-            for (int a = 0; a < 2; ++a) {
-              const int c = 8 * (h + j * G) + 2 * g + a;
-              if (own_v[j][a]) s_key[wave][xo][c] = refine[j][a] ? 1u : 0u;
-            }
-          __threadfence_block();
+          // candidate is undecided. Candidate 8 m + 2 g' + a of unit x is owned by lane
+          // (x G + m mod G) + 16 g' with flag set (m / G, a), so the tile and row flags come from the
+          // owners' ballots.
 #pragma unroll
           for (int x = 0; x < UG; ++x) {
-            // lanes of unit x: columns xG .. xG+G-1 in every lane group
-            const unsigned long long xl = (((1ull << G) - 1) << (x * G)) * 0x0001000100010001ull;
-            if (n_cand[x] <= K || !(ref_lanes & xl)) continue;
-            const int mt = (2 * n_cand[x] + 15) >> 4;
 #pragma unroll
             for (int m = 0; m < KM; ++m) {
-              if (m >= mt) break;
-              // the M-tile's 8 candidates: skip it when none is undecided (uniform)
-              const uint4 f0 = *reinterpret_cast<const uint4*>(&s_key[wave][x][8 * m]);
-              const uint4 f1 = *reinterpret_cast<const uint4*>(&s_key[wave][x][8 * m + 4]);
-              const bool tile = (8 * m + 0 < n_cand[x] && f0.x) || (8 * m + 1 < n_cand[x] && f0.y) ||
-                                (8 * m + 2 < n_cand[x] && f0.z) || (8 * m + 3 < n_cand[x] && f0.w) ||
-                                (8 * m + 4 < n_cand[x] && f1.x) || (8 * m + 5 < n_cand[x] && f1.y) ||
-                                (8 * m + 6 < n_cand[x] && f1.z) || (8 * m + 7 < n_cand[x] && f1.w);
-              if (!__builtin_amdgcn_readfirstlane((int)tile)) continue;  // same LDS words for every lane
+              const int oc = x * G + (m % G);
+              const unsigned long long tm = (rb[m / G][0] | rb[m / G][1]) & (0x0001000100010001ull << oc);
+              if (!tm) continue;
               const int kj = 4 * m + (col >> 2), c = kj * 2 + ((col >> 1) & 1);
               const bool valid = c < n_cand[x] && ((col & 1) == 0 || c < n_full[x]);
-              const bool need = valid && s_key[wave][x][c] != 0u;
+              const unsigned long long fr = ((col >> 1) & 1) ? rb[m / G][1] : rb[m / G][0];
+              const bool need = valid && ((fr >> (oc + 16 * (col >> 2))) & 1ull);
               const int kn = s_kept[wave][cur][x][kj < nk[x] ? kj : 0];
               Frag<uint16_t> lo[NS];
               rows.load_lo(lo, off + (need ? 4 * kn + (col & 3) : 0), g, need);
@@ -312,13 +314,7 @@ __global__ __launch_bounds__(kGroupWaves * 64) void route_group_kernel(GroupRout
               if (own_v[j][a]) s_key[wave][xo][c] = topk_key(own_s[j][a], c);
             }
           __threadfence_block();
-#pragma unroll
-          for (int j = 0; j < OWN; ++j)
-#pragma unroll
-            for (int a = 0; a < 2; ++a) {
-              const int c = 8 * (h + j * G) + 2 * g + a;
-              in[j][a] = own_v[j][a] && rank_of(topk_key(own_s[j][a], c)) < K;
-            }
+          owned_in();
         }
 #pragma unroll
         for (int j = 0; j < OWN; ++j)
