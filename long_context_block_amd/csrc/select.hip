@@ -46,18 +46,14 @@ struct RouteParams {
 
 // Top-K of the leaf candidates and the outputs. Lane c < n_cand is candidate c = 2*slot + bit
 // (leaf 2*kept[slot] + bit); ell(c, h) gives its per-head LSE. The heads are summed in index order.
+// sc: this lane's head-summed score (used when n_cand > K).
 template <typename F>
-__device__ __forceinline__ void leaf_topk_write(int n_cand, int leaf_c, int G, int K, long long u, long long qrow0,
-                                                long long qstride, F ell, int* sel, float* sel_lse, uint32_t* keys) {
+__device__ __forceinline__ void leaf_topk_write_sc(int n_cand, int leaf_c, float sc, int G, int K, long long u,
+                                                   long long qrow0, long long qstride, F ell, int* sel,
+                                                   float* sel_lse, uint32_t* keys) {
   const int lane = lane_id();
-  const bool need_rank = n_cand > K;
   bool keep = lane < n_cand;
-  if (need_rank) {
-    float sc = 0.f;
-    if (lane < n_cand)
-      for (int h = 0; h < G; ++h) sc += ell(lane, h);
-    keep = topk_keep(sc, n_cand, K, keys);
-  }
+  if (n_cand > K) keep = topk_keep(sc, n_cand, K, keys);
   int nsel;
   const int leaf_sel = compact_lanes(keep, leaf_c, &nsel);
   const int c_sel = compact_lanes(keep, lane, &nsel);
@@ -67,6 +63,15 @@ __device__ __forceinline__ void leaf_topk_write(int n_cand, int leaf_c, int G, i
       for (int h = 0; h < G; ++h) sel_lse[(qrow0 + h * qstride) * K + lane] = lane < nsel ? ell(c_sel, h) : kNegInf;
     }
   }
+}
+
+template <typename F>
+__device__ __forceinline__ void leaf_topk_write(int n_cand, int leaf_c, int G, int K, long long u, long long qrow0,
+                                                long long qstride, F ell, int* sel, float* sel_lse, uint32_t* keys) {
+  float sc = 0.f;
+  if (n_cand > K && lane_id() < n_cand)
+    for (int h = 0; h < G; ++h) sc += ell(lane_id(), h);
+  leaf_topk_write_sc(n_cand, leaf_c, sc, G, K, u, qrow0, qstride, ell, sel, sel_lse, keys);
 }
 
 template <typename T, int D, int C, bool FUSED, int KM>
@@ -444,26 +449,44 @@ struct FinParams {
   float* sel_lse;
 };
 
+// A wave finalizes kFinUnits consecutive units. Every unit's kept slots and its candidates' head-summed
+// leaf LSEs are requested before any Top-K, so the wave waits for memory once. Candidate lanes past a
+// unit's count read values that the Top-K ignores.
+constexpr int kFinUnits = 4;
+
 __global__ __launch_bounds__(256) void finalize_kernel(FinParams<float> p) {
   __shared__ __align__(16) uint32_t s_key[4][64];
-  const int lane = lane_id(), wave = threadIdx.x >> 6;
-  const long long U = (long long)p.B * p.Hkv * p.N;
-  const long long first = ((long long)xcd_logical_block(gridDim.x) * 4 + wave) * p.upw;
-  for (int it = 0; it < p.upw; ++it) {
-    const long long u = first + it;
+  // unit indices fit in 32 bits (packed pairs hold them in 27), and every index here is wave-uniform
+  const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const unsigned U = (unsigned)p.B * p.Hkv * p.N;
+  const unsigned first = ((unsigned)xcd_logical_block(gridDim.x) * 4 + wave) * kFinUnits;
+  const int slot = lane >> 1;
+  const bool cand_lane = slot < p.K;
+  int kp[kFinUnits];
+  float sc[kFinUnits];
+#pragma unroll
+  for (int it = 0; it < kFinUnits; ++it) {
+    const unsigned u = first + it < U ? first + it : U - 1;
+    kp[it] = cand_lane ? p.kept[(long long)u * p.K + slot] : -1;
+    const float* ll = p.leaf_lse + ((long long)u * p.K * 2 + (cand_lane ? lane : 0)) * p.G;
+    float x = 0.f;
+    for (int h = 0; h < p.G; ++h) x += ll[h];  // heads in index order
+    sc[it] = x;
+  }
+#pragma unroll
+  for (int it = 0; it < kFinUnits; ++it) {
+    const unsigned u = first + it;
     if (u >= U) break;
-    const long long bh = u / p.N, i = u % p.N;
-    const int b = (int)(bh / p.Hkv), r = (int)(bh % p.Hkv);
-    const int slot = lane >> 1;
-    const int kp = slot < p.K ? p.kept[u * p.K + slot] : -1;
-    const int leaf_c = 2 * kp + (lane & 1);
-    const bool valid = kp >= 0 && (long long)leaf_c * p.C <= i;
+    const unsigned bh = u / (unsigned)p.N, i = u - bh * (unsigned)p.N;
+    const int b = (int)(bh / (unsigned)p.Hkv), r = (int)(bh - (unsigned)b * p.Hkv);
+    const int leaf_c = 2 * kp[it] + (lane & 1);
+    const bool valid = kp[it] >= 0 && (long long)leaf_c * p.C <= (long long)i;
     const int n_cand = __popcll(__ballot(valid));
     const long long qrow0 = ((long long)b * p.Hq + (long long)r * p.G) * p.N + i;
     const float* ll = p.leaf_lse + u * p.K * 2 * p.G;
-    leaf_topk_write(
-        n_cand, leaf_c, p.G, p.K, u, qrow0, p.N, [&](int c, int h) { return ll[c * p.G + h]; }, p.sel, p.sel_lse,
-        s_key[wave]);
+    leaf_topk_write_sc(
+        n_cand, leaf_c, sc[it], p.G, p.K, u, qrow0, p.N, [&](int c, int h) { return ll[c * p.G + h]; }, p.sel,
+        p.sel_lse, s_key[wave]);
   }
 }
 
@@ -477,7 +500,7 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(int* x, long long n) {
 
 constexpr int kRegroupUnits = 1024;
 
-__global__ __launch_bounds__(256) void hist_kernel(const int* __restrict__ nodes, int K, int N, int nb, int chunks,
+__global__ __launch_bounds__(1024) void hist_kernel(const int* __restrict__ nodes, int K, int N, int nb, int chunks,
                                                    int chunk_log2, int use_lds, int* __restrict__ counts,
                                                    int* __restrict__ ranks) {
   extern __shared__ int lc[];  // nb local counts, then nb bases
@@ -571,7 +594,7 @@ hipError_t launch_regroup(const int* nodes, long long U, int K, int N, int nb, i
   const int chunks = (N + kRegroupUnits - 1) / kRegroupUnits;
   const int use_lds = nb <= 8192;  // 2*nb ints of LDS, at most 64 KiB
   const size_t lds = use_lds ? (size_t)nb * 2 * sizeof(int) : 0;
-  hipLaunchKernelGGL(hist_kernel, dim3(n_heads * chunks), dim3(256), lds, st, nodes, K, N, nb, chunks, chunk_log2,
+  hipLaunchKernelGGL(hist_kernel, dim3(n_heads * chunks), dim3(1024), lds, st, nodes, K, N, nb, chunks, chunk_log2,
                      use_lds, counts, ranks);
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, counts, NB, offsets);
   const long long n_pairs = U * K;
@@ -712,11 +735,11 @@ hipError_t launch_finalize(const SelDims& sd, const int* kept, const float* leaf
   p.N = sd.N;
   p.K = sd.K;
   p.C = sd.C;
-  p.upw = 4;
+  p.upw = kFinUnits;
   p.sel = sel;
   p.sel_lse = sel_lse;
   const long long U = (long long)sd.B * sd.Hkv * sd.N;
-  const long long waves = (U + p.upw - 1) / p.upw;
+  const long long waves = (U + kFinUnits - 1) / kFinUnits;
   hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, p);
   return hipGetLastError();
 }
