@@ -297,7 +297,8 @@ def main():
         "bsa_select": ("mfma", w["bsa_flops"], st_ms.get("bsa_select", 0.0)),
         "pyramid": ("hbm", w["pyramid_read_bytes"], st_ms.get("pyramid", 0.0)),
     }
-    dom = max(kern, key=lambda n: kern[n][2])
+    # the dominant kernel of the PISA path; the flat selection is the comparison baseline (listed below)
+    dom = max((n for n in kern if n != "bsa_select"), key=lambda n: kern[n][2])
     bound, amount, ms = kern[dom]
     traffic = measured_traffic(args.workload)
     if bound == "hbm":
