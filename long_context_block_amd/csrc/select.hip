@@ -469,8 +469,19 @@ __global__ __launch_bounds__(256) void finalize_kernel(FinParams<float> p) {
     const unsigned u = first + it < U ? first + it : U - 1;
     kp[it] = cand_lane ? p.kept[(long long)u * p.K + slot] : -1;
     const float* ll = p.leaf_lse + ((long long)u * p.K * 2 + (cand_lane ? lane : 0)) * p.G;
-    float x = 0.f;
-    for (int h = 0; h < p.G; ++h) x += ll[h];  // heads in index order
+    float x = 0.f;  // heads in index order
+    if ((p.G & 3) == 0) {
+      // 16-byte loads (the rows are 16-byte aligned): a lane quad reads 64 contiguous bytes
+      for (int h = 0; h < p.G; h += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(ll + h);
+        x += v.x;
+        x += v.y;
+        x += v.z;
+        x += v.w;
+      }
+    } else {
+      for (int h = 0; h < p.G; ++h) x += ll[h];
+    }
     sc[it] = x;
   }
 #pragma unroll
