@@ -21,6 +21,7 @@ SMALL = {
     "tiny_fp32_k_n0": dict(B=1, Hq=1, Hkv=1, N=1024, d=64, C=32, K=32, dtype="fp32", keys="iid"),
     "fp32_gqa_ragged": dict(B=2, Hq=4, Hkv=2, N=700, d=64, C=32, K=5, dtype="fp32", keys="ar1"),
     "bf16_ragged": dict(B=2, Hq=8, Hkv=2, N=1000, d=128, C=64, K=4, dtype="bf16", keys="ar1"),
+    "bf16_batch2": dict(B=2, Hq=8, Hkv=2, N=1100, d=128, C=64, K=5, dtype="bf16", keys="ar1"),
     "bf16_d64_c32": dict(B=1, Hq=4, Hkv=2, N=777, d=64, C=32, K=6, dtype="bf16", keys="ar1"),
     "bf16_d128_c32": dict(B=1, Hq=4, Hkv=1, N=1500, d=128, C=32, K=8, dtype="bf16", keys="ar1"),
     "bf16_d64_c64": dict(B=1, Hq=2, Hkv=1, N=1300, d=64, C=64, K=3, dtype="bf16", keys="iid"),
