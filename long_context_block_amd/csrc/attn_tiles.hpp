@@ -142,14 +142,24 @@ __device__ __forceinline__ void attend_tile_kv(KFrag kfrag, VFrag vfrag, const F
   float mx = kNegInf;
   const long long lim64 = ic - t0;
   const int lim = lim64 < 0 ? -1 : (lim64 > C ? C : (int)lim64);
+  bool all_visible = false;
+  if constexpr (sizeof(T) == 2) all_visible = __all(lim >= C - 1);
+  if (all_visible) {
+    // bf16: every column sees the whole leaf (the usual case away from the diagonal): no mask (same values)
 #pragma unroll
-  for (int m = 0; m < MS; ++m)
+    for (int m = 0; m < MS; ++m)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float x = attn_token(m, grp, j) <= lim ? sacc[m][j] : kNegInf;
-      sacc[m][j] = x;
-      mx = fmaxf(mx, x);
-    }
+      for (int j = 0; j < 4; ++j) mx = fmaxf(mx, sacc[m][j]);
+  } else {
+#pragma unroll
+    for (int m = 0; m < MS; ++m)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float x = attn_token(m, grp, j) <= lim ? sacc[m][j] : kNegInf;
+        sacc[m][j] = x;
+        mx = fmaxf(mx, x);
+      }
+  }
   mx = colgroup_max(mx);
   const bool any = mx != kNegInf;
   const float ms = any ? mx : 0.f;

@@ -430,15 +430,25 @@ __device__ __forceinline__ void leaf_pair_lse_k(KFrag kfrag, const Frag<T> (&qf)
   // causal mask on offsets within the tile: token t0 + o is visible iff o <= icol - t0
   const long long lim64 = icol - t0;
   const int lim = lim64 < 0 ? -1 : (lim64 > 2 * C ? 2 * C : (int)lim64);
+  // bf16: every column sees all 2C tokens (the usual case away from the diagonal): no mask (same values)
+  bool all_visible = false;
+  if constexpr (sizeof(T) == 2) all_visible = __all(lim >= 2 * C - 1);
 #pragma unroll
   for (int bit = 0; bit < 2; ++bit) {
     float x[ML * 4];
+    if (all_visible) {
 #pragma unroll
-    for (int mm = 0; mm < ML; ++mm) {
+      for (int mm = 0; mm < ML; ++mm)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int o = 16 * (bit * ML + mm) + 4 * grp + j;
-        x[mm * 4 + j] = o <= lim ? acc[bit * ML + mm][j] : kNegInf;
+        for (int j = 0; j < 4; ++j) x[mm * 4 + j] = acc[bit * ML + mm][j];
+    } else {
+#pragma unroll
+      for (int mm = 0; mm < ML; ++mm) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int o = 16 * (bit * ML + mm) + 4 * grp + j;
+          x[mm * 4 + j] = o <= lim ? acc[bit * ML + mm][j] : kNegInf;
+        }
       }
     }
     const float l = column_lse<ML * 4>(x, scale);
