@@ -2,7 +2,7 @@
 // pyramid bullet: leaf blocks of C tokens, mean pooling upward with merge factor 2, O(log N) levels).
 //
 // Stage 1 (pool_subtree): one work-group per (KV head, run of LB = 2048/d leaves). Thread (leaf,
-// 8-column chunk) sums its leaf's C keys in fp32 (token order), then the work-group builds levels
+// 8-column chunk) sums its leaf's C keys in fp32 (four interleaved partial sums), then the work-group builds levels
 // 1..log2(LB) of its subtree in LDS. Stage 2 (pool_upper): one work-group per KV head builds the
 // remaining levels from the stage-1 roots. A parent's mean is the token-weighted mean of its
 // children's means, (c1 m1 + c2 m2) / (c1 + c2), which is the mean of the raw keys in its span; with
@@ -43,17 +43,41 @@ __global__ __launch_bounds__(256) void pool_subtree_kernel(const T* __restrict__
     if (j < lv.n[0]) {
       cnt = node_count(len, 0, j, C);
       const T* src = k + ((long long)bh * N + j * C) * D + ch * 8;
-      for (int t = 0; t < cnt; ++t) {
-        Frag<T> f;
-        f.load(src + (long long)t * D);
+      auto add = [&](float (&a)[8], const Frag<T>& f) {
         if constexpr (sizeof(T) == 2) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[e] += f.get(e);
+          for (int e = 0; e < 8; ++e) a[e] += f.get(e);
         } else {
-          acc[0] += f.a.x; acc[1] += f.a.y; acc[2] += f.a.z; acc[3] += f.a.w;
-          acc[4] += f.b.x; acc[5] += f.b.y; acc[6] += f.b.z; acc[7] += f.b.w;
+          a[0] += f.a.x; a[1] += f.a.y; a[2] += f.a.z; a[3] += f.a.w;
+          a[4] += f.b.x; a[5] += f.b.y; a[6] += f.b.z; a[7] += f.b.w;
         }
+      };
+      // four partial sums over tokens t = 4 u + w (w = 0..3), so four loads are in flight per thread;
+      // combined as (p0 + p1) + (p2 + p3)
+      float part[3][8];
+#pragma unroll
+      for (int w = 0; w < 3; ++w)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part[w][e] = 0.f;
+      const int c4 = cnt & ~3;
+      for (int t = 0; t < c4; t += 4) {
+        Frag<T> f0, f1, f2, f3;
+        f0.load(src + (long long)t * D);
+        f1.load(src + (long long)(t + 1) * D);
+        f2.load(src + (long long)(t + 2) * D);
+        f3.load(src + (long long)(t + 3) * D);
+        add(acc, f0);
+        add(part[0], f1);
+        add(part[1], f2);
+        add(part[2], f3);
       }
+      for (int t = c4; t < cnt; ++t) {
+        Frag<T> f;
+        f.load(src + (long long)t * D);
+        add(acc, f);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = (acc[e] + part[0][e]) + (part[1][e] + part[2][e]);
       const float inv = cnt > 0 ? 1.f / (float)cnt : 0.f;
       float* mrow = mean + (head_row + lv.off[0] + j) * D + ch * 8;
 #pragma unroll
