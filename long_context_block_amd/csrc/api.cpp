@@ -119,6 +119,12 @@ pisa_status make_levels(long long n_tokens, int C, pisa::Levels* lv) {
   }
   lv->n_levels = l;
   lv->nodes = off;
+  long long roff = 0;
+  for (int j = 0; j < l; ++j) {
+    lv->roff[j] = roff;
+    roff += lv->n[j] >= 4 ? (lv->n[j] + 3) / 4 * 4 : lv->n[j];
+  }
+  lv->rnodes = (roff + 3) / 4 * 4;
   return PISA_OK;
 }
 
@@ -200,8 +206,8 @@ size_t carve_select(const Plan& p, void* ws, SelectWs* w) {
   Carver c(ws);
   SelectWs x{};
   if (p.sd.bf16) {
-    x.hilo = (uint16_t*)c.take((size_t)p.BH * p.sd.lv.nodes * 2 * p.sd.D * 2);
-    x.norms = (float*)c.take((size_t)p.BH * p.sd.lv.nodes * 4);
+    x.hilo = (uint16_t*)c.take((size_t)p.BH * p.sd.lv.rnodes * 2 * p.sd.D * 2);
+    x.norms = (float*)c.take((size_t)p.BH * p.sd.lv.rnodes * 4);
     x.hexp = (int*)c.take((size_t)p.BH * 4);
     x.part_max = (float*)c.take((size_t)p.BH * 64 * 4);
   }
@@ -370,7 +376,7 @@ pisa_status pisa_select(const pisa_shape* shape, const void* q, const void* k, c
   if (p.sd.bf16) {
     {
       Stage sc(s, "route_planes");
-      e = pisa::launch_route_planes(pyr_mean, p.BH, p.sd.lv.nodes, p.sd.D, w.part_max, w.hexp, w.hilo, w.norms, s);
+      e = pisa::launch_route_planes(pyr_mean, p.BH, p.sd.lv, p.sd.D, w.part_max, w.hexp, w.hilo, w.norms, s);
     }
     if (e != hipSuccess) return hip_status(e, "route_planes");
     nodes = w.hilo;

@@ -26,6 +26,11 @@ struct Levels {
   int n[kMaxLevels];
   long long off[kMaxLevels];
   long long nodes;  // rows per KV head
+  // Rows of the fp16 routing planes: level l starts at roff[l], and a level of at least 4 nodes takes a
+  // multiple of 4 rows (the tail rows are zero), so the 4 grandchildren 4j .. 4j+3 of a node always
+  // form one aligned group of 4. rnodes (a multiple of 4) = routing rows per KV head.
+  long long roff[kMaxLevels];
+  long long rnodes;
 };
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
@@ -121,6 +126,15 @@ __device__ __forceinline__ void mma_f16(f32x4& acc, const Frag<uint16_t>& a, con
   acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a.u), __builtin_bit_cast(f16x8_t, b.u),
                                                acc, 0, 0, 0);
 }
+// fp16 routing planes, quad-interleaved: routing rows 4a .. 4a+3 form one group of 8 D values, the
+// hi plane (4 D) then the lo plane (4 D); within a plane, 16-byte chunk c of the group's 4 rows is 64
+// contiguous bytes (row 4a + q at element 32 c + 8 q). The four lanes of a quad that read chunk c of
+// the 4 grandchildren of one node thus read one 64-byte segment. Returns the chunk's 8 elements.
+template <typename T>
+__device__ __forceinline__ T* route_plane_chunk(T* head, int R, int plane, int c, int D) {
+  return head + ((unsigned)(R >> 2) * 2u + (unsigned)plane) * (4u * (unsigned)D) + 32 * c + 8 * (R & 3);
+}
+
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) { return __builtin_bit_cast(uint16_t, (_Float16)x); }
 __device__ __forceinline__ float f16_bits_to_f32(uint16_t x) { return (float)__builtin_bit_cast(_Float16, x); }
 

@@ -47,7 +47,7 @@ hipError_t launch_route_group(const SelDims& sd, const void* q, const void* hilo
 // Routing planes of a bf16 pyramid: per KV head an exponent hexp (max |mean| 2^hexp in [2^14, 2^15)),
 // per row the fp16 hi/lo planes of 2^hexp mean and the hi-plane score bound (unscaled units).
 // part_max: 64 floats of scratch per KV head.
-hipError_t launch_route_planes(const float* mean, long long heads, long long rows_per_head, int D, float* part_max,
+hipError_t launch_route_planes(const float* mean, long long heads, const Levels& lv, int D, float* part_max,
                                int* hexp, uint16_t* hilo, float* bound, hipStream_t st);
 
 // Bucket (unit, slot) pairs by node: node lists [U, K] (-1 = none) -> pairs sorted by

@@ -196,12 +196,12 @@ __global__ __launch_bounds__(256) void split_hilo_kernel(const float* __restrict
 }
 
 // Routing planes. Per KV head an exponent e (max |mean| 2^e in [2^14, 2^15), from 64 partial maxima);
-// per row the fp16
-// planes hi = rne(2^e mean), lo = rne(2^e mean - hi) (row r at r*2D: hi[D] then lo[D]), and the
-// hi-plane score bound b = 2^-e (1.05 |lo| + 2^-16 |2^e mean|): for any q, |q . (hi + lo) - q . hi| =
-// |q . lo| <= |q| |lo| (Cauchy-Schwarz); the 2^-16 term covers the fp32 accumulation of the dot
-// products (each order of summation errs by under 2^-17 |q| |2^e mean|) and the 1.05 the rounding of
-// the norms. 2^-e returns b to the units of the unscaled means.
+// per routing row the fp16 planes hi = rne(2^e mean), lo = rne(2^e mean - hi) and the hi-plane score
+// bound b = 2^-e (1.05 |lo| + 2^-16 |2^e mean|): for any q, |q . (hi + lo) - q . hi| = |q . lo| <=
+// |q| |lo| (Cauchy-Schwarz); the 2^-16 term covers the fp32 accumulation of the dot products (each
+// order of summation errs by under 2^-17 |q| |2^e mean|) and the 1.05 the rounding of the norms. 2^-e
+// returns b to the units of the unscaled means. Node (l, j) is routing row roff[l] + j; rows are stored
+// in the quad-interleaved layout of route_plane_chunk (rows past a level's nodes are zero, bound 0).
 // Partial maxima of |mean|: kMaxParts work-groups per KV head, each over a contiguous slice.
 constexpr int kMaxParts = 64;
 __global__ __launch_bounds__(256) void head_max_kernel(const float* __restrict__ mean, long long rows_per_head, int D,
@@ -220,38 +220,46 @@ __global__ __launch_bounds__(256) void head_max_kernel(const float* __restrict__
   if (threadIdx.x == 0) part_max[blockIdx.x] = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
 }
 
-// One wave per row.
-__global__ __launch_bounds__(256) void split_f16_kernel(const float* __restrict__ mean, long long rows,
-                                                       long long rows_per_head, int D,
-                                                       const float* __restrict__ part_max, int* __restrict__ hexp,
-                                                       uint16_t* __restrict__ hilo, float* __restrict__ bound) {
-  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
+// One wave per routing row.
+__global__ __launch_bounds__(256) void split_f16_kernel(const float* __restrict__ mean, long long heads, Levels lv,
+                                                       int D, const float* __restrict__ part_max,
+                                                       int* __restrict__ hexp, uint16_t* __restrict__ hilo,
+                                                       float* __restrict__ bound) {
+  const long long rrow = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (rrow >= heads * lv.rnodes) return;
   const int lane = threadIdx.x & 63;
-  const long long bh = row / rows_per_head;
+  const long long bh = rrow / lv.rnodes;
+  const int R = (int)(rrow - bh * lv.rnodes);
+  // the level holding routing row R, and the node's index in it (past the level's nodes: padding)
+  int l = 0;
+  while (l + 1 < lv.n_levels && R >= lv.roff[l + 1]) ++l;
+  const int j = R - (int)lv.roff[l];
+  const bool node = j < lv.n[l];
   static_assert(kMaxParts == 64, "one partial per lane");
   float mx = part_max[bh * kMaxParts + lane];
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
   const int e = f16_range_exp(mx);
-  if (lane == 0 && row == bh * rows_per_head) hexp[bh] = e;
+  if (lane == 0 && R == 0) hexp[bh] = e;
+  uint16_t* head = hilo + bh * lv.rnodes * 2 * D;
+  const float* mrow = mean + (bh * lv.nodes + lv.off[l] + (node ? j : 0)) * D;
   float sv = 0.f, sl = 0.f;
   for (int c = lane; c < D; c += 64) {
-    const float v = ldexpf(mean[row * D + c], e);
+    const float v = node ? ldexpf(mrow[c], e) : 0.f;
     const uint16_t hb = f32_to_f16_bits(v);
     const uint16_t lb = f32_to_f16_bits(v - f16_bits_to_f32(hb));
-    hilo[row * 2 * D + c] = hb;
-    hilo[row * 2 * D + D + c] = lb;
-    const float l = f16_bits_to_f32(lb);
+    route_plane_chunk<uint16_t>(head, R, 0, c >> 3, D)[c & 7] = hb;
+    route_plane_chunk<uint16_t>(head, R, 1, c >> 3, D)[c & 7] = lb;
+    const float lf = f16_bits_to_f32(lb);
     sv += v * v;
-    sl += l * l;
+    sl += lf * lf;
   }
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     sv += __shfl_xor(sv, o);
     sl += __shfl_xor(sl, o);
   }
-  if (lane == 0) bound[row] = ldexpf(1.05f * sqrtf(sl) + 1.52587890625e-05f * sqrtf(sv), -e);
+  if (lane == 0) bound[rrow] = node ? ldexpf(1.05f * sqrtf(sl) + 1.52587890625e-05f * sqrtf(sv), -e) : 0.f;
 }
 
 // ------------------------------------------------------------------------------------------ host
@@ -282,13 +290,13 @@ hipError_t launch_pool(const void* k, bool bf16, const PyrDims& pd, LensArg lens
   return launch_pool_t<float, 64>((const float*)k, pd, lens, max_level, mean, sum, st);
 }
 
-hipError_t launch_route_planes(const float* mean, long long heads, long long rows_per_head, int D, float* part_max,
+hipError_t launch_route_planes(const float* mean, long long heads, const Levels& lv, int D, float* part_max,
                                int* hexp, uint16_t* hilo, float* bound, hipStream_t st) {
-  hipLaunchKernelGGL(head_max_kernel, dim3((unsigned)(heads * kMaxParts)), dim3(256), 0, st, mean, rows_per_head, D,
+  hipLaunchKernelGGL(head_max_kernel, dim3((unsigned)(heads * kMaxParts)), dim3(256), 0, st, mean, lv.nodes, D,
                      part_max);
-  const long long rows = heads * rows_per_head;
-  hipLaunchKernelGGL(split_f16_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, mean, rows, rows_per_head,
-                     D, part_max, hexp, hilo, bound);
+  const long long rows = heads * lv.rnodes;
+  hipLaunchKernelGGL(split_f16_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, mean, heads, lv, D,
+                     part_max, hexp, hilo, bound);
   return hipGetLastError();
 }
 

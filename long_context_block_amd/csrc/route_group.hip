@@ -26,8 +26,8 @@ constexpr int kGroupLdsBytes = 128 * 1024;
 
 struct GroupRouteParams {
   const uint16_t* q;
-  const uint16_t* hilo;  // [B*Hkv, nodes, 2D] fp16: hi plane then lo plane per row
-  const float* norms;    // per-row hi-plane bound
+  const uint16_t* hilo;  // fp16 routing planes, Levels::rnodes rows per KV head (route_plane_chunk layout)
+  const float* norms;    // per routing row: hi-plane bound
   const int* hexp;       // per KV head: planes hold 2^hexp mean
   int B, Hq, Hkv, N, K;
   float scale;
@@ -54,12 +54,12 @@ __global__ __launch_bounds__(kGroupWaves * 64) void route_group_kernel(GroupRout
   const int bh = blockIdx.x % BH, w = blockIdx.x / BH;
   const int K = p.K;
   LdsHiRows<D> rows;
-  rows.base = p.hilo + (long long)bh * p.lv.nodes * 2 * D;
-  const float* norms = p.norms + (long long)bh * p.lv.nodes;
+  rows.base = p.hilo + (long long)bh * p.lv.rnodes * 2 * D;
+  const float* norms = p.norms + (long long)bh * p.lv.rnodes;
   rows.lds = s_hi;
   rows.lds_bound = s_bound;
   rows.first = lds_first;
-  stage_hi_rows<D>(rows.base, norms, lds_first, (int)(p.lv.nodes - lds_first), s_hi, s_bound);
+  stage_hi_rows<D>(rows.base, norms, lds_first, (int)(p.lv.rnodes - lds_first), s_hi, s_bound);
   __syncthreads();
   const int hexp = p.hexp[bh];
   const int b = bh / p.Hkv, r = bh % p.Hkv;
@@ -114,7 +114,7 @@ __global__ __launch_bounds__(kGroupWaves * 64) void route_group_kernel(GroupRout
     }
     __threadfence_block();
     for (int l = lw; l >= 1; --l) {
-      const int off = (int)p.lv.off[l - 1];
+      const int off = (int)p.lv.roff[l - 1];  // routing row of the child level's node 0
       int n_cand[UG], n_full[UG];
       bool any_scored = false;
 #pragma unroll
@@ -382,14 +382,14 @@ static hipError_t route_group_t(const SelDims& sd, const void* q, const void* hi
   p.kept = kept;
   // LDS-resident upper levels: the smallest level whose rows up to the root fit
   int lcut = 0;
-  while (lcut < sd.lv.n_levels - 1 && (sd.lv.nodes - sd.lv.off[lcut]) * D * 2 > kGroupLdsBytes) ++lcut;
+  while (lcut < sd.lv.n_levels - 1 && (sd.lv.rnodes - sd.lv.roff[lcut]) * D * 2 > kGroupLdsBytes) ++lcut;
   const int BH = sd.B * sd.Hkv;
   const long long groups = (sd.N + 16 / G - 1) / (16 / G);
   long long wph = 256 / BH;  // about one work-group per CU
   if (wph < 1) wph = 1;
   if (wph > (groups + kGroupWaves - 1) / kGroupWaves) wph = (groups + kGroupWaves - 1) / kGroupWaves;
   hipLaunchKernelGGL((route_group_kernel<D, C, G, KM>), dim3((unsigned)(BH * wph)), dim3(kGroupWaves * 64), 0, st, p,
-                     (int)sd.lv.off[lcut], (int)wph);
+                     (int)sd.lv.roff[lcut], (int)wph);
   return hipGetLastError();
 }
 

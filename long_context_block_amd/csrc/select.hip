@@ -101,14 +101,11 @@ __global__ __launch_bounds__(256, FUSED ? 2 : 4) void route_kernel(RouteParams<T
       else
         qf[s].zero();
     }
-    NodeRows<T, D> rows;
-    if constexpr (sizeof(T) == 2)
-      rows.base = (const uint16_t*)p.nodes + bh * p.lv.nodes * 2 * D;
-    else
-      rows.base = (const float*)p.nodes + bh * p.lv.nodes * D;
     int kept;
     int nk;
     if constexpr (sizeof(T) == 2) {
+      RoutePlanes<D> rows;
+      rows.base = (const uint16_t*)p.nodes + bh * p.lv.rnodes * 2 * D;
       // sum over the group's heads of |q_h| (lane r16 = head holds its d/4 elements per lane group)
       float sq = 0.f;
 #pragma unroll
@@ -120,18 +117,19 @@ __global__ __launch_bounds__(256, FUSED ? 2 : 4) void route_kernel(RouteParams<T
         }
       const float sq_all = colgroup_sum(sq);  // every lane takes part in the exchange
       const float qn = row_sum16(hv ? sqrtf(sq_all) : 0.f);
-      const float* norms = p.norms + bh * p.lv.nodes;
+      const float* norms = p.norms + bh * p.lv.rnodes;
       Frag<uint16_t> qh[D / 32];
       const int te = route_q_f16<D>(qf, qh);
       const float col_scale = ldexpf(p.scale, -(te + p.hexp[bh]));
-      nk = walk_to_level1<T, D, KM>(p.lv, kLog2C, p.K, (int)i, &kept, [&](int off, int cn, int n_cand, int e_child) {
-        return select_level_refine<D, KM>(rows, norms, off, qh, qn, cn, n_cand, e_child, p.G, p.scale, col_scale, p.K,
-                                          s_sc[wave],
-                                          s_key[wave]);
+      nk = walk_to_level1<T, D, KM>(p.lv, kLog2C, p.K, (int)i, &kept, [&](int lc, int cn, int n_cand, int e_child) {
+        return select_level_refine<D, KM>(rows, norms, (int)p.lv.roff[lc], qh, qn, cn, n_cand, e_child, p.G, p.scale,
+                                          col_scale, p.K, s_sc[wave], s_key[wave]);
       });
     } else {
-      nk = walk_to_level1<T, D, KM>(p.lv, kLog2C, p.K, (int)i, &kept, [&](int off, int cn, int n_cand, int e_child) {
-        score_candidates<T, D, KM>(rows, off, qf, cn, n_cand, e_child, p.G, p.scale, s_sc[wave]);
+      NodeRows<T, D> rows;
+      rows.base = (const float*)p.nodes + bh * p.lv.nodes * D;
+      nk = walk_to_level1<T, D, KM>(p.lv, kLog2C, p.K, (int)i, &kept, [&](int lc, int cn, int n_cand, int e_child) {
+        score_candidates<T, D, KM>(rows, (int)p.lv.off[lc], qf, cn, n_cand, e_child, p.G, p.scale, s_sc[wave]);
         return topk_keep_lds(s_sc[wave], n_cand, p.K, s_key[wave]);
       });
     }
@@ -187,12 +185,12 @@ __global__ __launch_bounds__(1024) void route_lds_kernel(RouteParams<uint16_t> p
   const int BH = p.B * p.Hkv;
   const int bh = blockIdx.x % BH, w = blockIdx.x / BH;  // consecutive work-groups: different heads
   LdsHiRows<D> rows;
-  rows.base = (const uint16_t*)p.nodes + (long long)bh * p.lv.nodes * 2 * D;
-  const float* norms = p.norms + (long long)bh * p.lv.nodes;
+  rows.base = (const uint16_t*)p.nodes + (long long)bh * p.lv.rnodes * 2 * D;
+  const float* norms = p.norms + (long long)bh * p.lv.rnodes;
   rows.lds = s_hi;
   rows.lds_bound = s_bound;
   rows.first = lds_first;
-  stage_hi_rows<D>(rows.base, norms, lds_first, (int)(p.lv.nodes - lds_first), s_hi, s_bound);
+  stage_hi_rows<D>(rows.base, norms, lds_first, (int)(p.lv.rnodes - lds_first), s_hi, s_bound);
   __syncthreads();
   const int hexp = p.hexp[bh];
   const int b = bh / p.Hkv, r = bh % p.Hkv;
@@ -228,9 +226,9 @@ __global__ __launch_bounds__(1024) void route_lds_kernel(RouteParams<uint16_t> p
       const float col_scale = ldexpf(p.scale, -(te + hexp));
       int kept;
       const int nk =
-          walk_to_level1<uint16_t, D, KM>(p.lv, kLog2C, p.K, i, &kept, [&](int off, int cn, int n_cand, int e_child) {
-            return select_level_refine<D, KM>(rows, norms, off, qh, qn, cn, n_cand, e_child, p.G, p.scale, col_scale,
-                                              p.K, s_sc[wave], s_key[wave]);
+          walk_to_level1<uint16_t, D, KM>(p.lv, kLog2C, p.K, i, &kept, [&](int lc, int cn, int n_cand, int e_child) {
+            return select_level_refine<D, KM>(rows, norms, (int)p.lv.roff[lc], qh, qn, cn, n_cand, e_child, p.G,
+                                              p.scale, col_scale, p.K, s_sc[wave], s_key[wave]);
           });
       if (lane < p.K) p.kept[u * p.K + lane] = lane < nk ? kept : -1;
     }
@@ -640,8 +638,8 @@ static hipError_t route_t(const SelDims& sd, const void* q, const void* k, const
   if constexpr (sizeof(T) == 2 && !FUSED) {
     // LDS-resident upper levels: the smallest level whose rows up to the root fit in kRouteLdsBytes
     int lcut = 0;
-    while (lcut < sd.lv.n_levels - 1 && (sd.lv.nodes - sd.lv.off[lcut]) * D * 2 > kRouteLdsBytes) ++lcut;
-    const int lds_first = (int)sd.lv.off[lcut];
+    while (lcut < sd.lv.n_levels - 1 && (sd.lv.rnodes - sd.lv.roff[lcut]) * D * 2 > kRouteLdsBytes) ++lcut;
+    const int lds_first = (int)sd.lv.roff[lcut];
     const int BH = sd.B * sd.Hkv;
     const long long groups = (sd.N + kRouteUnits - 1) / kRouteUnits;
     long long wph = 256 / BH;  // about one work-group per CU

@@ -31,23 +31,28 @@ struct NodeRows<uint16_t, D> {
       mma(acc, f.lo[s], qf[s]);
     }
   }
-  // hi or lo plane of row `node` alone (the two passes of the routing walk over the fp16 planes)
-  __device__ __forceinline__ void load_hi(Frag<uint16_t> (&hi)[D / 32], int node, int grp) const {
-    const uint16_t* p = base + (unsigned)node * (2 * D) + 8 * grp;
+};
+
+// fp16 routing planes of one KV head (hi = rne(2^hexp mean), lo = rne(2^hexp mean - hi)), addressed by
+// routing row (Levels::roff) in the quad-interleaved layout of route_plane_chunk.
+template <int D>
+struct RoutePlanes {
+  const uint16_t* base;  // the KV head's planes
+  // hi plane of routing row R (the first pass of the routing walk)
+  __device__ __forceinline__ void load_hi(Frag<uint16_t> (&hi)[D / 32], int R, int grp) const {
 #pragma unroll
-    for (int s = 0; s < D / 32; ++s) hi[s].load(p + 32 * s);
+    for (int s = 0; s < D / 32; ++s) hi[s].load(route_plane_chunk(base, R, 0, 4 * s + grp, D));
   }
   // the row's hi-plane score bound
-  __device__ __forceinline__ float bound(const float* norms, int node) const { return norms[node]; }
-  // lo plane of row `node`, zero where !need. `node` must be a valid row either way: the load is
+  __device__ __forceinline__ float bound(const float* norms, int R) const { return norms[R]; }
+  // lo plane of routing row R, zero where !need. R must be a valid row either way: the load is
   // unconditional and its value dropped afterwards, because a load under a lane condition makes the
   // compiler wait for it before issuing the next one.
-  __device__ __forceinline__ void load_lo(Frag<uint16_t> (&lo)[D / 32], int node, int grp, bool need) const {
-    const uint16_t* p = base + (unsigned)node * (2 * D) + D + 8 * grp;
+  __device__ __forceinline__ void load_lo(Frag<uint16_t> (&lo)[D / 32], int R, int grp, bool need) const {
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) {
       Frag<uint16_t> v;
-      v.load(p + 32 * s);
+      v.load(route_plane_chunk(base, R, 1, 4 * s + grp, D));
       lo[s].u = need ? v.u : make_uint4(0u, 0u, 0u, 0u);
     }
   }
@@ -82,7 +87,7 @@ __device__ __forceinline__ int route_q_f16(const Frag<uint16_t> (&qf)[D / 32], F
 // consecutive rows of one kept node (its grandchildren) fall on distinct chunk columns. Lower rows and
 // every lo plane are read from global memory.
 template <int D>
-struct LdsHiRows : NodeRows<uint16_t, D> {
+struct LdsHiRows : RoutePlanes<D> {
   const uint16_t* lds;
   const float* lds_bound;  // the same rows' hi-plane bounds
   int first;
@@ -96,7 +101,7 @@ struct LdsHiRows : NodeRows<uint16_t, D> {
       for (int s = 0; s < D / 32; ++s)
         hi[s].u = *reinterpret_cast<const uint4*>(lds + r * D + 8 * ((4 * s + grp) ^ (r & (D / 8 - 1))));
     } else {
-      NodeRows<uint16_t, D>::load_hi(hi, node, grp);
+      RoutePlanes<D>::load_hi(hi, node, grp);
     }
   }
 };
@@ -106,7 +111,7 @@ struct LdsHiRows : NodeRows<uint16_t, D> {
 // be in flight together; a per-lane choice compiles to flat loads, each waited for before its MFMA.
 template <int D>
 struct GlobalHiLoader {
-  const NodeRows<uint16_t, D>* rows;
+  const RoutePlanes<D>* rows;
   __device__ __forceinline__ void load_hi(Frag<uint16_t> (&hi)[D / 32], int node, int grp) const {
     rows->load_hi(hi, node, grp);
   }
@@ -127,7 +132,7 @@ struct LdsHiLoader {
 };
 // f(loader) for the level whose rows start at level_off (wave-uniform)
 template <int D, class F>
-__device__ __forceinline__ void for_level_rows(const NodeRows<uint16_t, D>& rows, int, F&& f) {
+__device__ __forceinline__ void for_level_rows(const RoutePlanes<D>& rows, int, F&& f) {
   f(GlobalHiLoader<D>{&rows});
 }
 template <int D, class F>
@@ -138,17 +143,20 @@ __device__ __forceinline__ void for_level_rows(const LdsHiRows<D>& rows, int lev
     f(GlobalHiLoader<D>{&rows});
 }
 
-// Cooperative copy of the hi planes of pyramid rows [first, first + n) into lds (layout above) and of
-// their bounds into lds_bound.
+// Cooperative copy of the hi planes of routing rows [first, first + n) into lds (layout above) and of
+// their bounds into lds_bound. Consecutive threads read consecutive 16-byte pieces of a row group.
 template <int D>
 __device__ __forceinline__ void stage_hi_rows(const uint16_t* base, const float* norms, int first, int n,
                                               uint16_t* lds, float* lds_bound) {
   constexpr int CHR = D / 8;
   for (int x = threadIdx.x; x < n; x += blockDim.x) lds_bound[x] = norms[first + x];
-  for (int x = threadIdx.x; x < n * CHR; x += blockDim.x) {
-    const int r = x / CHR, c = x % CHR;
-    *reinterpret_cast<uint4*>(lds + r * D + 8 * (c ^ (r & (CHR - 1)))) =
-        *reinterpret_cast<const uint4*>(base + (long long)(first + r) * (2 * D) + 8 * c);
+  const int a0 = first >> 2, a1 = (first + n + 3) >> 2;  // row groups touched
+  for (int x = threadIdx.x; x < (a1 - a0) * 4 * CHR; x += blockDim.x) {
+    const int R = 4 * (a0 + x / (4 * CHR)) + (x & 3), c = (x >> 2) % CHR;
+    const int r = R - first;
+    if (r >= 0 && r < n)
+      *reinterpret_cast<uint4*>(lds + r * D + 8 * (c ^ (r & (CHR - 1)))) =
+          *reinterpret_cast<const uint4*>(route_plane_chunk(base, R, 0, c, D));
   }
 }
 
@@ -351,7 +359,8 @@ __device__ bool select_level_refine(const Rows& rows, const float* norms, int le
 
 // Walk from the root to level 1 for query position i. Level l has e_l = (i >> (log2 C + l)) + 1
 // eligible nodes; levels with e_l <= K keep all of them, so the walk starts below the highest level
-// with more than K. Returns the number of kept level-1 nodes; lane c < n holds the c-th (ascending).
+// with more than K. level_select(child level, candidate node, n_cand, eligible children) scores one
+// level. Returns the number of kept level-1 nodes; lane c < n holds the c-th (ascending).
 // A pyramid of one leaf has the virtual level-1 node 0.
 template <typename T, int D, int KM, class LevelSelect>
 __device__ int walk_to_level1(const Levels& lv, int log2c, int K, int i, int* kept_out, LevelSelect&& level_select) {
@@ -383,7 +392,7 @@ __device__ int walk_to_level1(const Levels& lv, int log2c, int K, int i, int* ke
       nk = n_cand;
       continue;
     }
-    const bool keep = level_select((int)lv.off[l - 1], cn, n_cand, (i >> (log2c + l - 1)) + 1);
+    const bool keep = level_select(l - 1, cn, n_cand, (i >> (log2c + l - 1)) + 1);
     int cnt;
     const int nxt = compact_lanes(keep, cn, &cnt);
     kept = lane < cnt ? nxt : -1;
