@@ -35,6 +35,13 @@ struct Levels {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// v, opaque to the optimiser: values derived from it are computed where they are used instead of being
+// hoisted out of the enclosing loops (where they would occupy registers for the whole loop)
+__device__ __forceinline__ int opaque_int(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t x) { return __uint_as_float(((uint32_t)x) << 16); }
 
 // fp32 -> bf16, round to nearest, ties to even.

@@ -21,8 +21,14 @@
 
 namespace pisa {
 
-constexpr int kGroupWaves = 12;
+// waves per work-group: the per-wave LDS lists grow with the candidate tiles (KM)
+constexpr int kGroupWavesK16 = 16;  // KM <= 4 (K <= 16): LDS holds the lists of 16 waves
+template <int KM>
+constexpr int group_waves() {
+  return KM <= 4 ? kGroupWavesK16 : 12;
+}
 constexpr int kGroupLdsBytes = 128 * 1024;
+constexpr int kRowRound = 4;  // M-tiles of one unit whose hi rows are in flight together
 
 struct GroupRouteParams {
   const uint16_t* q;
@@ -36,13 +42,14 @@ struct GroupRouteParams {
 };
 
 template <int D, int C, int G, int KM>
-__global__ __launch_bounds__(kGroupWaves * 64) void route_group_kernel(GroupRouteParams p, int lds_first,
+__global__ __launch_bounds__(group_waves<KM>() * 64) void route_group_kernel(GroupRouteParams p, int lds_first,
                                                                       int wg_per_head) {
   constexpr int UG = 16 / G;             // units per wave
   constexpr int LOG2C = C == 64 ? 6 : 5;
   constexpr int NS = D / 32;             // k steps
   constexpr int OWN = (KM + G - 1) / G;  // owned M-tile slots per lane (x2 candidates)
   constexpr int NC = 8 * KM;             // candidate slots per unit (>= 2K)
+  constexpr int kGroupWaves = group_waves<KM>();
   __shared__ __align__(16) uint16_t s_hi[kGroupLdsBytes / 2];
   __shared__ float s_bound[kGroupLdsBytes / 128];
   __shared__ int s_kept[kGroupWaves][2][UG][NC / 2];
@@ -155,19 +162,23 @@ __global__ __launch_bounds__(kGroupWaves * 64) void route_group_kernel(GroupRout
             if (n_cand[x] <= K) continue;
             // every M-tile is loaded (rows past the unit's candidates read row `off`, and their sums
             // are never used), so no branch separates the tiles' loads
+            constexpr int MR = kRowRound < KM ? kRowRound : KM;
 #pragma unroll
-            for (int m = 0; m < KM; ++m) {
-              const int kj = 4 * m + (col >> 2), c = kj * 2 + ((col >> 1) & 1);
-              const bool valid = c < n_cand[x] && ((col & 1) == 0 || c < n_full[x]);
-              const int kn = s_kept[wave][cur][x][kj < nk[x] ? kj : 0];
-              Frag<uint16_t> hi[NS];
-              ld.load_hi(hi, off + (valid ? 4 * kn + (col & 3) : 0), g);
-              f32x4 a = zero4();
+            for (int m0 = 0; m0 < KM; m0 += MR) {
 #pragma unroll
-              for (int s = 0; s < NS; ++s) mma_f16(a, hi[s], qh[s]);
-              if (xo == x) acc_own[m] = a;
+              for (int m = m0; m < m0 + MR; ++m) {
+                const int kj = 4 * m + (col >> 2), c = kj * 2 + ((col >> 1) & 1);
+                const bool valid = c < n_cand[x] && ((col & 1) == 0 || c < n_full[x]);
+                const int kn = s_kept[wave][cur][x][kj < nk[x] ? kj : 0];
+                Frag<uint16_t> hi[NS];
+                ld.load_hi(hi, off + (valid ? 4 * kn + (col & 3) : 0), g);
+                f32x4 a = zero4();
+#pragma unroll
+                for (int s = 0; s < NS; ++s) mma_f16(a, hi[s], qh[s]);
+                if (xo == x) acc_own[m] = a;
+              }
+              __builtin_amdgcn_sched_barrier(0);  // MR M-tiles' rows in flight at a time (register budget)
             }
-            __builtin_amdgcn_sched_barrier(0);  // one unit's rows in flight at a time (register budget)
           }
           // the owned candidates' bounds: E = scale * sum_h |q_h| * max over the two children
 #pragma unroll
@@ -288,7 +299,11 @@ __global__ __launch_bounds__(kGroupWaves * 64) void route_group_kernel(GroupRout
               const int kj = 4 * m + (col >> 2), c = kj * 2 + ((col >> 1) & 1);
               const bool valid = c < n_cand[x] && ((col & 1) == 0 || c < n_full[x]);
               const unsigned long long fr = ((col >> 1) & 1) ? rb[m / G][1] : rb[m / G][0];
-              const bool need = valid && ((fr >> (oc + 16 * (col >> 2))) & 1ull);
+              // the owner's flag bit, computed here: hoisted out of the unit loop, the 16 shifted
+              // 64-bit masks would hold 32 registers for the whole walk
+              const int sh = opaque_int(oc + 16 * (col >> 2));
+              const uint32_t fw = sh < 32 ? (uint32_t)fr : (uint32_t)(fr >> 32);
+              const bool need = valid && ((fw >> (sh & 31)) & 1u);
               const int kn = s_kept[wave][cur][x][kj < nk[x] ? kj : 0];
               Frag<uint16_t> lo[NS];
               rows.load_lo(lo, off + (need ? 4 * kn + (col & 3) : 0), g, need);
@@ -387,6 +402,7 @@ static hipError_t route_group_t(const SelDims& sd, const void* q, const void* hi
   const long long groups = (sd.N + 16 / G - 1) / (16 / G);
   long long wph = 256 / BH;  // about one work-group per CU
   if (wph < 1) wph = 1;
+  constexpr int kGroupWaves = group_waves<KM>();
   if (wph > (groups + kGroupWaves - 1) / kGroupWaves) wph = (groups + kGroupWaves - 1) / kGroupWaves;
   hipLaunchKernelGGL((route_group_kernel<D, C, G, KM>), dim3((unsigned)(BH * wph)), dim3(kGroupWaves * 64), 0, st, p,
                      (int)sd.lv.roff[lcut], (int)wph);

@@ -421,21 +421,13 @@ __device__ __forceinline__ void load_leaf_pair(const T* kbh, long long t0, int N
 // kfrag(m, s) returns the A-fragment of tokens t0 + 16 m + (0..15), k step s.
 // kPhased: a scheduling fence after each k step, so that LDS-sourced fragments of one step at a time
 // are live (the arithmetic is unchanged).
-template <typename T, int D, int C, bool kPhased = false, typename KFrag>
-__device__ __forceinline__ void leaf_pair_lse_k(KFrag kfrag, const Frag<T> (&qf)[D / 32], long long t0,
-                                                long long icol, float scale, float& lse0, float& lse1) {
-  constexpr int MT = C / 8;
+// Per-column LSEs of the two leaves from the accumulated tile dot products (acc[m]: tokens t0 + 16 m +
+// (0..15)), masking tokens after icol.
+template <typename T, int C>
+__device__ __forceinline__ void leaf_pair_lse_acc(const f32x4 (&acc)[C / 8], long long t0, long long icol, float scale,
+                                                  float& lse0, float& lse1) {
   constexpr int ML = C / 16;  // M-tiles per leaf
   const int grp = lane_id() >> 4;
-  f32x4 acc[MT];
-#pragma unroll
-  for (int m = 0; m < MT; ++m) acc[m] = zero4();
-#pragma unroll
-  for (int s = 0; s < D / 32; ++s) {
-#pragma unroll
-    for (int m = 0; m < MT; ++m) mma(acc[m], kfrag(m, s), qf[s]);
-    if constexpr (kPhased) __builtin_amdgcn_sched_barrier(0);
-  }
   // causal mask on offsets within the tile: token t0 + o is visible iff o <= icol - t0
   const long long lim64 = icol - t0;
   const int lim = lim64 < 0 ? -1 : (lim64 > 2 * C ? 2 * C : (int)lim64);
@@ -466,6 +458,26 @@ __device__ __forceinline__ void leaf_pair_lse_k(KFrag kfrag, const Frag<T> (&qf)
     else
       lse1 = l;
   }
+}
+
+// Per-column LSE over leaf 2p (lse0) and leaf 2p+1 (lse1) of scale * q_col . k_t for t <= icol.
+// kfrag(m, s) returns the A-fragment of tokens t0 + 16 m + (0..15), k step s.
+// kPhased: a scheduling fence after each k step, so that LDS-sourced fragments of one step at a time
+// are live (the arithmetic is unchanged).
+template <typename T, int D, int C, bool kPhased = false, typename KFrag>
+__device__ __forceinline__ void leaf_pair_lse_k(KFrag kfrag, const Frag<T> (&qf)[D / 32], long long t0,
+                                                long long icol, float scale, float& lse0, float& lse1) {
+  constexpr int MT = C / 8;
+  f32x4 acc[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) acc[m] = zero4();
+#pragma unroll
+  for (int s = 0; s < D / 32; ++s) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m) mma(acc[m], kfrag(m, s), qf[s]);
+    if constexpr (kPhased) __builtin_amdgcn_sched_barrier(0);
+  }
+  leaf_pair_lse_acc<T, C>(acc, t0, icol, scale, lse0, lse1);
 }
 
 template <typename T, int D, int C>
