@@ -237,6 +237,34 @@ __device__ __forceinline__ float row_sum16(float v) {
   return v + dpp_rot<0x121>(v);  // row_ror:1
 }
 
+// v of lane (this lane ^ O): a DPP quad permutation for O = 1, 2 (no LDS round trip), else a shuffle.
+template <int O>
+__device__ __forceinline__ float xor_lane(float v) {
+  if constexpr (O == 1)
+    return dpp_rot<0xB1>(v);  // quad_perm [1, 0, 3, 2]
+  else if constexpr (O == 2)
+    return dpp_rot<0x4E>(v);  // quad_perm [2, 3, 0, 1]
+  else
+    return __shfl_xor(v, O);
+}
+// Butterfly sum over the G consecutive lanes of a group (strides G/2 .. 1, in that order).
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (G >= 16) v += xor_lane<8>(v);
+  if constexpr (G >= 8) v += xor_lane<4>(v);
+  if constexpr (G >= 4) v += xor_lane<2>(v);
+  if constexpr (G >= 2) v += xor_lane<1>(v);
+  return v;
+}
+template <int G>
+__device__ __forceinline__ float group_max(float v) {
+  if constexpr (G >= 16) v = fmaxf(v, xor_lane<8>(v));
+  if constexpr (G >= 8) v = fmaxf(v, xor_lane<4>(v));
+  if constexpr (G >= 4) v = fmaxf(v, xor_lane<2>(v));
+  if constexpr (G >= 2) v = fmaxf(v, xor_lane<1>(v));
+  return v;
+}
+
 // Wave-uniform read of lane c.
 __device__ __forceinline__ int readlane(int v, int c) { return __builtin_amdgcn_readlane(v, c); }
 __device__ __forceinline__ float readlane(float v, int c) {

@@ -57,6 +57,7 @@ __global__ __launch_bounds__(group_waves<KM>() * 64) void route_group_kernel(Gro
   __shared__ unsigned long long s_mask[kGroupWaves][UG];
   const int lane = lane_id(), wave = threadIdx.x >> 6, col = lane & 15, g = lane >> 4;
   const int xo = col / G, h = col % G;  // this lane's unit and head
+  const int cb = 2 * (col >> 2) + ((col >> 1) & 1);  // candidate of row col in M-tile 0
   const int BH = p.B * p.Hkv;
   const int bh = blockIdx.x % BH, w = blockIdx.x / BH;
   const int K = p.K;
@@ -98,8 +99,7 @@ __global__ __launch_bounds__(group_waves<KM>() * 64) void route_group_kernel(Gro
           sq += v * v;
         }
       qn = sqrtf(colgroup_sum(sq));
-#pragma unroll
-      for (int o = G / 2; o >= 1; o >>= 1) qn += __shfl_xor(qn, o);
+      qn = group_sum<G>(qn);
     }
     const int te = route_q_f16<D>(qf, qh);
     const float col_scale = ldexpf(p.scale, -(te + hexp));
@@ -143,6 +143,11 @@ __global__ __launch_bounds__(group_waves<KM>() * 64) void route_group_kernel(Gro
         my_nk = xo == x ? nk[x] : my_nk;
       }
       const bool my_scored = my_nc > K;
+      // row (col) of an M-tile m is valid iff its candidate 8 m + cb exists and, for a second child
+      // (odd col), has two eligible children: 8 m + cb < lim[x]. Valid rows have kept index kj < nk.
+      int lim[UG];
+#pragma unroll
+      for (int x = 0; x < UG; ++x) lim[x] = (col & 1) ? n_full[x] : n_cand[x];
       // candidate c: node 2 kept[c >> 1] + (c & 1) at level l
       auto cand_node = [&](int c) {
         const int kj = c >> 1;
@@ -167,11 +172,10 @@ __global__ __launch_bounds__(group_waves<KM>() * 64) void route_group_kernel(Gro
             for (int m0 = 0; m0 < KM; m0 += MR) {
 #pragma unroll
               for (int m = m0; m < m0 + MR; ++m) {
-                const int kj = 4 * m + (col >> 2), c = kj * 2 + ((col >> 1) & 1);
-                const bool valid = c < n_cand[x] && ((col & 1) == 0 || c < n_full[x]);
-                const int kn = s_kept[wave][cur][x][kj < nk[x] ? kj : 0];
+                const bool valid = 8 * m + cb < lim[x];
+                const unsigned kn = (unsigned)s_kept[wave][cur][x][4 * m + (col >> 2)];  // any value if !valid
                 Frag<uint16_t> hi[NS];
-                ld.load_hi(hi, off + (valid ? 4 * kn + (col & 3) : 0), g);
+                ld.load_hi(hi, off + (valid ? (int)(4 * kn) + (col & 3) : 0), g);
                 f32x4 a = zero4();
 #pragma unroll
                 for (int s = 0; s < NS; ++s) mma_f16(a, hi[s], qh[s]);
@@ -205,9 +209,7 @@ __global__ __launch_bounds__(group_waves<KM>() * 64) void route_group_kernel(Gro
               const int c = 8 * m + 2 * g + a;
               const float x0 = col_scale * acc_own[m][2 * a], x1 = col_scale * acc_own[m][2 * a + 1];
               float v = c < my_nf ? lse2(x0, x1) : x0;
-#pragma unroll
-              for (int o = G / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-              sc[m][a] = v;
+              sc[m][a] = group_sum<G>(v);
             }
         };
         float sc[KM][2];
@@ -226,7 +228,9 @@ __global__ __launch_bounds__(group_waves<KM>() * 64) void route_group_kernel(Gro
             const int c = 8 * m + 2 * g + a;
             own_v[j][a] = m < KM && c < my_nc;
             own_s[j][a] = s;
-            if (own_v[j][a]) s_key[wave][xo][c] = topk_key(s, c);
+            // every slot below NC has an owner: slots past the unit's candidates hold 0, which ranks
+            // below every key (keys of finite and infinite scores are positive)
+            if (m < KM) s_key[wave][xo][c] = own_v[j][a] ? topk_key(s, c) : 0u;
           }
         __threadfence_block();
         // in-flags of the owned candidates (fewer than K of the unit's keys above theirs), all owned
@@ -241,14 +245,13 @@ __global__ __launch_bounds__(group_waves<KM>() * 64) void route_group_kernel(Gro
               key[j][a] = topk_key(own_s[j][a], 8 * (h + j * G) + 2 * g + a);
               rank[j][a] = 0;
             }
-          for (int c = 0; c < my_nc; c += 4) {
+          for (int c = 0; c < my_nc; c += 4) {  // slots up to the next multiple of 4 are padded
             const uint4 v = *reinterpret_cast<const uint4*>(&s_key[wave][xo][c]);
 #pragma unroll
             for (int j = 0; j < OWN; ++j)
 #pragma unroll
               for (int a = 0; a < 2; ++a)
-                rank[j][a] += (v.x > key[j][a]) + (c + 1 < my_nc && v.y > key[j][a]) +
-                              (c + 2 < my_nc && v.z > key[j][a]) + (c + 3 < my_nc && v.w > key[j][a]);
+                rank[j][a] += (v.x > key[j][a]) + (v.y > key[j][a]) + (v.z > key[j][a]) + (v.w > key[j][a]);
           }
 #pragma unroll
           for (int j = 0; j < OWN; ++j)
@@ -265,11 +268,8 @@ __global__ __launch_bounds__(group_waves<KM>() * 64) void route_group_kernel(Gro
             if (in[j][a]) l_in = fminf(l_in, own_s[j][a] - own_e[j][a]);
           }
         // over the unit's lanes (its G columns in each of the 4 lane groups)
-#pragma unroll
-        for (int o = 1; o < G; o <<= 1) {
-          u_out = fmaxf(u_out, __shfl_xor(u_out, o));
-          l_in = fminf(l_in, __shfl_xor(l_in, o));
-        }
+        u_out = group_max<G>(u_out);
+        l_in = -group_max<G>(-l_in);
         u_out = colgroup_max(u_out);
         l_in = -colgroup_max(-l_in);
         bool refine[OWN][2];
@@ -296,18 +296,19 @@ __global__ __launch_bounds__(group_waves<KM>() * 64) void route_group_kernel(Gro
               const int oc = x * G + (m % G);
               const unsigned long long tm = (rb[m / G][0] | rb[m / G][1]) & (0x0001000100010001ull << oc);
               if (!tm) continue;
-              const int kj = 4 * m + (col >> 2), c = kj * 2 + ((col >> 1) & 1);
-              const bool valid = c < n_cand[x] && ((col & 1) == 0 || c < n_full[x]);
+              const bool valid = 8 * m + cb < lim[x];
               const unsigned long long fr = ((col >> 1) & 1) ? rb[m / G][1] : rb[m / G][0];
               // the owner's flag bit, computed here: hoisted out of the unit loop, the 16 shifted
               // 64-bit masks would hold 32 registers for the whole walk
               const int sh = opaque_int(oc + 16 * (col >> 2));
               const uint32_t fw = sh < 32 ? (uint32_t)fr : (uint32_t)(fr >> 32);
               const bool need = valid && ((fw >> (sh & 31)) & 1u);
-              const int kn = s_kept[wave][cur][x][kj < nk[x] ? kj : 0];
+              const unsigned kn = (unsigned)s_kept[wave][cur][x][4 * m + (col >> 2)];  // any value if !valid
+              // rows of decided candidates read row `off` and add its lo plane: their sums are not used
+              // again (a decided candidate's final key is +-inf), and other units' lanes drop `a`
               Frag<uint16_t> lo[NS];
-              rows.load_lo(lo, off + (need ? 4 * kn + (col & 3) : 0), g, need);
-              f32x4 a = xo == x ? acc_own[m] : zero4();
+              rows.load_lo_any(lo, off + (need ? (int)(4 * kn) + (col & 3) : 0), g);
+              f32x4 a = acc_own[m];
 #pragma unroll
               for (int s = 0; s < NS; ++s) mma_f16(a, lo[s], qh[s]);
               if (xo == x) acc_own[m] = a;

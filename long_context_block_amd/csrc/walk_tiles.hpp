@@ -48,6 +48,11 @@ struct RoutePlanes {
   // lo plane of routing row R, zero where !need. R must be a valid row either way: the load is
   // unconditional and its value dropped afterwards, because a load under a lane condition makes the
   // compiler wait for it before issuing the next one.
+  // lo plane of routing row R as read (for rows whose sums are discarded when not needed)
+  __device__ __forceinline__ void load_lo_any(Frag<uint16_t> (&lo)[D / 32], int R, int grp) const {
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) lo[s].load(route_plane_chunk(base, R, 1, 4 * s + grp, D));
+  }
   __device__ __forceinline__ void load_lo(Frag<uint16_t> (&lo)[D / 32], int R, int grp, bool need) const {
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) {
@@ -82,6 +87,16 @@ __device__ __forceinline__ int route_q_f16(const Frag<uint16_t> (&qf)[D / 32], F
   return te;
 }
 
+// Fragments of local LDS row r (layout below): chunk 4 s + grp sits at chunk (4 s + grp) ^ (r mod D/8),
+// i.e. at element (r D + 8 (grp ^ (r mod D/8))) ^ 32 s, since 4 s only flips chunk bits that r D and
+// grp do not touch: one address per row, then a constant XOR per k step.
+template <int D>
+__device__ __forceinline__ void lds_hi_row(Frag<uint16_t> (&hi)[D / 32], const uint16_t* lds, int r, int grp) {
+  const unsigned e0 = (unsigned)(r * D + 8 * (grp ^ (r & (D / 8 - 1))));
+#pragma unroll
+  for (int s = 0; s < D / 32; ++s) hi[s].u = *reinterpret_cast<const uint4*>(lds + (e0 ^ (32u * s)));
+}
+
 // Routing walk with the hi plane of the upper pyramid rows (node >= first) resident in LDS: local row
 // r = node - first holds D hi values, 16-byte chunk c stored at chunk c ^ (r mod D/8), so the 4
 // consecutive rows of one kept node (its grandchildren) fall on distinct chunk columns. Lower rows and
@@ -96,10 +111,7 @@ struct LdsHiRows : RoutePlanes<D> {
   }
   __device__ __forceinline__ void load_hi(Frag<uint16_t> (&hi)[D / 32], int node, int grp) const {
     if (node >= first) {
-      const int r = node - first;
-#pragma unroll
-      for (int s = 0; s < D / 32; ++s)
-        hi[s].u = *reinterpret_cast<const uint4*>(lds + r * D + 8 * ((4 * s + grp) ^ (r & (D / 8 - 1))));
+      lds_hi_row<D>(hi, lds, node - first, grp);
     } else {
       RoutePlanes<D>::load_hi(hi, node, grp);
     }
@@ -123,10 +135,7 @@ struct LdsHiLoader {
   const float* lds_bound;
   int first;
   __device__ __forceinline__ void load_hi(Frag<uint16_t> (&hi)[D / 32], int node, int grp) const {
-    const int r = node - first;
-#pragma unroll
-    for (int s = 0; s < D / 32; ++s)
-      hi[s].u = *reinterpret_cast<const uint4*>(lds + r * D + 8 * ((4 * s + grp) ^ (r & (D / 8 - 1))));
+    lds_hi_row<D>(hi, lds, node - first, grp);
   }
   __device__ __forceinline__ float bound(const float*, int node) const { return lds_bound[node - first]; }
 };
