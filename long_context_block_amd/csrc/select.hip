@@ -387,25 +387,33 @@ __global__ __launch_bounds__(256, 3) void leaf_lse_wg_kernel(LeafParams<uint16_t
     stage_leaf_pair_wg<D, C>(kbh, t0, p.N, s_k);
     __syncthreads();
     const int bi = (int)(bh / p.Hkv), ri = (int)(bh % p.Hkv);
-    const uint16_t* qhead = p.q + (((long long)bi * p.Hq + (long long)ri * p.G + h) * p.N) * D + 8 * grp;
+    // quad-coalesced query loads: lane 4 r + c reads chunks 4 s + c of column r's query row (64
+    // contiguous bytes per quad and k step); quad_rows_to_mfma() moves them to the MFMA layout
+    const int qr = quad_row(), hq = qr % p.G;
+    const uint16_t* qhead =
+        p.q + (((long long)bi * p.Hq + (long long)ri * p.G + hq) * p.N) * D + 8 * quad_chunk();
     const long long ubase = bh * p.N;
     const int ntiles = (b - a + p.q_tile - 1) / p.q_tile;
     // A column past the run, past the tile's q_tile units, or past the wave's last tile repeats the
     // run's first pair: it computes that pair's values again and stores the same bits to the same place.
+    // pc: the pair of this lane's column (r16).
     auto fetch = [&](int t, Frag<uint16_t> (&qf)[D / 32], uint32_t& pc) {
+      int xl = a + t * p.q_tile + qr / p.G;
+      xl = (t < ntiles && qr < cols && xl < b) ? xl : a;
+      const uint16_t* qrow = qhead + ((long long)(s_pair[xl] >> 5) - ubase) * D;
+#pragma unroll
+      for (int s2 = 0; s2 < D / 32; ++s2) qf[s2].load(qrow + 32 * s2);
       int x = a + t * p.q_tile + r16 / p.G;
       x = (t < ntiles && r16 < cols && x < b) ? x : a;
       pc = s_pair[x];
-      const uint16_t* qrow = qhead + ((long long)(pc >> 5) - ubase) * D;
-#pragma unroll
-      for (int s2 = 0; s2 < D / 32; ++s2) qf[s2].load(qrow + 32 * s2);
     };
     struct Out {
       float l0, l1;
       uint32_t pc;
     };
-    auto score = [&](const Frag<uint16_t> (&qf)[D / 32], uint32_t pc, Out& out) {
+    auto score = [&](Frag<uint16_t> (&qf)[D / 32], uint32_t pc, Out& out) {
       out.pc = pc;
+      quad_rows_to_mfma(qf);
       leaf_pair_lse_k<uint16_t, D, C, true>([&](int m, int s2) { return leaf_k_frag_wg<D>(s_k, m, s2); }, qf, t0,
                                       (long long)(pc >> 5) - ubase, p.scale, out.l0, out.l1);
     };
