@@ -162,6 +162,22 @@ __global__ __launch_bounds__(group_waves<KM>() * 64) void route_group_kernel(Gro
 #pragma unroll
         for (int m = 0; m < KM; ++m) acc_own[m] = zero4();
         for_level_rows(rows, off, [&](const auto& ld) {
+          if (l == lw) {
+            // top scored level: the wave's units lie in one aligned block of 16 / G positions, so they
+            // share the kept list (every eligible node of level lw + 1) and the candidate rows; one
+            // pass serves all 16 columns
+#pragma unroll
+            for (int m = 0; m < KM; ++m) {
+              const bool valid = 8 * m + cb < lim[0];
+              const unsigned kn = (unsigned)s_kept[wave][cur][0][4 * m + (col >> 2)];  // any value if !valid
+              Frag<uint16_t> hi[NS];
+              ld.load_hi(hi, off + (valid ? (int)(4 * kn) + (col & 3) : 0), g);
+              f32x4 a = zero4();
+#pragma unroll
+              for (int s = 0; s < NS; ++s) mma_f16(a, hi[s], qh[s]);
+              acc_own[m] = a;
+            }
+          } else {
 #pragma unroll
           for (int x = 0; x < UG; ++x) {
             if (n_cand[x] <= K) continue;
@@ -183,6 +199,7 @@ __global__ __launch_bounds__(group_waves<KM>() * 64) void route_group_kernel(Gro
               }
               __builtin_amdgcn_sched_barrier(0);  // MR M-tiles' rows in flight at a time (register budget)
             }
+          }
           }
           // the owned candidates' bounds: E = scale * sum_h |q_h| * max over the two children
 #pragma unroll
@@ -289,6 +306,23 @@ __global__ __launch_bounds__(group_waves<KM>() * 64) void route_group_kernel(Gro
           // candidate is undecided. Candidate 8 m + 2 g' + a of unit x is owned by lane
           // (x G + m mod G) + 16 g' with flag set (m / G, a), so the tile and row flags come from the
           // owners' ballots.
+          if (l == lw) {
+            // shared rows (top scored level): a tile with an undecided candidate of any unit gets the lo
+            // plane of all its valid rows; the sums of decided candidates are not used again
+#pragma unroll
+            for (int m = 0; m < KM; ++m) {
+              unsigned long long tmask = 0ull;
+#pragma unroll
+              for (int x = 0; x < UG; ++x) tmask |= 0x0001000100010001ull << (x * G + (m % G));
+              if (!((rb[m / G][0] | rb[m / G][1]) & tmask)) continue;
+              const bool valid = 8 * m + cb < lim[0];
+              const unsigned kn = (unsigned)s_kept[wave][cur][0][4 * m + (col >> 2)];  // any value if !valid
+              Frag<uint16_t> lo[NS];
+              rows.load_lo_any(lo, off + (valid ? (int)(4 * kn) + (col & 3) : 0), g);
+#pragma unroll
+              for (int s = 0; s < NS; ++s) mma_f16(acc_own[m], lo[s], qh[s]);
+            }
+          } else
 #pragma unroll
           for (int x = 0; x < UG; ++x) {
 #pragma unroll
