@@ -53,7 +53,8 @@ __global__ __launch_bounds__(group_waves<KM>() * 64) void route_group_kernel(Gro
   __shared__ __align__(16) uint16_t s_hi[kGroupLdsBytes / 2];
   __shared__ float s_bound[kGroupLdsBytes / 128];
   __shared__ int s_kept[kGroupWaves][2][UG][NC / 2];
-  __shared__ __align__(16) uint32_t s_key[kGroupWaves][UG][NC];
+  // a unit's keys (padded by 4 words: the units' 16-byte reads fall on different banks)
+  __shared__ __align__(16) uint32_t s_key[kGroupWaves][UG][NC + 4];
   __shared__ unsigned long long s_mask[kGroupWaves][UG];
   const int lane = lane_id(), wave = threadIdx.x >> 6, col = lane & 15, g = lane >> 4;
   const int xo = col / G, h = col % G;  // this lane's unit and head

@@ -92,9 +92,11 @@ __device__ __forceinline__ int route_q_f16(const Frag<uint16_t> (&qf)[D / 32], F
 // grp do not touch: one address per row, then a constant XOR per k step.
 template <int D>
 __device__ __forceinline__ void lds_hi_row(Frag<uint16_t> (&hi)[D / 32], const uint16_t* lds, int r, int grp) {
-  const unsigned e0 = (unsigned)(r * D + 8 * (grp ^ (r & (D / 8 - 1))));
+  // byte offsets: one XOR per k step
+  const unsigned b0 = 2u * (unsigned)(r * D + 8 * (grp ^ (r & (D / 8 - 1))));
+  const char* base = reinterpret_cast<const char*>(lds);
 #pragma unroll
-  for (int s = 0; s < D / 32; ++s) hi[s].u = *reinterpret_cast<const uint4*>(lds + (e0 ^ (32u * s)));
+  for (int s = 0; s < D / 32; ++s) hi[s].u = *reinterpret_cast<const uint4*>(base + (b0 ^ (64u * s)));
 }
 
 // Routing walk with the hi plane of the upper pyramid rows (node >= first) resident in LDS: local row
