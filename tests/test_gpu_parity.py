@@ -92,6 +92,10 @@ LDS_SPILL = {
     "g16_32k": dict(B=1, Hq=16, Hkv=1, N=32768, d=128, C=64, K=16),
     "k32_64k": dict(B=1, Hq=8, Hkv=2, N=65536, d=128, C=64, K=32),
     "d64_c32_64k": dict(B=1, Hq=8, Hkv=2, N=65536, d=64, C=32, K=16),
+    # ragged lengths: leaf levels whose node counts are not multiples of 4 (padded routing rows) in the
+    # rows gathered from global memory
+    "g4_ragged_64k": dict(B=1, Hq=8, Hkv=2, N=65436, d=128, C=64, K=16),
+    "g2_ragged_b2": dict(B=2, Hq=4, Hkv=2, N=40000, d=64, C=32, K=8),
 }
 
 
