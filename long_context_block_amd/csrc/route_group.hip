@@ -219,9 +219,11 @@ __global__ __launch_bounds__(group_waves<KM>() * 64) void route_group_kernel(Gro
             }
         });
         // ---- per-head candidate scores, summed over the unit's heads (strides G/2 .. 1)
-        auto head_scores = [&](float (&sc)[KM][2]) {
+        // tiles: bit m set = recompute M-tile m (wave-uniform)
+        auto head_scores = [&](float (&sc)[KM][2], unsigned tiles) {
 #pragma unroll
           for (int m = 0; m < KM; ++m)
+            if ((tiles >> m) & 1u)
 #pragma unroll
             for (int a = 0; a < 2; ++a) {
               const int c = 8 * m + 2 * g + a;
@@ -231,7 +233,7 @@ __global__ __launch_bounds__(group_waves<KM>() * 64) void route_group_kernel(Gro
             }
         };
         float sc[KM][2];
-        head_scores(sc);
+        head_scores(sc, ~0u);
         // ---- owned candidates: hi score, hi Top-K
         float own_s[OWN][2];
         bool own_v[OWN][2], in[OWN][2];
@@ -263,7 +265,8 @@ __global__ __launch_bounds__(group_waves<KM>() * 64) void route_group_kernel(Gro
               key[j][a] = topk_key(own_s[j][a], 8 * (h + j * G) + 2 * g + a);
               rank[j][a] = 0;
             }
-          for (int c = 0; c < my_nc; c += 4) {  // slots up to the next multiple of 4 are padded
+#pragma unroll 2
+          for (int c = 0; c < NC; c += 4) {  // every slot below NC holds a key or the padding 0
             const uint4 v = *reinterpret_cast<const uint4*>(&s_key[wave][xo][c]);
 #pragma unroll
             for (int j = 0; j < OWN; ++j)
@@ -349,7 +352,17 @@ __global__ __launch_bounds__(group_waves<KM>() * 64) void route_group_kernel(Gro
               if (xo == x) acc_own[m] = a;
             }
           }
-          head_scores(sc);
+          // only tiles holding an undecided candidate of some unit change; the other tiles' scores
+          // belong to decided candidates and are not read again
+          unsigned rtiles = 0u;
+#pragma unroll
+          for (int m = 0; m < KM; ++m) {
+            unsigned long long tmask = 0ull;
+#pragma unroll
+            for (int x = 0; x < UG; ++x) tmask |= 0x0001000100010001ull << (x * G + (m % G));
+            if ((rb[m / G][0] | rb[m / G][1]) & tmask) rtiles |= 1u << m;
+          }
+          head_scores(sc, rtiles);
           __threadfence_block();
           // final keys: undecided -> hi+lo score, decided in -> +inf, decided out -> -inf
 #pragma unroll
