@@ -237,7 +237,7 @@ __global__ __launch_bounds__(256, 3) void attn_leaf_wg_kernel(AttnParams<uint16_
         w.w = pack_bf16x2(out.o[2 * c + 1][2] * inv, out.o[2 * c + 1][3] * inv);
         *reinterpret_cast<uint4*>(dst + 32 * c) = w;
       }
-      p.part_lse[prow] = out.lse;  // the column's 4 lanes hold the same value
+      if (grp == 0) p.part_lse[prow] = out.lse;  // the column's 4 lanes hold the same value
     };
     if (wave < ntiles) {
       // two register sets in turn: this wave's tiles t and t + 4 are computed while the queries of
