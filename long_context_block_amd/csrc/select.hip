@@ -507,6 +507,86 @@ __global__ __launch_bounds__(256) void finalize_kernel(FinParams<float> p) {
   }
 }
 
+// K <= 16: a unit has at most 32 leaf candidates, so each half-wave finalizes its own unit (lanes
+// 32 half + c hold candidate c of unit 2 it + half): ranking, compaction and stores run for two units at
+// once. Same keys, same ranking rule and the same head order as finalize_kernel, so the same outputs.
+__global__ __launch_bounds__(256) void finalize_half_kernel(FinParams<float> p) {
+  __shared__ __align__(16) uint32_t s_key[4][64];
+  const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int half = lane >> 5, cl = lane & 31;
+  const unsigned U = (unsigned)p.B * p.Hkv * p.N;
+  const unsigned first = ((unsigned)xcd_logical_block(gridDim.x) * 4 + wave) * kFinUnits;
+  const int slot = cl >> 1;
+  const bool cand_lane = slot < p.K;
+  constexpr int NP = kFinUnits / 2;  // passes of two units
+  int kp[NP];
+  float sc[NP];
+#pragma unroll
+  for (int it = 0; it < NP; ++it) {
+    const unsigned u0 = first + 2 * it + half;
+    const unsigned u = u0 < U ? u0 : U - 1;
+    kp[it] = cand_lane ? p.kept[(long long)u * p.K + slot] : -1;
+    const float* ll = p.leaf_lse + ((long long)u * p.K * 2 + (cand_lane ? cl : 0)) * p.G;
+    float x = 0.f;  // heads in index order
+    if ((p.G & 3) == 0) {
+      for (int h = 0; h < p.G; h += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(ll + h);
+        x += v.x;
+        x += v.y;
+        x += v.z;
+        x += v.w;
+      }
+    } else {
+      for (int h = 0; h < p.G; ++h) x += ll[h];
+    }
+    sc[it] = x;
+  }
+  uint32_t* keys = s_key[wave] + 32 * half;
+  const unsigned long long hmask = 0xffffffffull << (32 * half);
+#pragma unroll
+  for (int it = 0; it < NP; ++it) {
+    const unsigned u = first + 2 * it + half;
+    const bool live = u < U;  // both halves run every step; a dead half stores nothing
+    const unsigned uu = live ? u : U - 1;
+    const unsigned bh = uu / (unsigned)p.N, i = uu - bh * (unsigned)p.N;
+    const int b = (int)(bh / (unsigned)p.Hkv), r = (int)(bh - (unsigned)b * p.Hkv);
+    const int leaf_c = 2 * kp[it] + (cl & 1);
+    const bool valid = kp[it] >= 0 && (long long)leaf_c * p.C <= (long long)i;
+    const int n_cand = __popcll(__ballot(valid) & hmask);  // valid candidates are a prefix
+    // Top-K by key (score descending, index ascending); slots past the candidates hold 0
+    const uint32_t mine = cl < n_cand ? topk_key(sc[it], cl) : 0u;
+    keys[cl] = mine;
+    __threadfence_block();
+    bool keep = cl < n_cand;
+    if (n_cand > p.K) {
+      int rank = 0;
+#pragma unroll
+      for (int c = 0; c < 32; c += 4) {
+        const uint4 v = *reinterpret_cast<const uint4*>(keys + c);
+        rank += (v.x > mine) + (v.y > mine) + (v.z > mine) + (v.w > mine);
+      }
+      keep = keep && rank < p.K;
+    }
+    __threadfence_block();  // the next unit rewrites the keys
+    // stable compaction within the half
+    const unsigned m = (unsigned)((__ballot(keep) & hmask) >> (32 * half));
+    const int below = __popc(m & ((1u << cl) - 1u));
+    const int nsel = __popc(m);
+    const int dst = 32 * half + (keep ? below : nsel + (cl - below));
+    const int leaf_sel = __builtin_amdgcn_ds_permute(dst << 2, leaf_c);
+    const int c_sel = __builtin_amdgcn_ds_permute(dst << 2, cl);
+    if (live && cl < p.K) {
+      p.sel[(long long)u * p.K + cl] = cl < nsel ? leaf_sel : -1;
+      if (p.sel_lse) {
+        const long long qrow0 = ((long long)b * p.Hq + (long long)r * p.G) * p.N + i;
+        const float* ll = p.leaf_lse + (long long)u * p.K * 2 * p.G;
+        for (int h = 0; h < p.G; ++h)
+          p.sel_lse[(qrow0 + (long long)h * p.N) * p.K + cl] = cl < nsel ? ll[c_sel * p.G + h] : kNegInf;
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------------------------------ regroup
 // Counting sort of (unit, slot) pairs by (KV head, node). Work-group = a run of units of one KV head;
 // ranks are taken in LDS, then each non-empty bucket reserves its range with one global atomic.
@@ -757,7 +837,10 @@ hipError_t launch_finalize(const SelDims& sd, const int* kept, const float* leaf
   p.sel_lse = sel_lse;
   const long long U = (long long)sd.B * sd.Hkv * sd.N;
   const long long waves = (U + kFinUnits - 1) / kFinUnits;
-  hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, p);
+  if (sd.K <= 16)
+    hipLaunchKernelGGL(finalize_half_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
