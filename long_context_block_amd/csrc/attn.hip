@@ -176,7 +176,8 @@ __global__ __launch_bounds__(256, 3) void attn_leaf_wg_kernel(AttnParams<uint16_
       p.pairs, base, n,
       [&](uint32_t pr) {
         const long long u = pr >> 5;
-        return ((u / p.N) * nch + ((u % p.N) >> p.chunk_log2)) * (1LL << 32) + p.sel[u * p.K + (pr & 31)];
+        const unsigned bh = (unsigned)u / (unsigned)p.N, i = (unsigned)u - bh * (unsigned)p.N;  // u < 2^27
+        return ((long long)bh * nch + (i >> p.chunk_log2)) * (1LL << 32) + p.sel[u * p.K + (pr & 31)];
       },
       s_pair, s_key, s_run, s_wcount);
   const int tile_units = 16 / p.G;

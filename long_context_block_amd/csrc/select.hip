@@ -372,7 +372,8 @@ __global__ __launch_bounds__(256, 3) void leaf_lse_wg_kernel(LeafParams<uint16_t
       p.pairs, base, n,
       [&](uint32_t pr) {
         const long long u = pr >> 5;
-        return ((u / p.N) * nch + ((u % p.N) >> p.chunk_log2)) * (1LL << 32) + p.kept[u * p.K + (pr & 31)];
+        const unsigned bh = (unsigned)u / (unsigned)p.N, i = (unsigned)u - bh * (unsigned)p.N;  // u < 2^27
+        return ((long long)bh * nch + (i >> p.chunk_log2)) * (1LL << 32) + p.kept[u * p.K + (pr & 31)];
       },
       s_pair, s_key, s_run, s_wcount);
   const int h = r16 % p.G;
@@ -672,11 +673,12 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int* __restrict__ no
       if (to_positions) ranks[x] = 0;
       continue;
     }
-    const long long u = x / K;
-    const int slot = (int)(x % K);
-    const long long bh = u / N, i = u % N;
-    const int at = offsets[(bh * nch + (i >> chunk_log2)) * nb + nd] + ranks[x];
-    pairs[at] = (uint32_t)((u << 5) | slot);
+    // pair indices fit in 32 bits (a packed pair holds its unit in 27), so the divisions are 32-bit
+    const unsigned u = (unsigned)x / (unsigned)K;
+    const int slot = (int)((unsigned)x - u * (unsigned)K);
+    const unsigned bh = u / (unsigned)N, i = u - bh * (unsigned)N;
+    const int at = offsets[((long long)bh * nch + (i >> chunk_log2)) * nb + nd] + ranks[x];
+    pairs[at] = (uint32_t)((u << 5) | (unsigned)slot);
     if (to_positions) ranks[x] = at;
   }
 }
