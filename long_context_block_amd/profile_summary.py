@@ -36,7 +36,7 @@ STAGE_KERNELS = {
     "route": ["route_group_kernel", "route_lds_kernel", "route_kernel"],
     "regroup": ["hist_kernel", "scan_kernel", "scatter_kernel", "fill_zero_kernel"],
     "leaf_lse": ["leaf_lse_wg_kernel", "leaf_lse_kernel"],
-    "finalize": ["finalize_kernel"],
+    "finalize": ["finalize_kernel", "finalize_half_kernel"],
     "attn_leaf": ["attn_leaf_wg_kernel", "attn_leaf_kernel"],
     "attn_merge": ["attn_merge_kernel"],
     "bsa_select": ["bsa_kernel"],
