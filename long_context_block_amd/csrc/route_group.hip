@@ -6,7 +6,8 @@
 // One work-group of 16 waves per CU (12 for K > 16) serves one KV head: the fp16 hi plane (and row
 // bounds) of the upper pyramid levels is staged into LDS once, then each wave walks UG = 16 / G
 // consecutive query positions at once (an aligned block, so at the top scored level the units share
-// their candidates and one pass over the rows serves them all). Matrix column col = x G + h is head h of unit x, so all 16 columns carry data. At a scored
+// their candidates and one pass over the rows serves them all). Matrix column col = x G + h is head h
+// of unit x, so all 16 columns carry data. At a scored
 // level, row 16 m + r of unit x's M-tile m is child (r & 1) of candidate 8 m + (r >> 1); all lanes load
 // and multiply every unit's rows, and the lanes of unit x keep the accumulators of their own M-tiles. A
 // lane (col, g) then holds both children of candidates 8 m + 2 g + {0, 1} for its head, so the per-head
