@@ -366,21 +366,58 @@ __global__ __launch_bounds__(group_waves<KM>() * 64) void route_group_kernel(Gro
           }
           head_scores(sc, rtiles);
           __threadfence_block();
-          // final keys: undecided -> hi+lo score, decided in -> +inf, decided out -> -inf
+          // Decided candidates keep their flags: at most K were decided in (all ranked in by the hi
+          // scores), and those together with the undecided hold every place, so the decided-out stay
+          // out. An undecided candidate is in iff (decided in) + (undecided of its unit with a larger
+          // hi+lo key) < K, i.e. its rank among all keys with the decided ones at +-inf. The undecided
+          // keys of each unit are compacted to the front of its LDS key slots (0 after them), so the
+          // ranking reads only those.
+          const unsigned long long umask = (((1ull << G) - 1ull) << (xo * G)) * 0x0001000100010001ull;
+          const unsigned long long below = lane ? (~0ull >> (64 - lane)) : 0ull;
+          int n_in_dec = 0, n_ref = 0, pos[OWN][2];
+#pragma unroll
+          for (int j = 0; j < OWN; ++j)
+#pragma unroll
+            for (int a = 0; a < 2; ++a) {
+              n_in_dec += __popcll(__ballot(own_v[j][a] && in[j][a] && !refine[j][a]) & umask);
+              pos[j][a] = n_ref + __popcll(rb[j][a] & umask & below);
+              n_ref += __popcll(rb[j][a] & umask);
+            }
+          uint32_t rkey[OWN][2];
 #pragma unroll
           for (int j = 0; j < OWN; ++j)
 #pragma unroll
             for (int a = 0; a < 2; ++a) {
               const int m = h + j * G;
-              float s = 0.f;
+              float sv = 0.f;
 #pragma unroll
-              for (int mm = 0; mm < KM; ++mm) s = mm == m ? sc[mm][a] : s;
-              own_s[j][a] = refine[j][a] ? s : (in[j][a] ? -kNegInf : kNegInf);
-              const int c = 8 * m + 2 * g + a;
-              if (own_v[j][a]) s_key[wave][xo][c] = topk_key(own_s[j][a], c);
+              for (int mm = 0; mm < KM; ++mm) sv = mm == m ? sc[mm][a] : sv;
+              rkey[j][a] = topk_key(sv, 8 * m + 2 * g + a);
+              if (refine[j][a]) s_key[wave][xo][pos[j][a]] = rkey[j][a];
             }
+          if (h == 0 && g == 0) {  // one lane per unit pads the slots after its undecided keys
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s_key[wave][xo][n_ref + e] = 0u;
+          }
           __threadfence_block();
-          owned_in();
+          int rank[OWN][2];
+#pragma unroll
+          for (int j = 0; j < OWN; ++j)
+#pragma unroll
+            for (int a = 0; a < 2; ++a) rank[j][a] = n_in_dec;
+          for (int c = 0; c < n_ref; c += 4) {
+            const uint4 v = *reinterpret_cast<const uint4*>(&s_key[wave][xo][c]);
+#pragma unroll
+            for (int j = 0; j < OWN; ++j)
+#pragma unroll
+              for (int a = 0; a < 2; ++a)
+                rank[j][a] += (v.x > rkey[j][a]) + (v.y > rkey[j][a]) + (v.z > rkey[j][a]) + (v.w > rkey[j][a]);
+          }
+#pragma unroll
+          for (int j = 0; j < OWN; ++j)
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+              if (refine[j][a]) in[j][a] = rank[j][a] < K;
         }
 #pragma unroll
         for (int j = 0; j < OWN; ++j)
