@@ -179,6 +179,67 @@ __global__ __launch_bounds__(256) void pool_upper_kernel(int first_level, Levels
   }
 }
 
+// The same levels when no sums are kept and the first input level has at most kUpperLdsRows nodes:
+// that level's means are read into LDS once and every level above is built there (two barriers per
+// level instead of a global round trip), each level's means also written out. Same arithmetic per
+// node as pool_upper_kernel.
+constexpr int kUpperLdsRows = 256;
+template <int D>
+__global__ __launch_bounds__(256) void pool_upper_lds_kernel(int first_level, Levels lv, int C, LensArg lens, int N,
+                                                             float* __restrict__ mean) {
+  constexpr int CH = D / 8;
+  __shared__ __align__(16) float s_m[kUpperLdsRows][D];
+  const int bh = blockIdx.x;
+  const int b = bh / lens.hkv;
+  const long long len = lens.has ? lens.len[b] : N;
+  const long long head_row = (long long)bh * lv.nodes;
+  {
+    const int n_in = lv.n[first_level - 1];
+    const float* src = mean + (head_row + lv.off[first_level - 1]) * D;
+    for (int x = threadIdx.x; x < n_in * (D / 4); x += blockDim.x)
+      *reinterpret_cast<float4*>(&s_m[x / (D / 4)][4 * (x % (D / 4))]) = *reinterpret_cast<const float4*>(src + 4 * x);
+  }
+  __syncthreads();
+  for (int l = first_level; l < lv.n_levels; ++l) {
+    const long long cspan = (long long)C << (l - 1);
+    const int items = lv.n[l] * CH;
+    constexpr int IPT = (kUpperLdsRows / 2) * CH / 256;  // items per thread, at most
+    float res[IPT > 0 ? IPT : 1][8];
+#pragma unroll
+    for (int q = 0; q < (IPT > 0 ? IPT : 1); ++q) {
+      const int it = threadIdx.x + 256 * q;
+      if (it < items) {
+        const int j = it / CH, ch = it % CH;
+        const long long c0 = 2LL * j, c1 = 2LL * j + 1;
+        const bool has1 = c1 < lv.n[l - 1];
+        const float w0 = (float)node_count(len, 0, c0, cspan);
+        const float w1 = has1 ? (float)node_count(len, 0, c1, cspan) : 0.f;
+        const float wt = w0 + w1;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float a = s_m[c0][ch * 8 + e], bb = has1 ? s_m[has1 ? c1 : c0][ch * 8 + e] : 0.f;
+          res[q][e] = wt > 0.f ? (w0 * a + w1 * bb) / wt : 0.f;
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < (IPT > 0 ? IPT : 1); ++q) {
+      const int it = threadIdx.x + 256 * q;
+      if (it < items) {
+        const int j = it / CH, ch = it % CH;
+        float* mo = mean + (head_row + lv.off[l] + j) * D + ch * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          s_m[j][ch * 8 + e] = res[q][e];
+          mo[e] = res[q][e];
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
 // fp32 means -> bf16 hi and lo planes: row (head_row + node) holds hi[d] then lo[d], with
 // hi = rne(m) and lo = rne(m - hi), so hi + lo carries about 16 significant bits of m.
 __global__ __launch_bounds__(256) void split_hilo_kernel(const float* __restrict__ mean, long long rows, int D,
@@ -274,8 +335,12 @@ static hipError_t launch_pool_t(const T* k, const PyrDims& pd, LensArg lens, int
   hipLaunchKernelGGL((pool_subtree_kernel<T, D>), dim3(grid), dim3(256), 0, st, k, pd.N, nsub, pd.lv, pd.C, lens,
                      sub_top, mean, sum);
   if (max_level > sub_top) {
-    hipLaunchKernelGGL((pool_upper_kernel<D>), dim3(pd.BH), dim3(256), 0, st, sub_top + 1, pd.lv, pd.C, lens, pd.N,
-                       mean, sum);
+    if (!sum && pd.lv.n[sub_top] <= kUpperLdsRows)
+      hipLaunchKernelGGL((pool_upper_lds_kernel<D>), dim3(pd.BH), dim3(256), 0, st, sub_top + 1, pd.lv, pd.C, lens,
+                         pd.N, mean);
+    else
+      hipLaunchKernelGGL((pool_upper_kernel<D>), dim3(pd.BH), dim3(256), 0, st, sub_top + 1, pd.lv, pd.C, lens,
+                         pd.N, mean, sum);
   }
   return hipGetLastError();
 }
