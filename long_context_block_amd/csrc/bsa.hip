@@ -147,48 +147,55 @@ __global__ __launch_bounds__(256) void bsa_kernel(BsaParams<T> p) {
     s_ix[wave][r16][grp * KMAX + e] = e < p.K ? bj[e] : 0x7fffffff;
   }
   __threadfence_block();
+  constexpr int NH = (4 * KMAX + 63) / 64;  // candidates per lane
   for (int c = 0; c < 16; ++c) {
     const int pos = i0 + c;
     if (pos >= p.N) break;
     const long long u = bh * p.N + pos;
-    // 4*KMAX <= 128 candidates: two per lane
-    float cs[2];
-    int cj[2];
+    float cs[NH];
+    int cj[NH];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < NH; ++h) {
       const int x = lane + 64 * h;
       const bool in = x < 4 * KMAX;
       cs[h] = in ? s_sc[wave][c][x] : kNegInf;
       cj[h] = in ? s_ix[wave][c][x] : 0x7fffffff;
     }
-    int rank[2] = {0, 0};
+    int rank[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) rank[h] = 0;
     for (int y = 0; y < 4 * KMAX; ++y) {
       const float ys = s_sc[wave][c][y];
       const int yj = s_ix[wave][c][y];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) rank[h] += bsa_better(ys, yj, cs[h], cj[h]);
+      for (int h = 0; h < NH; ++h) rank[h] += bsa_better(ys, yj, cs[h], cj[h]);
     }
-    // kept: rank < K and a real leaf; output position = number of kept leaves with a smaller index
-    int opos[2] = {0, 0};
-    bool kp[2];
+    // kept: rank < K and a real leaf. The lane lists hold disjoint leaves, so a kept leaf's output
+    // position is the number of kept leaves with a smaller index: counted over the kept lanes only
+    // (at most K of them, a scalar loop over the ballot bits).
+    bool kp[NH];
+    unsigned long long km[NH];
+    int nkept = 0, opos[NH];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) kp[h] = rank[h] < p.K && cj[h] != 0x7fffffff;
-    const unsigned long long m0 = __ballot(kp[0]);
-    const unsigned long long m1 = __ballot(kp[1]);
-    const int nkept = __popcll(m0) + __popcll(m1);
+    for (int h = 0; h < NH; ++h) {
+      kp[h] = rank[h] < p.K && cj[h] != 0x7fffffff;
+      km[h] = __ballot(kp[h]);
+      nkept += __popcll(km[h]);
+      opos[h] = 0;
+    }
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      int below = 0;
-      for (int y = 0; y < 128; ++y) {
-        const int src = y & 63;
-        const bool yk = (y < 64 ? (m0 >> src) & 1ull : (m1 >> src) & 1ull) != 0;
-        const int yj = readlane(y < 64 ? cj[0] : cj[1], src);
-        below += yk && yj < cj[h];
+    for (int hh = 0; hh < NH; ++hh) {
+      unsigned long long mm = km[hh];
+      while (mm) {
+        const int y = __builtin_ctzll(mm);
+        mm &= mm - 1ull;
+        const int yj = readlane(cj[hh], y);
+#pragma unroll
+        for (int h = 0; h < NH; ++h) opos[h] += yj < cj[h];
       }
-      opos[h] = below;
     }
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < NH; ++h)
       if (kp[h]) p.sel[u * p.K + opos[h]] = cj[h];
     if (lane < p.K && lane >= nkept) p.sel[u * p.K + lane] = -1;
   }
