@@ -171,6 +171,27 @@ def _topk_order(cands: list[int], scores: np.ndarray) -> list[int]:
     return sorted(range(len(cands)), key=lambda p: (-scores[p], cands[p]))
 
 
+def _level_margin(scores: np.ndarray, order: list[int], K: int) -> float:
+    """Gap between the K-th and the (K+1)-th best score of one scored level."""
+    return scores[order[K - 1]] - scores[order[K]]
+
+
+def _unit_margin(level_margins: dict) -> float:
+    """A unit's margin: the smallest level gap over every level that had more than K candidates
+    (+inf if none had). A near-tie at a coarse level changes the candidates below it, so every scored
+    level counts."""
+    return min(level_margins.values(), default=math.inf)
+
+
+def _selected_lse(active: list[int], leaf_head_lse: dict, G: int, K: int) -> np.ndarray:
+    """[G, K] per-head leaf LSE of the selected leaves, column s for the s-th selected leaf in
+    ascending order, -inf for padding."""
+    out = np.full((G, K), NEG_INF)
+    for s_, j in enumerate(active):
+        out[:, s_] = leaf_head_lse[j]
+    return out
+
+
 @dataclasses.dataclass
 class UnitSelection:
     sel: np.ndarray  # [K] ascending leaf indices, -1 padded
@@ -178,6 +199,7 @@ class UnitSelection:
     margin: float  # min over levels with > K candidates of S_(K) - S_(K+1); +inf if none
     kept: dict  # level -> sorted kept node list
     leaf_scores: dict  # leaf -> summed score, for the leaf candidates that were scored
+    level_margins: dict = dataclasses.field(default_factory=dict)  # scored level -> S_(K) - S_(K+1)
 
 
 # ----------------------------------------------------------------------------------------------
@@ -194,7 +216,7 @@ def select_unit(qg: np.ndarray, k: np.ndarray, pyr: Pyramid, i: int, K: int, sca
     assert 0 <= i < n
     kept = {pyr.root_level: [0]}
     active = [0]
-    margin = math.inf
+    level_margins = {}
     leaf_scores = {}
     leaf_head_lse = {}
     for l in range(pyr.root_level - 1, -1, -1):
@@ -213,18 +235,17 @@ def select_unit(qg: np.ndarray, k: np.ndarray, pyr: Pyramid, i: int, K: int, sca
             else:
                 scores = np.array([node_lse_per_head(qg, pyr, l, c, i, scale).sum() for c in cand])
             order = _topk_order(cand, scores)
-            margin = min(margin, scores[order[K - 1]] - scores[order[K]])
+            level_margins[l] = _level_margin(scores, order, K)
             active = sorted(cand[p] for p in order[:K])
         kept[l] = list(active)
     if pyr.root_level == 0:
         # a single leaf: it is the whole selection
         leaf_head_lse[0] = leaf_lse_per_head(qg, k, 0, i, C, scale, n)
     sel = np.full(K, -1, dtype=np.int64)
-    sel_lse = np.full((G, K), NEG_INF)
-    for s_, j in enumerate(active):
-        sel[s_] = j
-        sel_lse[:, s_] = leaf_head_lse[j]
-    return UnitSelection(sel=sel, sel_lse=sel_lse, margin=margin, kept=kept, leaf_scores=leaf_scores)
+    sel[:len(active)] = active
+    return UnitSelection(sel=sel, sel_lse=_selected_lse(active, leaf_head_lse, G, K),
+                         margin=_unit_margin(level_margins), kept=kept, leaf_scores=leaf_scores,
+                         level_margins=level_margins)
 
 
 # ----------------------------------------------------------------------------------------------
@@ -262,7 +283,7 @@ def bsa_select_unit(qg: np.ndarray, leaf_means: np.ndarray, i: int, C: int, K: i
         sel[:len(cand)] = cand
         return sel, math.inf
     order = _topk_order(cand, scores)
-    margin = scores[order[K - 1]] - scores[order[K]]
+    margin = _level_margin(scores, order, K)
     sel[:K] = sorted(cand[p] for p in order[:K])
     return sel, margin
 

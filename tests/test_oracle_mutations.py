@@ -21,6 +21,9 @@ def _pins_pass() -> bool:
         lambda: P.test_attention_all_blocks_equals_dense_sdpa(),
         lambda: P.test_selection_invariants(),
         lambda: P.test_exact_ties_break_to_lowest_index(4),
+        lambda: P.test_sel_lse_equals_library_lse_over_selected_tokens(3, "ar1"),
+        lambda: P.test_walk_equals_dense_all_levels_bruteforce(4, 2),
+        lambda: P.test_bsa_matches_dense_mean_key_scores(),
     ]
     for c in checks:
         try:
@@ -88,6 +91,25 @@ def _mut_attend_no_scale(qg, k, v, sel, i, C, scale, n_tokens):
     return _orig_scale_attend(qg, k, v, sel, i, C, 1.0, n_tokens)
 
 
+def _mut_margin_max_over_levels(level_margins):
+    return max(level_margins.values(), default=math.inf)
+
+
+def _mut_margin_leaf_level_only(level_margins):
+    return level_margins.get(0, math.inf)
+
+
+def _mut_margin_off_by_one_rank(scores, order, K):
+    return scores[order[K]] - scores[order[K + 1]] if len(order) > K + 1 else math.inf
+
+
+def _mut_sel_lse_reversed(active, leaf_head_lse, G, K):
+    out = np.full((G, K), -np.inf)
+    for s_, j in enumerate(reversed(active)):
+        out[:, s_] = leaf_head_lse[j]
+    return out
+
+
 MUTANTS = {
     "topk_ascending": ("_topk_order", _mut_topk_ascending),
     "tiebreak_high_index": ("_topk_order", _mut_tiebreak_high_index),
@@ -98,6 +120,10 @@ MUTANTS = {
     "pyramid_sums_not_means": ("build_pyramid", _mut_pyramid_sums),
     "pyramid_unweighted_ragged": ("build_pyramid", _mut_pyramid_unweighted),
     "attention_without_scale": ("attend_unit", _mut_attend_no_scale),
+    "margin_max_over_levels": ("_unit_margin", _mut_margin_max_over_levels),
+    "margin_leaf_level_only": ("_unit_margin", _mut_margin_leaf_level_only),
+    "margin_off_by_one_rank": ("_level_margin", _mut_margin_off_by_one_rank),
+    "sel_lse_misaligned_with_sel": ("_selected_lse", _mut_sel_lse_reversed),
 }
 
 

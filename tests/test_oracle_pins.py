@@ -19,6 +19,13 @@ def _rng(seed=0):
     return np.random.default_rng(seed)
 
 
+def _same_margin(a, b, tol=1e-9):
+    """Both +inf (no scored level), or equal up to float64 rounding of the scores."""
+    if math.isinf(a) or math.isinf(b):
+        return a == b
+    return abs(a - b) <= tol * (1.0 + abs(b))
+
+
 # ---------------------------------------------------------------- C1: LogSumExp
 def test_lse_matches_direct_and_library():
     x = _rng(1).uniform(-50, 50, size=(37, 19))
@@ -149,12 +156,15 @@ def test_walk_equals_flat_exact_when_k_covers_level1(K):
     for i in range(1024):
         us = O.select_unit(q[:, i], k, pyr, i, K, scale)
         sel_b, gap = brute[i]
+        # with K >= n_1 only the leaf level can be scored, so the unit's margin is the leaf gap
+        assert _same_margin(us.margin, gap), (i, us.margin, gap)
         if gap < 1e-9:
             continue
         got = [j for j in us.sel.tolist() if j >= 0]
         assert got == sel_b, (i, got, sel_b)
-        fe, _ = O.flat_exact_select_unit(q[:, i], k, i, 32, K, scale)
+        fe, fgap = O.flat_exact_select_unit(q[:, i], k, i, 32, K, scale)
         assert [j for j in fe.tolist() if j >= 0] == sel_b
+        assert _same_margin(fgap, gap)
         if K == 32:
             assert got == list(range(i // 32 + 1))
         n_checked += 1
@@ -169,6 +179,7 @@ def test_walk_gqa_equals_flat_exact_when_k_covers_level1():
     for i in range(0, 640, 3):
         us = O.select_unit(q[:, i], k, pyr, i, K, scale)
         sel_b, gap = brute[i]
+        assert _same_margin(us.margin, gap), (i, us.margin, gap)
         if gap >= 1e-9:
             assert [j for j in us.sel.tolist() if j >= 0] == sel_b
 
@@ -229,6 +240,8 @@ def test_walk_equals_dense_two_level_bruteforce(K, G):
         if gap < 1e-9:
             continue
         assert [j for j in us.sel.tolist() if j >= 0] == sel_b, i
+        # the margin is the smaller of the level-1 and leaf gaps (each +inf when unscored)
+        assert _same_margin(us.margin, gap), (i, us.margin, gap)
         n_ok += 1
     assert n_ok > 400
 
@@ -359,6 +372,8 @@ def test_bsa_matches_dense_mean_key_scores():
         o = np.lexsort((np.arange(e), -f))
         want = sorted(o[:6].tolist())
         sel, gap = O.bsa_select_unit(q[:, i], leaf_mean, i, 32, 6, scale)
+        dense_gap = f[o[5]] - f[o[6]] if e > 6 else math.inf
+        assert _same_margin(gap, dense_gap), (i, gap, dense_gap)
         if e > 6 and gap < 1e-9:
             continue
         assert [j for j in sel.tolist() if j >= 0] == want
@@ -377,3 +392,97 @@ def test_exact_ties_break_to_lowest_index(K):
         us = O.select_unit(q, k, pyr, i, K, 0.25)
         assert us.sel.tolist() == list(range(K)), (i, us.sel)
         assert us.margin == 0.0
+
+
+# ---------------------------------------------------------------- per-head leaf LSEs of the selection
+@pytest.mark.parametrize("G,keys", [(1, "iid"), (3, "ar1")])
+def test_sel_lse_equals_library_lse_over_selected_tokens(G, keys):
+    """Column s of sel_lse is, for each head, scipy's LSE of s * q_h . k_t over the tokens t <= i of the
+    s-th selected leaf (ascending), and -inf past the selection."""
+    q, k, v, scale = _tiny(N=777, d=32, C=32, G=G, keys=keys, seed=41)
+    pyr = O.build_pyramid(k, 32)
+    K = 5
+    for i in range(0, 777, 5):
+        us = O.select_unit(q[:, i], k, pyr, i, K, scale)
+        row = scale * np.einsum("gd,td->gt", q[:, i], k[: i + 1])  # the causal score row, [G, i+1]
+        for s_, j in enumerate(us.sel.tolist()):
+            if j < 0:
+                assert np.all(us.sel_lse[:, s_] == -np.inf)
+                continue
+            want = scipy.special.logsumexp(row[:, j * 32:min(i + 1, (j + 1) * 32)], axis=-1)
+            np.testing.assert_allclose(us.sel_lse[:, s_], want, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------- dense brute force of the whole walk
+def _dense_walk(q, k, C, K, scale):
+    """Independent dense brute force of the walk at every level. Node means come straight from the raw
+    keys of each node's span; every node's score for every query is one dense masked matrix (scipy
+    LSE over eligible children, or over the leaf's tokens t <= i); the walk is boolean masks over whole
+    levels, children by np.repeat, Top-K by lexsort. Returns per query (sel, per-head leaf LSEs of
+    sel, margin = smallest gap over the scored levels)."""
+    G, N, d = q.shape
+    n = [-(-N // C)]
+    while n[-1] > 1:
+        n.append(-(-n[-1] // 2))
+    L = len(n) - 1
+    means = []
+    for l in range(L + 1):
+        w = C * 2 ** l
+        means.append(np.stack([k[j * w:min(N, (j + 1) * w)].mean(axis=0) for j in range(n[l])]))
+    pos = np.arange(N)
+    elig = [(np.arange(n[l])[None, :] * (C * 2 ** l)) <= pos[:, None] for l in range(L + 1)]  # [N, n_l]
+    S = {}
+    for l in range(1, L + 1):
+        X = scale * np.einsum("gnd,jd->gnj", q, means[l - 1])
+        X = np.where(elig[l - 1][None], X, -np.inf)
+        Xp = np.full((G, N, 2 * n[l]), -np.inf)
+        Xp[:, :, :n[l - 1]] = X
+        S[l] = scipy.special.logsumexp(Xp.reshape(G, N, n[l], 2), axis=-1).sum(axis=0)  # [N, n_l]
+    T = scale * np.einsum("gnd,td->gnt", q, k)
+    T = np.where(np.tril(np.ones((N, N), dtype=bool))[None], T, -np.inf)
+    Tp = np.full((G, N, n[0] * C), -np.inf)
+    Tp[:, :, :N] = T
+    LH = scipy.special.logsumexp(Tp.reshape(G, N, n[0], C), axis=-1)  # [G, N, n_0], -inf when no token
+    S[0] = LH.sum(axis=0)
+    out = []
+    for i in range(N):
+        kept = np.ones(1, dtype=bool)  # the root
+        gaps = []
+        for l in range(L - 1, -1, -1):
+            cand = np.repeat(kept, 2)[:n[l]] & elig[l][i]
+            idx = np.flatnonzero(cand)
+            if idx.size > K:
+                sc = S[l][i, idx]
+                order = np.lexsort((idx, -sc))
+                gaps.append(sc[order[K - 1]] - sc[order[K]])
+                kept = np.zeros(n[l], dtype=bool)
+                kept[idx[order[:K]]] = True
+            else:
+                kept = cand
+        sel = np.flatnonzero(kept)
+        out.append((sel.tolist(), LH[:, i, sel], min(gaps) if gaps else math.inf))
+    return out
+
+
+@pytest.mark.parametrize("K,G", [(3, 1), (4, 2), (6, 4)])
+def test_walk_equals_dense_all_levels_bruteforce(K, G):
+    """N = 2000, C = 32: 63 leaves (the last one ragged) and 7 levels, so K = 3, 4, 6 score 5, 4 and 4
+    levels. Selection, per-head leaf LSEs and margin all equal the dense brute force."""
+    N, C = 2000, 32
+    q, k, v, scale = _tiny(N=N, d=32, C=C, G=G, keys="ar1", seed=51 + K)
+    pyr = O.build_pyramid(k, C)
+    brute = _dense_walk(q, k, C, K, scale)
+    n_ok = n_deep = 0
+    for i in range(N):
+        sel_b, lse_b, gap = brute[i]
+        us = O.select_unit(q[:, i], k, pyr, i, K, scale)
+        if gap < 1e-9:
+            continue
+        got = [j for j in us.sel.tolist() if j >= 0]
+        assert got == sel_b, (i, got, sel_b)
+        assert _same_margin(us.margin, gap), (i, us.margin, gap, us.level_margins)
+        np.testing.assert_allclose(us.sel_lse[:, :len(got)], lse_b, rtol=1e-12, atol=1e-12)
+        n_ok += 1
+        n_deep += len(us.level_margins) >= 3
+    assert n_ok > 0.9 * N
+    assert n_deep > 0.5 * N  # most units are scored at three or more levels
