@@ -1,9 +1,15 @@
 """Shared plumbing for the GPU parity tests: upload seeded inputs, run the HIP path through the C ABI,
-and compare with the float64 oracle unit by unit."""
+and compare with the float64 oracle unit by unit.
+
+The oracle runs in a pool of forked worker processes (one per host core the test may use, at most 16).
+The workers never touch the GPU: they read the inputs and the GPU's outputs, which the parent holds in
+host memory before forking, and each returns a report for its share of the units."""
 from __future__ import annotations
 
 import dataclasses
 import math
+import multiprocessing as mp
+import os
 import sys
 
 import numpy as np
@@ -16,11 +22,50 @@ from long_context_block_amd import pisa as P
 DEV = "cuda"
 TOL_ATTN = {"fp32": 1e-5, "bf16": 2e-2}
 MARGIN = 1e-3
+MAX_WORKERS = 16
+
+# Lines collected for the end-of-run summary (printed by conftest's terminal-summary hook, so they
+# appear in the output of a quiet run too).
+SUMMARY: list[str] = []
 
 
 def say(msg: str):
     print(msg, flush=True)
     sys.stdout.flush()
+
+
+def summary(msg: str):
+    say(msg)
+    SUMMARY.append(msg)
+
+
+def n_workers() -> int:
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    return max(1, min(MAX_WORKERS, cores))
+
+
+# Context read by the forked workers: set by the parent right before the pool forks.
+_CTX: dict = {}
+
+
+def _worker_init():
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(limits=1)
+    except Exception:  # pragma: no cover
+        pass
+
+
+def pool_map(fn, tasks):
+    """fn over tasks in forked worker processes (in order). fn and the data it reads from _CTX are
+    inherited by the fork; only the tasks and the results are pickled."""
+    if len(tasks) <= 1 or n_workers() == 1:
+        return [fn(t) for t in tasks]
+    with mp.get_context("fork").Pool(n_workers(), initializer=_worker_init) as pool:
+        return pool.map(fn, tasks, chunksize=1)
 
 
 def to_device(t: I.Tensor) -> torch.Tensor:
@@ -56,21 +101,26 @@ def run_gpu(pf: I.Prefill, q_tile: int, *, lse=True, attn=True, bsa=False, dev=N
     sel_lse = torch.empty((pf.B, pf.Hq, pf.N, pf.K), dtype=torch.float32, device=DEV) if lse else None
     ws = P.alloc_workspace(s, P.PISA_OP_SELECT)
     P.pisa_select(s, q, k, pyr, sel, sel_lse, ws)
+    del ws
     o = o_lse = None
     if attn:
         o = torch.empty_like(q)
         o_lse = torch.empty((pf.B, pf.Hq, pf.N), dtype=torch.float32, device=DEV)
         wsa = P.alloc_workspace(s, P.PISA_OP_ATTN)
         P.pisa_sparse_attn(s, q, k, v, sel, o, o_lse, wsa)
+        del wsa
     bsel = None
     if bsa:
         bsel = torch.empty_like(sel)
         wsb = P.alloc_workspace(s, P.PISA_OP_BSA)
         P.bsa_select(s, q, k, bsel, wsb)
+        del wsb
     torch.cuda.synchronize()
     out = GpuOut(pyr=pyr.cpu().numpy(), sel=sel.cpu().numpy(), sel_lse=sel_lse.cpu().numpy() if lse else None,
                  o=o.float().cpu().numpy() if attn else None, o_lse=o_lse.cpu().numpy() if attn else None,
                  bsa=bsel.cpu().numpy() if bsa else None)
+    del q, k, v, pyr, sel, sel_lse, o, o_lse, bsel
+    torch.cuda.empty_cache()
     return out
 
 
@@ -117,17 +167,52 @@ def units_sample(pf, n, seed=0, extra=()):
     return out
 
 
+def units_stratified(pf, frac, seed=0, extra=()):
+    """A seeded sample of at least `frac` of the units, stratified by KV head and by position (one draw
+    in every block of round(1 / frac) consecutive positions), plus the head edges and `extra`."""
+    rng = np.random.default_rng(seed)
+    step = max(1, int(round(1.0 / frac)))
+    picks = set()
+    for b in range(pf.B):
+        for r in range(pf.Hkv):
+            base = (b * pf.Hkv + r) * pf.N
+            starts = np.arange(0, pf.N, step)
+            offs = rng.integers(0, step, size=starts.size)
+            for i in np.minimum(starts + offs, pf.N - 1):
+                picks.add(base + int(i))
+    return units_sample(pf, 0, seed=seed, extra=sorted(picks | set(int(u) for u in extra)))
+
+
 @dataclasses.dataclass
 class Report:
     n_units: int = 0
     n_decided: int = 0
+    n_undecided_equal: int = 0  # undecided units whose GPU selection still equals the oracle's
     sel_mismatch: list = dataclasses.field(default_factory=list)
     invariant_fail: list = dataclasses.field(default_factory=list)
     lse_err: float = 0.0
     attn_err: float = 0.0
     olse_err: float = 0.0
+    bsa_units: int = 0
     bsa_mismatch: list = dataclasses.field(default_factory=list)
     bsa_decided: int = 0
+
+    def merge(self, o: "Report"):
+        self.n_units += o.n_units
+        self.n_decided += o.n_decided
+        self.n_undecided_equal += o.n_undecided_equal
+        self.sel_mismatch += o.sel_mismatch[:20]
+        self.invariant_fail += o.invariant_fail[:20]
+        self.lse_err = max(self.lse_err, o.lse_err)
+        self.attn_err = max(self.attn_err, o.attn_err)
+        self.olse_err = max(self.olse_err, o.olse_err)
+        self.bsa_units += o.bsa_units
+        self.bsa_mismatch += o.bsa_mismatch[:20]
+        self.bsa_decided += o.bsa_decided
+
+    @property
+    def decided_frac(self) -> float:
+        return self.n_decided / max(1, self.n_units)
 
 
 def check_invariants(sel_row, i, C, K):
@@ -139,11 +224,30 @@ def check_invariants(sel_row, i, C, K):
     return ok
 
 
-def compare(pf: I.Prefill, g: GpuOut, units, oc: OracleCache | None = None, check_attn=True, check_bsa=False) -> Report:
-    oc = oc or OracleCache(pf)
+def invariant_violations(sel: np.ndarray, C: int) -> np.ndarray:
+    """Vectorised selection invariants over every unit of sel [..., N, K]: the selected leaves are a
+    left-packed prefix of min(K, i // C + 1) entries, strictly ascending and eligible (j C <= i), and the
+    rest is -1. Returns the flat indices (over the leading dims and N) of the units that violate any."""
+    *lead, N, K = sel.shape
+    s = sel.reshape(-1, N, K).astype(np.int64)
+    i = np.arange(N, dtype=np.int64)[None, :, None]
+    valid = s >= 0
+    want = np.minimum(K, np.arange(N) // C + 1)[None, :]
+    bad = valid.sum(-1) != want
+    bad |= (valid[..., 1:] & ~valid[..., :-1]).any(-1)  # a selected entry after a padding entry
+    bad |= (valid[..., 1:] & (np.diff(s, axis=-1) <= 0)).any(-1)  # not strictly ascending
+    bad |= (valid & (s * C > i)).any(-1)  # not eligible
+    bad |= (~valid & (s != -1)).any(-1)  # padding other than -1
+    return np.flatnonzero(bad.reshape(-1))
+
+
+def _compare_chunk(task) -> Report:
+    """Worker: compare the units of one chunk. Reads the inputs and the GPU outputs from _CTX."""
+    pf, g, check_attn, check_bsa = _CTX["pf"], _CTX["g"], _CTX["attn"], _CTX["bsa"]
+    oc = _CTX["oc"]
     rep = Report()
     G, C, K = pf.G, pf.C, pf.K
-    for (b, r, i) in units:
+    for (b, r, i) in task:
         k, v, pyr = oc.head(b, r)
         qg = oc.q(b, r, i)
         us = O.select_unit(qg, k, pyr, i, K, pf.scale)
@@ -159,6 +263,8 @@ def compare(pf: I.Prefill, g: GpuOut, units, oc: OracleCache | None = None, chec
                 nsel = int((us.sel >= 0).sum())
                 e = np.abs(g.sel_lse[b, r * G:(r + 1) * G, i, :nsel] - us.sel_lse[:, :nsel]).max()
                 rep.lse_err = max(rep.lse_err, float(e))
+        elif gsel.tolist() == us.sel.tolist():
+            rep.n_undecided_equal += 1
         if check_attn and g.o is not None:
             o_ref, lse_ref = O.attend_unit(qg, k, v, gsel, i, C, pf.scale, pf.N)
             e = np.abs(g.o[b, r * G:(r + 1) * G, i] - o_ref).max()
@@ -167,6 +273,7 @@ def compare(pf: I.Prefill, g: GpuOut, units, oc: OracleCache | None = None, chec
             rep.olse_err = max(rep.olse_err, float(el))
         if check_bsa and g.bsa is not None:
             bsel, bm = O.bsa_select_unit(qg, pyr.means[0], i, C, K, pf.scale)
+            rep.bsa_units += 1
             if bm >= MARGIN:
                 rep.bsa_decided += 1
                 if g.bsa[b, r, i].tolist() != bsel.tolist():
@@ -176,13 +283,39 @@ def compare(pf: I.Prefill, g: GpuOut, units, oc: OracleCache | None = None, chec
     return rep
 
 
-def assert_report(rep: Report, dtype: str, check_attn=True, pyr_err=None):
-    say(f"units={rep.n_units} decided={rep.n_decided} sel_mismatch={len(rep.sel_mismatch)} "
-        f"invariant_fail={len(rep.invariant_fail)} lse_err={rep.lse_err:.3g} attn_err={rep.attn_err:.3g} "
-        f"olse_err={rep.olse_err:.3g} bsa_decided={rep.bsa_decided} bsa_mismatch={len(rep.bsa_mismatch)}")
+def compare(pf: I.Prefill, g: GpuOut, units, oc: OracleCache | None = None, check_attn=True, check_bsa=False,
+            chunk=512) -> Report:
+    """The oracle on `units` (a list of (b, r, i)) in the worker pool, compared with the GPU outputs."""
+    oc = oc or OracleCache(pf)
+    # the pyramids of the touched heads are built once, before the fork, and shared by the workers
+    for (b, r) in sorted({(b, r) for (b, r, _) in units}):
+        oc.head(b, r)
+    units = list(units)
+    tasks = [units[x:x + chunk] for x in range(0, len(units), chunk)]
+    _CTX.update(pf=pf, g=g, attn=check_attn, bsa=check_bsa, oc=oc)
+    try:
+        reps = pool_map(_compare_chunk, tasks)
+    finally:
+        _CTX.clear()
+    rep = Report()
+    for r_ in reps:
+        rep.merge(r_)
+    return rep
+
+
+def assert_report(rep: Report, dtype: str, check_attn=True, min_decided=0.9, label=""):
+    msg = (f"{label} units={rep.n_units} decided={rep.n_decided} ({rep.decided_frac:.4f}, floor {min_decided}) "
+           f"undecided_equal={rep.n_undecided_equal} sel_mismatch={len(rep.sel_mismatch)} "
+           f"invariant_fail={len(rep.invariant_fail)} lse_err={rep.lse_err:.3g} attn_err={rep.attn_err:.3g} "
+           f"olse_err={rep.olse_err:.3g}")
+    if rep.bsa_units:
+        msg += f" bsa_units={rep.bsa_units} bsa_decided={rep.bsa_decided} bsa_mismatch={len(rep.bsa_mismatch)}"
+    summary(msg.strip())
     assert not rep.invariant_fail, rep.invariant_fail[:5]
     assert not rep.sel_mismatch, rep.sel_mismatch[:5]
     assert not rep.bsa_mismatch, rep.bsa_mismatch[:5]
+    assert rep.n_units > 0
+    assert rep.decided_frac >= min_decided, (rep.decided_frac, min_decided)
     assert rep.lse_err <= 2e-4 if dtype == "bf16" else rep.lse_err <= 2e-5
     if check_attn:
         assert rep.attn_err <= TOL_ATTN[dtype], rep.attn_err
