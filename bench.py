@@ -6,6 +6,11 @@ and the flat block selection used for comparison. The headline value is routed q
 of the pyramid selection (B * Hq * N / (pyramid + selection seconds)). Per-stage times come from HIP
 events recorded by the library around each kernel launch on the stream it uses.
 
+Besides the timed step the line carries: the q_tile 1 selection time, the decode step latency, a
+crossover sweep of the pyramid selection against the flat selection at 16K-256K tokens (prefixes of
+the 256K planted-needle workload, same heads), the needle recall@K at 256K, and the float64 oracle's
+selection rate on the host cores.
+
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -85,45 +90,102 @@ def measured_traffic(workload):
     return {st: e["bytes"] for st, e in t["stages"].items()}
 
 
-def cpu_baseline(pf, seconds_target=15.0, seed=0):
-    """The float64 oracle (as it stands) on a bounded random sample of units, one thread."""
-    import oracle as O
+# ---------------------------------------------------------------- the oracle on the host cores
+# Worker context, set in the parent before the pool forks (the workers never touch the GPU).
+_CTX = {}
+
+
+def _pool_workers():
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    return max(1, min(16, cores))
+
+
+def _pool_init():
     try:
         from threadpoolctl import threadpool_limits
-        limiter = threadpool_limits(limits=1)
+        threadpool_limits(limits=1)
     except Exception:  # pragma: no cover
-        limiter = None
-    rng = np.random.default_rng(seed)
-    U = pf.B * pf.Hkv * pf.N
-    order = rng.permutation(U)
-    heads = {}
-    t0 = time.perf_counter()
-    done = 0
-    t_pyr = 0.0
-    for u in order:
-        bh, i = divmod(int(u), pf.N)
-        b, r = divmod(bh, pf.Hkv)
-        if (b, r) not in heads:
-            tp = time.perf_counter()
-            k = pf.k.f64((b, r))
-            v = pf.v.f64((b, r))
-            heads[(b, r)] = (k, v, O.build_pyramid(k, pf.C, 2))
-            t_pyr += time.perf_counter() - tp
-        k, v, pyr = heads[(b, r)]
+        pass
+
+
+def _pool_map(fn, tasks):
+    import multiprocessing as mp
+    with mp.get_context("fork").Pool(_pool_workers(), initializer=_pool_init) as pool:
+        return pool.map(fn, tasks, chunksize=1)
+
+
+def _oracle_pyramid(bh):
+    import oracle as O
+    pf = _CTX["pf"]
+    b, r = divmod(bh, pf.Hkv)
+    t = time.perf_counter()
+    O.build_pyramid(pf.k.f64((b, r)), pf.C, 2)
+    return time.perf_counter() - t
+
+
+def _oracle_select(units):
+    """Selections of a list of units (b, r, i); returns (seconds in select_unit, undecided count)."""
+    import oracle as O
+    pf, heads = _CTX["pf"], _CTX["heads"]
+    el = 0.0
+    und = 0
+    for (b, r, i) in units:
+        k, pyr = heads[(b, r)]
         qg = pf.q.f64((b, slice(r * pf.G, (r + 1) * pf.G), i))
+        t = time.perf_counter()
         us = O.select_unit(qg, k, pyr, i, pf.K, pf.scale)
-        O.attend_unit(qg, k, v, us.sel, i, pf.C, pf.scale, pf.N)
-        done += 1
-        if time.perf_counter() - t0 > seconds_target:
-            break
-    el = time.perf_counter() - t0 - t_pyr
-    if limiter is not None:
-        limiter.unregister() if hasattr(limiter, "unregister") else None
-    qheads_per_s = done * pf.G / el
-    return {"value": qheads_per_s, "unit": "q-heads/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} random units (of {U}) of the same workload: float64 selection walk + sparse "
-                      f"attention per unit, one thread, pyramid build of the touched heads excluded "
-                      f"({t_pyr:.1f}s); value = units*G/s"}
+        el += time.perf_counter() - t
+        und += us.margin < 1e-3
+    return el, und
+
+
+def cpu_baseline(pf, cpu_seconds=20.0, seed=0):
+    """The float64 oracle as it stands: the pyramids of every KV head, then the selection walk of a
+    random sample of units sized to about cpu_seconds of CPU work, both spread over a pool of worker
+    processes on the host cores. value = q-heads / (pyramid wall time + sample wall time scaled to all
+    units), the same quantity as the GPU's routed q-heads/s."""
+    workers = _pool_workers()
+    U = pf.B * pf.Hkv * pf.N
+    rng = np.random.default_rng(seed)
+    _CTX["pf"] = pf
+    try:
+        t = time.perf_counter()
+        pyr_cpu = _pool_map(_oracle_pyramid, list(range(pf.B * pf.Hkv)))
+        t_pyr = time.perf_counter() - t
+        # the walks below read the pyramids built here once (the timed builds ran in the workers)
+        import oracle as O
+        heads = {}
+        for b in range(pf.B):
+            for r in range(pf.Hkv):
+                k = pf.k.f64((b, r))
+                heads[(b, r)] = (k, O.build_pyramid(k, pf.C, 2))
+        _CTX["heads"] = heads
+        # per-unit cost from a short probe, then a sample of about cpu_seconds of CPU work
+        probe = [divmod(int(u), pf.N) for u in rng.choice(U, size=64, replace=False)]
+        probe = [(bh // pf.Hkv, bh % pf.Hkv, i) for bh, i in probe]
+        per_unit = max(_oracle_select(probe)[0] / len(probe), 1e-4)
+        n = int(min(U, max(256, cpu_seconds / per_unit)))
+        picks = np.sort(rng.choice(U, size=n, replace=False))
+        units = [((int(u) // pf.N) // pf.Hkv, (int(u) // pf.N) % pf.Hkv, int(u) % pf.N) for u in picks]
+        chunks = [units[x::workers * 4] for x in range(workers * 4)]
+        t = time.perf_counter()
+        res = _pool_map(_oracle_select, chunks)
+        t_sel = time.perf_counter() - t
+    finally:
+        _CTX.clear()
+    cpu_sel = sum(x[0] for x in res)
+    und = sum(x[1] for x in res)
+    full_s = t_pyr + t_sel * U / n
+    return {"value": round(pf.B * pf.Hq * pf.N / full_s, 1), "unit": "q-heads/s", "cores": workers, "kind": "oracle",
+            "sample": f"float64 oracle in {workers} worker processes (one thread each): pyramids of all "
+                      f"{pf.B * pf.Hkv} KV heads ({t_pyr:.2f} s wall, {sum(pyr_cpu):.2f} s CPU), then the "
+                      f"selection walk of {n} random units of {U} ({t_sel:.2f} s wall, {cpu_sel:.1f} s CPU); "
+                      f"full-problem time extrapolated as pyramid + sample x {U / n:.1f} = {full_s:.1f} s; "
+                      f"{und / n:.3f} of the sampled units are undecided (margin < 1e-3)",
+            "full_problem_s_extrapolated": round(full_s, 2), "undecided_frac_sample": round(float(und) / n, 4)}
 
 
 def decode_latency(P, I, torch, steps_cap=None):
@@ -171,6 +233,116 @@ def decode_latency(P, I, torch, steps_cap=None):
             "step_ms_mean": round(float(t.mean()), 4)}
 
 
+def _needle_oracle(units):
+    """Oracle selections of needle units: recall@K of each against its eligible needle leaves."""
+    import oracle as O
+    pf, heads = _CTX["pf"], _CTX["heads"]
+    out = []
+    for (b, r, i) in units:
+        E = [int(j) for j in pf.needle_leaves[b, r] if j * pf.C <= i]
+        k, pyr = heads[(b, r)]
+        us = O.select_unit(pf.q.f64((b, slice(r * pf.G, (r + 1) * pf.G), i)), k, pyr, i, pf.K, pf.scale)
+        out.append(len(set(us.sel.tolist()) & set(E)) / min(pf.K, len(E)))
+    return out
+
+
+def crossover(P, I, torch, lengths=(16384, 32768, 65536, 131072, 262144), reps=4, oracle_needles=256):
+    """Pyramid selection (pyramid + pisa_select, q_tile 4) against the flat selection (bsa_select, its
+    own leaf pooling included) on prefixes of the 256K planted-needle workload (32 query / 8 KV heads,
+    d 128, C 64, K 16, AR(1) keys), and the needle recall@K of the 256K selection."""
+    import oracle as O
+    log("[bench] crossover: generating prefill_256k_needles")
+    t = time.time()
+    pf = I.make_workload("prefill_256k_needles")
+    log(f"[bench] generated in {time.time() - t:.1f}s")
+    qa = torch.from_numpy(pf.q.data.view(np.int16)).cuda().view(torch.bfloat16)
+    ka = torch.from_numpy(pf.k.data.view(np.int16)).cuda().view(torch.bfloat16)
+    points = []
+    sel_full = None
+    for N in lengths:
+        q = qa if N == pf.N else qa[:, :, :N].contiguous()
+        k = ka if N == pf.N else ka[:, :, :N].contiguous()
+        s = P.make_shape(batch=pf.B, seq_len=N, n_q_heads=pf.Hq, n_kv_heads=pf.Hkv, head_dim=pf.d, block=pf.C,
+                         top_k=pf.K, q_tile=4, dtype=pf.dtype)
+        pyr = torch.empty((P.pyramid_rows(s), pf.d), dtype=torch.float32, device="cuda")
+        sel = torch.empty((pf.B, pf.Hkv, N, pf.K), dtype=torch.int32, device="cuda")
+        bsel = torch.empty_like(sel)
+        ws = P.alloc_workspace(s, P.PISA_OP_SELECT)
+        wsb = P.alloc_workspace(s, P.PISA_OP_BSA)
+
+        def once():
+            P.pisa_build_pyramid(s, k, pyr)
+            P.pisa_select(s, q, k, pyr, sel, None, ws)
+            P.bsa_select(s, q, k, bsel, wsb)
+
+        once()
+        torch.cuda.synchronize()
+        P.pisa_stage_timing(True)
+        for _ in range(reps):
+            once()
+        torch.cuda.synchronize()
+        st = {n: tot / c for n, (tot, c) in P.pisa_stage_times().items()}
+        P.pisa_stage_timing(False)
+        pisa_ms = sum(st.get(n, 0.0) for n in ("pyramid", "route_planes", "route", "regroup_select", "leaf_lse",
+                                                "finalize"))
+        bsa_ms = st.get("bsa_pool", 0.0) + st.get("bsa_select", 0.0)
+        i = np.arange(N, dtype=np.int64)
+        n_levels = int(math.ceil(math.log2(max(1, -(-N // pf.C))))) + 1
+        s_lv = sum((i // (pf.C << l) + 1 > pf.K).astype(np.int64) for l in range(1, n_levels))
+        pisa_flops = pf.B * pf.Hkv * (int(s_lv.sum()) * 4 * pf.K * 2 * pf.G * pf.d +
+                                      int(np.minimum(pf.K, i // (2 * pf.C) + 1).sum()) * 4 * pf.C * pf.G * pf.d)
+        bsa_flops = pf.B * pf.Hkv * int((i // pf.C + 1).sum()) * 2 * pf.d
+        points.append({"seq_len": N, "pisa_selection_ms": round(pisa_ms, 4), "bsa_selection_ms": round(bsa_ms, 4),
+                       "bsa_over_pisa_time": round(bsa_ms / pisa_ms, 3), "pisa_flops": pisa_flops,
+                       "bsa_flops": bsa_flops,
+                       "pisa_stages_ms": {n: round(st[n], 4) for n in sorted(st) if not n.startswith("bsa")}})
+        log(f"[bench] crossover N={N}: pisa {pisa_ms:.3f} ms, bsa {bsa_ms:.3f} ms")
+        if N == pf.N:
+            sel_full = sel.cpu().numpy()
+        del q, k, pyr, sel, bsel, ws, wsb
+        torch.cuda.empty_cache()
+    del qa, ka
+    torch.cuda.empty_cache()
+    res = {"workload": "prefixes of prefill_256k_needles", "n_q_heads": pf.Hq, "n_kv_heads": pf.Hkv,
+           "head_dim": pf.d, "block": pf.C, "top_k": pf.K, "q_tile": 4, "reps": reps, "points": points}
+    if sel_full is not None:
+        # needle recall@K = |sel(r, i) & E| / min(K, |E|), E = the eligible needle leaves, over every
+        # needle query row (GPU) and, on a sample of needle units, for the oracle as well
+        rec, units = [], []
+        for b in range(pf.B):
+            for h in range(pf.Hq):
+                r = h // pf.G
+                leaves = np.asarray(pf.needle_leaves[b, r])
+                for i in pf.needle_queries[b, h]:
+                    E = leaves[leaves * pf.C <= i]
+                    if E.size:
+                        row = sel_full[b, r, int(i)]
+                        rec.append(np.isin(row[row >= 0], E).sum() / min(pf.K, E.size))
+                        if h % pf.G == 0:
+                            units.append((b, r, int(i)))
+        rng = np.random.default_rng(3)
+        pick = [units[x] for x in sorted(rng.choice(len(units), size=min(oracle_needles, len(units)), replace=False))]
+        heads = {}
+        for (b, r) in sorted({(b, r) for (b, r, _) in pick}):
+            kk = pf.k.f64((b, r))
+            heads[(b, r)] = (kk, O.build_pyramid(kk, pf.C, 2))
+        _CTX.update(pf=pf, heads=heads)
+        try:
+            workers = _pool_workers()
+            orc = [x for part in _pool_map(_needle_oracle, [pick[j::workers] for j in range(workers)]) for x in part]
+        finally:
+            _CTX.clear()
+        gpu_s = []
+        for (b, r, i) in pick:
+            E = [int(j) for j in pf.needle_leaves[b, r] if j * pf.C <= i]
+            gpu_s.append(len(set(sel_full[b, r, i].tolist()) & set(E)) / min(pf.K, len(E)))
+        res["needle_recall_at_k"] = {"gpu_all_needle_queries": round(float(np.mean(rec)), 4),
+                                     "needle_query_rows": len(rec),
+                                     "sample_units": len(pick), "gpu_on_sample": round(float(np.mean(gpu_s)), 4),
+                                     "oracle_on_sample": round(float(np.mean(orc)), 4)}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -179,8 +351,10 @@ def main():
     ap.add_argument("--workload", default="prefill_64k")
     ap.add_argument("--q-tile", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
+                    help="CPU seconds of oracle work in the host-core baseline sample")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-crossover", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes three times (the reference kernel that "
                          "scales the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -348,15 +522,19 @@ def main():
                      "frac": round(achieved / peak, 4),
                      "traffic": round(traffic[dom]) if traffic and dom in traffic else None},
     }
+    del q, k, v, o, ws_sel, ws_att, ws_bsa, pyr, sel, bsel
+    torch.cuda.empty_cache()
     if not args.no_decode:
         log("[bench] decode: generating the 8 x 128K cache and timing 256 steps")
-        del q, k, v, o, ws_sel, ws_att, ws_bsa, pyr, sel, bsel
-        torch.cuda.empty_cache()
         out["decode"] = decode_latency(P, I, torch)
         log(f"[bench] decode {out['decode']}")
+    if not args.no_crossover:
+        out["crossover"] = crossover(P, I, torch)
+        log(f"[bench] crossover {json.dumps(out['crossover'])}")
     if not args.no_cpu_baseline:
-        log("[bench] timing the oracle on a CPU sample")
+        log("[bench] timing the oracle's selection on the host cores")
         out["cpu_baseline"] = cpu_baseline(pf, args.cpu_seconds)
+        log(f"[bench] cpu_baseline {out['cpu_baseline']}")
     print(json.dumps(out), flush=True)
 
 

@@ -11,6 +11,7 @@ import math
 import multiprocessing as mp
 import os
 import sys
+import time
 
 import numpy as np
 import torch
@@ -59,13 +60,31 @@ def _worker_init():
         pass
 
 
-def pool_map(fn, tasks):
-    """fn over tasks in forked worker processes (in order). fn and the data it reads from _CTX are
-    inherited by the fork; only the tasks and the results are pickled."""
+def progress(msg: str):
+    """A progress line on the process's real stdout (not captured by pytest), so that a long oracle
+    phase is visibly alive."""
+    try:
+        sys.__stdout__.write(msg + "\n")
+        sys.__stdout__.flush()
+    except Exception:  # pragma: no cover
+        pass
+
+
+def pool_map(fn, tasks, every_s=20.0):
+    """fn over tasks in forked worker processes (results in task order). fn and the data it reads from
+    _CTX are inherited by the fork; only the tasks and the results are pickled. Prints a progress line
+    about every `every_s` seconds."""
     if len(tasks) <= 1 or n_workers() == 1:
         return [fn(t) for t in tasks]
+    out = []
+    t0 = last = time.time()
     with mp.get_context("fork").Pool(n_workers(), initializer=_worker_init) as pool:
-        return pool.map(fn, tasks, chunksize=1)
+        for res in pool.imap(fn, tasks, chunksize=1):
+            out.append(res)
+            if time.time() - last > every_s:
+                last = time.time()
+                progress(f"[oracle pool] {len(out)}/{len(tasks)} tasks done, {last - t0:.0f} s")
+    return out
 
 
 def to_device(t: I.Tensor) -> torch.Tensor:
