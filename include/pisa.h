@@ -113,6 +113,20 @@ pisa_status pisa_build_pyramid(const pisa_shape* shape, const void* k, const int
 pisa_status pisa_select(const pisa_shape* shape, const void* q, const void* k, const float* pyr_mean, int32_t* sel,
                         float* sel_lse, void* ws, size_t ws_bytes, void* stream);
 
+/* pisa_select for callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc). Same arguments, kernels and results as pisa_select,
+ * but the workspace is a scratch array of pisa_select_noalloc_max_bytes() bytes (64 MiB) that the
+ * library holds in every GPU's memory from its first use on that GPU until the process ends; the call
+ * itself allocates and frees nothing. The scratch of the current device (hipGetDevice) is used, so
+ * `stream` must belong to that device. Every call on one GPU shares that GPU's scratch: calls that
+ * overlap in time on one GPU (other streams, other threads) race and give undefined results; calls on
+ * one stream are ordered and safe. Returns PISA_EUNSUPPORTED, before anything is enqueued, when
+ * pisa_workspace_size(shape, PISA_OP_SELECT) exceeds the scratch (for example 64K tokens x 8 KV heads
+ * with K = 16; 16K tokens x 2 KV heads with 16 query heads fits). */
+pisa_status pisa_select_noalloc(const pisa_shape* shape, const void* q, const void* k, const float* pyr_mean,
+                                int32_t* sel, float* sel_lse, void* stream);
+size_t pisa_select_noalloc_max_bytes(void);
+
 /* Block-sparse attention over the selected leaves (explainer 核心方法 §7, last step). For each
  * (b, h, i): O = sum over t in T of softmax_t(s * q_{h,i} . k_t) v_t, T = the tokens t <= i of the
  * leaves in sel[b, h/G, i, :]; the softmax normalises over T only.

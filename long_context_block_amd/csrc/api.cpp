@@ -7,6 +7,7 @@
 #include <cstdio>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -291,6 +292,33 @@ pisa_status lens_arg(const int32_t* host_lens, int B, int Hkv, int lo, int hi_in
   return PISA_OK;
 }
 
+// ---- scratch of pisa_select_noalloc
+// One copy of the array per GPU, held until the process ends. Host code never passes the array's name
+// to a kernel (on the host it only stands for the symbol); it passes the device address that
+// hipGetSymbolAddress returns for the current device, resolved once per device.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+pisa_status scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PISA_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(PISA_EUNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return fail(PISA_EHIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return PISA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -414,6 +442,25 @@ pisa_status pisa_select(const pisa_shape* shape, const void* q, const void* k, c
   }
   return hip_status(e, "finalize");
 }
+
+pisa_status pisa_select_noalloc(const pisa_shape* shape, const void* q, const void* k, const float* pyr_mean,
+                                int32_t* sel, float* sel_lse, void* stream) {
+  Plan p;
+  pisa_status st = plan(shape, &p);
+  if (st != PISA_OK) return st;
+  const size_t need = carve_select(p, nullptr, nullptr);
+  if (need > kNoAllocScratchBytes)
+    return fail(PISA_EUNSUPPORTED,
+                "pisa_select_noalloc: this shape needs %zu bytes of scratch; the library's fixed scratch holds %zu "
+                "(call pisa_select with a workspace instead)",
+                need, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != PISA_OK) return st;
+  return pisa_select(shape, q, k, pyr_mean, sel, sel_lse, ws, kNoAllocScratchBytes, stream);
+}
+
+size_t pisa_select_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
 
 pisa_status pisa_sparse_attn(const pisa_shape* shape, const void* q, const void* k, const void* v, const int32_t* sel,
                              void* o, float* o_lse, void* ws, size_t ws_bytes, void* stream) {

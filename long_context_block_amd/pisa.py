@@ -20,7 +20,7 @@ PISA_OP_SELECT, PISA_OP_ATTN, PISA_OP_DECODE, PISA_OP_BSA = 1, 2, 3, 4
 
 EXPORTED = ["pisa_pyramid_layout", "pisa_workspace_size", "pisa_build_pyramid", "pisa_select", "pisa_sparse_attn",
             "pisa_decode_step", "bsa_select", "pisa_status_string", "pisa_last_error", "pisa_stage_timing",
-            "pisa_stage_times"]
+            "pisa_stage_times", "pisa_select_noalloc", "pisa_select_noalloc_max_bytes"]
 
 
 class Shape(ctypes.Structure):
@@ -62,6 +62,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "pisa_workspace_size": [_SP, i32, ctypes.POINTER(sz)],
         "pisa_build_pyramid": [_SP, _P, ctypes.POINTER(i32), _P, _P, _P],
         "pisa_select": [_SP, _P, _P, _P, _P, _P, _P, sz, _P],
+        "pisa_select_noalloc": [_SP, _P, _P, _P, _P, _P, _P],
         "pisa_sparse_attn": [_SP, _P, _P, _P, _P, _P, _P, _P, sz, _P],
         "pisa_decode_step": [_SP, ctypes.POINTER(i32), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, sz, _P],
         "bsa_select": [_SP, _P, _P, _P, _P, sz, _P],
@@ -74,6 +75,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pisa_status_string.restype = ctypes.c_char_p
     lib.pisa_last_error.argtypes = []
     lib.pisa_last_error.restype = ctypes.c_char_p
+    lib.pisa_select_noalloc_max_bytes.argtypes = []
+    lib.pisa_select_noalloc_max_bytes.restype = ctypes.c_size_t
     lib.pisa_stage_timing.argtypes = [ctypes.c_int32]
     lib.pisa_stage_timing.restype = ctypes.c_int
     lib.pisa_stage_times.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32),
@@ -137,6 +140,15 @@ def pisa_select(shape, q, k, pyr_mean, sel, sel_lse=None, ws=None, stream=None):
     nbytes = ws.numel() * ws.element_size() if ws is not None else 0
     _check(load().pisa_select(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(pyr_mean), _ptr(sel), _ptr(sel_lse),
                               _ptr(ws), nbytes, _stream(stream)), "pisa_select")
+
+
+def pisa_select_noalloc(shape, q, k, pyr_mean, sel, sel_lse=None, stream=None):
+    _check(load().pisa_select_noalloc(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(pyr_mean), _ptr(sel),
+                                      _ptr(sel_lse), _stream(stream)), "pisa_select_noalloc")
+
+
+def pisa_select_noalloc_max_bytes() -> int:
+    return int(load().pisa_select_noalloc_max_bytes())
 
 
 def pisa_sparse_attn(shape, q, k, v, sel, o, o_lse=None, ws=None, stream=None):

@@ -141,3 +141,15 @@ def test_status_strings():
     lib = P.load()
     for st in (0, -1, -2, -3, -4):
         assert lib.pisa_status_string(st)
+
+
+def test_noalloc_rejects_oversized_shape_before_any_hip_call():
+    lib = P.load()
+    assert lib.pisa_select_noalloc_max_bytes() == 64 << 20
+    s = _shape(seq_len=65536, n_q_heads=32, n_kv_heads=8)
+    fake = ctypes.c_void_p(1 << 20)
+    st = lib.pisa_select_noalloc(ctypes.byref(s), fake, fake, fake, fake, None, None)
+    assert st == P.PISA_EUNSUPPORTED
+    assert b"scratch" in lib.pisa_last_error()
+    assert lib.pisa_select_noalloc(ctypes.byref(_shape(head_dim=96)), fake, fake, fake, fake, None, None) == \
+        P.PISA_EUNSUPPORTED
