@@ -24,6 +24,8 @@ def _pins_pass() -> bool:
         lambda: P.test_sel_lse_equals_library_lse_over_selected_tokens(3, "ar1"),
         lambda: P.test_walk_equals_dense_all_levels_bruteforce(4, 2),
         lambda: P.test_bsa_matches_dense_mean_key_scores(),
+        lambda: P.test_row_lse_and_mass_closed_forms(),
+        lambda: P.test_mass_equals_leaf_lse_weights(),
     ]
     for c in checks:
         try:
@@ -110,6 +112,19 @@ def _mut_sel_lse_reversed(active, leaf_head_lse, G, K):
     return out
 
 
+_orig_mass = PO.attention_mass_unit
+
+
+def _mut_mass_past_i(qg, k, sel, i, C, scale):
+    # the selected leaves' tokens after i are counted too (the mass then exceeds the causal share)
+    return _orig_mass(qg, k, np.array([j for j in sel]), min(k.shape[0] - 1, i + C), C, scale)
+
+
+def _mut_row_lse_without_diagonal(qg, k, i, scale):
+    return O.logsumexp(scale * (np.asarray(qg) @ k[:i].T), axis=-1) if i > 0 else \
+        O.logsumexp(scale * (np.asarray(qg) @ k[:1].T), axis=-1)
+
+
 MUTANTS = {
     "topk_ascending": ("_topk_order", _mut_topk_ascending),
     "tiebreak_high_index": ("_topk_order", _mut_tiebreak_high_index),
@@ -124,6 +139,8 @@ MUTANTS = {
     "margin_leaf_level_only": ("_unit_margin", _mut_margin_leaf_level_only),
     "margin_off_by_one_rank": ("_level_margin", _mut_margin_off_by_one_rank),
     "sel_lse_misaligned_with_sel": ("_selected_lse", _mut_sel_lse_reversed),
+    "mass_counts_tokens_past_i": ("attention_mass_unit", _mut_mass_past_i),
+    "row_lse_without_diagonal": ("row_lse_unit", _mut_row_lse_without_diagonal),
 }
 
 

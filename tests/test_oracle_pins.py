@@ -486,3 +486,53 @@ def test_walk_equals_dense_all_levels_bruteforce(K, G):
         n_deep += len(us.level_margins) >= 3
     assert n_ok > 0.9 * N
     assert n_deep > 0.5 * N  # most units are scored at three or more levels
+
+
+# ---------------------------------------------------------------- selection quality (Recall@K, mass)
+def test_row_lse_and_mass_closed_forms():
+    """Identical keys: every score of a row is s q . k0, so the row LSE is s q . k0 + ln(i + 1) and a
+    selection holds exactly |T| / (i + 1) of the softmax mass."""
+    d, C, N = 16, 32, 300
+    k = np.tile(_rng(61).standard_normal(d), (N, 1))
+    q = _rng(62).standard_normal((3, d))
+    scale = 0.25
+    for i in (0, 31, 32, 100, 299):
+        want = scale * q @ k[0] + math.log(i + 1)
+        np.testing.assert_allclose(O.row_lse_unit(q, k, i, scale), want, rtol=1e-13)
+        sel = np.array([j for j in (0, 2, 3) if j * C <= i] + [-1] * 3)[:3]
+        T = sum(min(i + 1, (j + 1) * C) - j * C for j in sel if j >= 0)
+        np.testing.assert_allclose(O.attention_mass_unit(q, k, sel, i, C, scale), T / (i + 1), rtol=1e-12)
+        everything = np.arange(i // C + 1)
+        np.testing.assert_allclose(O.attention_mass_unit(q, k, everything, i, C, scale), 1.0, rtol=1e-13)
+        np.testing.assert_allclose(O.attention_mass_unit(q, k, np.array([-1, -1]), i, C, scale), 0.0, atol=0)
+
+
+def test_mass_equals_leaf_lse_weights():
+    """The mass of a selection is sum over its leaves of exp(leaf LSE - row LSE) per head: the leaf LSEs
+    partition the row's LSE, checked against scipy on the raw causal row."""
+    q, k, v, scale = _tiny(N=500, d=32, C=32, G=3, keys="ar1", seed=63)
+    for i in (40, 255, 499):
+        row = scale * q[:, i] @ k[: i + 1].T
+        L = scipy.special.logsumexp(row, axis=-1)
+        np.testing.assert_allclose(O.row_lse_unit(q[:, i], k, i, scale), L, rtol=1e-13)
+        sel = np.array([0, 3, i // 32])
+        leaf = np.stack([scipy.special.logsumexp(row[:, j * 32:min(i + 1, (j + 1) * 32)], axis=-1) for j in sel])
+        np.testing.assert_allclose(O.attention_mass_unit(q[:, i], k, sel, i, 32, scale),
+                                   np.exp(leaf - L[None]).sum(axis=0), rtol=1e-11)
+
+
+def test_recall_of_walk_is_one_when_k_covers_level1():
+    """With K >= n_1 the walk is the flat exact Top-K, so its Recall@K against it is 1 on every unit
+    whose flat gap is clear; with K < n_1 it is a fraction in [0, 1]."""
+    q, k, v, scale = _tiny(N=1024, d=64, C=32, G=1)
+    pyr = O.build_pyramid(k, 32)
+    for i in range(0, 1024, 9):
+        us = O.select_unit(q[:, i], k, pyr, i, 16, scale)
+        fe, gap = O.flat_exact_select_unit(q[:, i], k, i, 32, 16, scale)
+        if gap >= 1e-9:
+            assert O.recall_at_k(us.sel, fe) == 1.0
+        us4 = O.select_unit(q[:, i], k, pyr, i, 4, scale)
+        fe4, _ = O.flat_exact_select_unit(q[:, i], k, i, 32, 4, scale)
+        r = O.recall_at_k(us4.sel, fe4)
+        assert 0.0 <= r <= 1.0
+    assert O.recall_at_k(np.array([1, 2, -1]), np.array([2, 5, 7])) == pytest.approx(1 / 3)
