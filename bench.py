@@ -246,6 +246,56 @@ def _needle_oracle(units):
     return out
 
 
+def quality_measures(P, torch, pf, positions, q_tile):
+    """Selection quality on one workload at the given query positions (digest 关键实验: Recall@K and the
+    attention mass ratio): the dense causal pass scores every leaf at those positions; from it the flat
+    exact Top-K, and for the pyramid selection, the flat selection (bsa_select) and the flat exact
+    Top-K itself, the mean Recall@K against the flat exact Top-K and the mean share of full attention's
+    softmax mass inside the selected blocks."""
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x.data).view(np.int16)).cuda().view(torch.bfloat16)
+    q, k = dev(pf.q), dev(pf.k)
+    s = P.make_shape(batch=pf.B, seq_len=pf.N, n_q_heads=pf.Hq, n_kv_heads=pf.Hkv, head_dim=pf.d, block=pf.C,
+                     top_k=pf.K, q_tile=q_tile, dtype=pf.dtype)
+    pyr = torch.empty((P.pyramid_rows(s), pf.d), dtype=torch.float32, device="cuda")
+    P.pisa_build_pyramid(s, k, pyr)
+    sels = {"pisa": torch.empty((pf.B, pf.Hkv, pf.N, pf.K), dtype=torch.int32, device="cuda")}
+    P.pisa_select(s, q, k, pyr, sels["pisa"], None, P.alloc_workspace(s, P.PISA_OP_SELECT))
+    sels["bsa"] = torch.empty_like(sels["pisa"])
+    P.bsa_select(s, q, k, sels["bsa"], P.alloc_workspace(s, P.PISA_OP_BSA))
+    pos = torch.tensor(positions, dtype=torch.int32, device="cuda")
+    n0, npos = -(-pf.N // pf.C), len(positions)
+    leaf = torch.empty((pf.B, pf.Hq, npos, n0), dtype=torch.float32, device="cuda")
+    row = torch.empty((pf.B, pf.Hq, npos), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    P.pisa_stage_timing(True)
+    P.pisa_flat_leaf_lse(s, q, k, pos, leaf, row)
+    torch.cuda.synchronize()
+    flat_ms = P.pisa_stage_times()["flat_leaf_lse"][0]
+    P.pisa_stage_timing(False)
+    flat = torch.empty((pf.B, pf.Hkv, npos, pf.K), dtype=torch.int32, device="cuda")
+    rec = torch.empty((pf.B, pf.Hkv, npos), dtype=torch.float32, device="cuda")
+    mass = torch.empty((pf.B, pf.Hq, npos), dtype=torch.float32, device="cuda")
+    out = {"positions": npos, "position_sample": "all" if npos == pf.N else "seeded uniform sample"}
+    for name in ("pisa", "bsa", "flat_exact"):
+        if name == "flat_exact":
+            # the flat exact Top-K placed at its positions of a full selection array
+            sx = torch.full_like(sels["pisa"], -1)
+            sx[:, :, pos.long()] = flat
+        else:
+            sx = sels[name]
+        P.pisa_selection_quality(s, leaf, row, pos, sx, flat, rec, mass)
+        torch.cuda.synchronize()
+        out[f"{name}_recall_at_k"] = round(float(rec.mean()), 4)
+        out[f"{name}_attention_mass"] = round(float(mass.mean()), 4)
+    i = np.asarray(positions, dtype=np.int64)
+    dense_flops = 2 * pf.B * pf.Hq * pf.d * int(((i // (2 * pf.C) + 1) * 2 * pf.C).sum())
+    out["dense_pass_ms"] = round(flat_ms, 3)
+    out["dense_pass_tflops"] = round(dense_flops / (flat_ms * 1e-3) / 1e12, 1)
+    del q, k, pyr, sels, leaf, row, flat, rec, mass
+    torch.cuda.empty_cache()
+    return out
+
+
 def crossover(P, I, torch, lengths=(16384, 32768, 65536, 131072, 262144), reps=4, oracle_needles=256):
     """Pyramid selection (pyramid + pisa_select, q_tile 4) against the flat selection (bsa_select, its
     own leaf pooling included) on prefixes of the 256K planted-needle workload (32 query / 8 KV heads,
@@ -336,10 +386,36 @@ def crossover(P, I, torch, lengths=(16384, 32768, 65536, 131072, 262144), reps=4
         for (b, r, i) in pick:
             E = [int(j) for j in pf.needle_leaves[b, r] if j * pf.C <= i]
             gpu_s.append(len(set(sel_full[b, r, i].tolist()) & set(E)) / min(pf.K, len(E)))
+        # the flat exact Top-K (every leaf scored exactly) at the sampled needle positions: how findable
+        # the planted needles are for any selection of K leaves
+        pos_l = sorted({i for (_, _, i) in pick})
+        s = P.make_shape(batch=pf.B, seq_len=pf.N, n_q_heads=pf.Hq, n_kv_heads=pf.Hkv, head_dim=pf.d, block=pf.C,
+                         top_k=pf.K, q_tile=4, dtype=pf.dtype)
+        qa = torch.from_numpy(pf.q.data.view(np.int16)).cuda().view(torch.bfloat16)
+        ka = torch.from_numpy(pf.k.data.view(np.int16)).cuda().view(torch.bfloat16)
+        pos = torch.tensor(pos_l, dtype=torch.int32, device="cuda")
+        n0 = -(-pf.N // pf.C)
+        leaf = torch.empty((pf.B, pf.Hq, len(pos_l), n0), dtype=torch.float32, device="cuda")
+        row = torch.empty((pf.B, pf.Hq, len(pos_l)), dtype=torch.float32, device="cuda")
+        P.pisa_flat_leaf_lse(s, qa, ka, pos, leaf, row)
+        dummy = torch.full((pf.B, pf.Hkv, pf.N, pf.K), -1, dtype=torch.int32, device="cuda")
+        flat = torch.empty((pf.B, pf.Hkv, len(pos_l), pf.K), dtype=torch.int32, device="cuda")
+        rr = torch.empty((pf.B, pf.Hkv, len(pos_l)), dtype=torch.float32, device="cuda")
+        mm = torch.empty((pf.B, pf.Hq, len(pos_l)), dtype=torch.float32, device="cuda")
+        P.pisa_selection_quality(s, leaf, row, pos, dummy, flat, rr, mm)
+        flat_np = flat.cpu().numpy()
+        del qa, ka, pos, leaf, row, dummy, flat, rr, mm
+        torch.cuda.empty_cache()
+        at = {i: x for x, i in enumerate(pos_l)}
+        flat_rec = []
+        for (b, r, i) in pick:
+            E = [int(j) for j in pf.needle_leaves[b, r] if j * pf.C <= i]
+            flat_rec.append(len(set(flat_np[b, r, at[i]].tolist()) & set(E)) / min(pf.K, len(E)))
         res["needle_recall_at_k"] = {"gpu_all_needle_queries": round(float(np.mean(rec)), 4),
                                      "needle_query_rows": len(rec),
                                      "sample_units": len(pick), "gpu_on_sample": round(float(np.mean(gpu_s)), 4),
-                                     "oracle_on_sample": round(float(np.mean(orc)), 4)}
+                                     "oracle_on_sample": round(float(np.mean(orc)), 4),
+                                     "flat_exact_topk_on_sample": round(float(np.mean(flat_rec)), 4)}
     return res
 
 
@@ -355,6 +431,7 @@ def main():
                     help="CPU seconds of oracle work in the host-core baseline sample")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-crossover", action="store_true")
+    ap.add_argument("--no-quality", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes three times (the reference kernel that "
                          "scales the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -528,6 +605,18 @@ def main():
         log("[bench] decode: generating the 8 x 128K cache and timing 256 steps")
         out["decode"] = decode_latency(P, I, torch)
         log(f"[bench] decode {out['decode']}")
+    if not args.no_quality:
+        log("[bench] selection quality (Recall@K, attention mass) at 16K and 64K")
+        qual = {}
+        pf16 = I.make_workload("prefill_16k")
+        qual["prefill_16k"] = quality_measures(P, torch, pf16, list(range(pf16.N)), q_tile=2)
+        del pf16
+        rng = np.random.default_rng(12)
+        pos64 = sorted(rng.choice(pf.N, 2048, replace=False).tolist()) if args.workload == "prefill_64k" else None
+        if pos64 is not None:
+            qual["prefill_64k"] = quality_measures(P, torch, pf, pos64, q_tile=4)
+        out["quality"] = qual
+        log(f"[bench] quality {json.dumps(qual)}")
     if not args.no_crossover:
         out["crossover"] = crossover(P, I, torch)
         log(f"[bench] crossover {json.dumps(out['crossover'])}")

@@ -158,6 +158,32 @@ pisa_status pisa_decode_step(const pisa_shape* shape, const int32_t* host_lens, 
 pisa_status bsa_select(const pisa_shape* shape, const void* q, const void* k, int32_t* sel, void* ws, size_t ws_bytes,
                        void* stream);
 
+/* Selection quality (digest 关键实验: block selections are compared by Recall@K and by the attention
+ * mass ratio). A dense causal pass that scores every leaf, not a bounded candidate set, at chosen
+ * query positions, and the measures computed from it.
+ *
+ * pisa_flat_leaf_lse: for every (b, query head h, position index x) with i = positions[x]:
+ *   leaf_lse out fp32 [B, Hq, n_pos, n0] (n0 = ceil(N / C)): per leaf j, the exact LSE over the leaf's
+ *            tokens t <= i of s * q_{h,i} . k_t, -inf for leaves after i (the same per-leaf arithmetic
+ *            as pisa_select's leaf stage);
+ *   row_lse  out fp32 [B, Hq, n_pos]: the LSE of the whole causal row (every t <= i).
+ *   positions: device int32 [n_pos], each in [0, N); a position outside gives NaN rows.
+ * Work is O(n_pos * i * d * Hq) MFMA flops: use it on samples of positions at long N.
+ *
+ * pisa_selection_quality: per unit (b, r, x), from the outputs of pisa_flat_leaf_lse:
+ *   flat_sel out int32 [B, Hkv, n_pos, K]: the flat exact Top-K, the K eligible leaves with the largest
+ *            head-summed leaf LSE (score descending, then lower index), ascending, -1 padded;
+ *   recall   out fp32 [B, Hkv, n_pos]: |sel[b, r, i] & flat_sel| / min(K, eligible leaves);
+ *   mass     out fp32 [B, Hq, n_pos]: per head, sum over the leaves j of sel[b, r, i] of
+ *            exp(leaf_lse[j] - row_lse), the share of full causal attention's softmax mass inside the
+ *            selected blocks.
+ *   sel: int32 [B, Hkv, N, K] as written by pisa_select or bsa_select. At most 16384 leaves. */
+pisa_status pisa_flat_leaf_lse(const pisa_shape* shape, const void* q, const void* k, const int32_t* positions,
+                               int32_t n_pos, float* leaf_lse, float* row_lse, void* stream);
+pisa_status pisa_selection_quality(const pisa_shape* shape, const float* leaf_lse, const float* row_lse,
+                                   const int32_t* positions, int32_t n_pos, const int32_t* sel, int32_t* flat_sel,
+                                   float* recall, float* mass, void* stream);
+
 const char* pisa_status_string(pisa_status status);
 const char* pisa_last_error(void);
 

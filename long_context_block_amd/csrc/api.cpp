@@ -575,6 +575,50 @@ pisa_status bsa_select(const pisa_shape* shape, const void* q, const void* k, in
   return hip_status(e, "bsa_select");
 }
 
+pisa_status pisa_flat_leaf_lse(const pisa_shape* shape, const void* q, const void* k, const int32_t* positions,
+                               int32_t n_pos, float* leaf_lse, float* row_lse, void* stream) {
+  Plan p;
+  pisa_status st = plan(shape, &p);
+  if (st != PISA_OK) return st;
+  PISA_CHECK_PTR(q, "q");
+  PISA_CHECK_PTR(k, "k");
+  PISA_CHECK_PTR(positions, "positions");
+  PISA_CHECK_PTR(leaf_lse, "leaf_lse");
+  PISA_CHECK_PTR(row_lse, "row_lse");
+  if (n_pos < 1) return fail(PISA_EINVAL, "n_pos must be >= 1");
+  if ((long long)p.BH * n_pos * p.sd.lv.n[0] * p.sd.G >= (1LL << 40)) return fail(PISA_EUNSUPPORTED, "output too large");
+  hipError_t e;
+  {
+    Stage sc((hipStream_t)stream, "flat_leaf_lse");
+    e = pisa::launch_flat_leaf_lse(p.sd, q, k, positions, n_pos, leaf_lse, row_lse, (hipStream_t)stream);
+  }
+  return hip_status(e, "pisa_flat_leaf_lse");
+}
+
+pisa_status pisa_selection_quality(const pisa_shape* shape, const float* leaf_lse, const float* row_lse,
+                                   const int32_t* positions, int32_t n_pos, const int32_t* sel, int32_t* flat_sel,
+                                   float* recall, float* mass, void* stream) {
+  Plan p;
+  pisa_status st = plan(shape, &p);
+  if (st != PISA_OK) return st;
+  PISA_CHECK_PTR(leaf_lse, "leaf_lse");
+  PISA_CHECK_PTR(row_lse, "row_lse");
+  PISA_CHECK_PTR(positions, "positions");
+  PISA_CHECK_PTR(sel, "sel");
+  PISA_CHECK_PTR(flat_sel, "flat_sel");
+  PISA_CHECK_PTR(recall, "recall");
+  PISA_CHECK_PTR(mass, "mass");
+  if (n_pos < 1) return fail(PISA_EINVAL, "n_pos must be >= 1");
+  if (p.sd.lv.n[0] > 16384) return fail(PISA_EUNSUPPORTED, "at most 16384 leaves (the leaf scores of a unit are held in LDS)");
+  hipError_t e;
+  {
+    Stage sc((hipStream_t)stream, "selection_quality");
+    e = pisa::launch_quality(p.sd, leaf_lse, row_lse, positions, n_pos, sel, flat_sel, recall, mass,
+                             (hipStream_t)stream);
+  }
+  return hip_status(e, "pisa_selection_quality");
+}
+
 pisa_status pisa_stage_timing(int32_t enable) {
   g_timer.on = enable != 0;
   if (!enable) {

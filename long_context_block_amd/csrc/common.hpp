@@ -231,6 +231,13 @@ __device__ __forceinline__ float lse2(float a, float b) {
   return m + kLn2 * fast_log2(1.f + fast_exp2(d * kLog2e));
 }
 
+// LSE of two already-scaled values, either of which may be -inf.
+__device__ __forceinline__ float lse2_inf(float a, float b) {
+  if (a == kNegInf) return b;
+  if (b == kNegInf) return a;
+  return lse2(a, b);
+}
+
 // Sum over the 16 lanes of each row by DPP row rotations: every lane gets the row total (the order of
 // the additions depends on the lane, so read one fixed lane when bit reproducibility matters).
 template <int CTRL>

@@ -73,6 +73,13 @@ hipError_t launch_attn_merge(const SelDims& sd, const int* sel, const int* pos, 
 hipError_t launch_bsa(const SelDims& sd, const void* q, const float* leaf_mean, const uint16_t* leaf_hilo, int* sel,
                       hipStream_t st);
 
+// Selection quality: every leaf's exact per-head LSE and each row's LSE at the given positions, then
+// per unit the flat exact Top-K, the recall of `sel` against it and its share of the softmax mass.
+hipError_t launch_flat_leaf_lse(const SelDims& sd, const void* q, const void* k, const int* pos, int n_pos,
+                                float* leaf_lse, float* row_lse, hipStream_t st);
+hipError_t launch_quality(const SelDims& sd, const float* leaf_lse, const float* row_lse, const int* pos, int n_pos,
+                          const int* sel, int* flat_sel, float* recall, float* mass, hipStream_t st);
+
 // Decode step.
 struct DecodeArgs {
   int B, Hq, Hkv, G, Nmax, D, C, K;

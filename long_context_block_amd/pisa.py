@@ -20,7 +20,8 @@ PISA_OP_SELECT, PISA_OP_ATTN, PISA_OP_DECODE, PISA_OP_BSA = 1, 2, 3, 4
 
 EXPORTED = ["pisa_pyramid_layout", "pisa_workspace_size", "pisa_build_pyramid", "pisa_select", "pisa_sparse_attn",
             "pisa_decode_step", "bsa_select", "pisa_status_string", "pisa_last_error", "pisa_stage_timing",
-            "pisa_stage_times", "pisa_select_noalloc", "pisa_select_noalloc_max_bytes"]
+            "pisa_stage_times", "pisa_select_noalloc", "pisa_select_noalloc_max_bytes", "pisa_flat_leaf_lse",
+            "pisa_selection_quality"]
 
 
 class Shape(ctypes.Structure):
@@ -66,6 +67,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "pisa_sparse_attn": [_SP, _P, _P, _P, _P, _P, _P, _P, sz, _P],
         "pisa_decode_step": [_SP, ctypes.POINTER(i32), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, sz, _P],
         "bsa_select": [_SP, _P, _P, _P, _P, sz, _P],
+        "pisa_flat_leaf_lse": [_SP, _P, _P, _P, i32, _P, _P, _P],
+        "pisa_selection_quality": [_SP, _P, _P, _P, i32, _P, _P, _P, _P, _P],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -169,6 +172,17 @@ def bsa_select(shape, q, k, sel, ws=None, stream=None):
     nbytes = ws.numel() * ws.element_size() if ws is not None else 0
     _check(load().bsa_select(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(sel), _ptr(ws), nbytes, _stream(stream)),
            "bsa_select")
+
+
+def pisa_flat_leaf_lse(shape, q, k, positions, leaf_lse, row_lse, stream=None):
+    _check(load().pisa_flat_leaf_lse(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(positions), int(positions.numel()),
+                                     _ptr(leaf_lse), _ptr(row_lse), _stream(stream)), "pisa_flat_leaf_lse")
+
+
+def pisa_selection_quality(shape, leaf_lse, row_lse, positions, sel, flat_sel, recall, mass, stream=None):
+    _check(load().pisa_selection_quality(ctypes.byref(shape), _ptr(leaf_lse), _ptr(row_lse), _ptr(positions),
+                                         int(positions.numel()), _ptr(sel), _ptr(flat_sel), _ptr(recall), _ptr(mass),
+                                         _stream(stream)), "pisa_selection_quality")
 
 
 def pisa_stage_timing(enable: bool):
