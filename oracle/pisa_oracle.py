@@ -311,6 +311,108 @@ def flat_exact_select_unit(qg: np.ndarray, k: np.ndarray, i: int, C: int, K: int
 
 
 # ----------------------------------------------------------------------------------------------
+# Selection variants.
+# [digest] 方法关键点, scoring bullet: in the ablations PISA-1 scores blocks by the mean and PISA-2 by
+# the mean plus the variance, and full LSE scoring does better. Readings: a node's "mean" score is
+# s * q . mu(node) from its own pooled summary (at the leaves too, from the leaf's full span, as the
+# flat selection does); PISA-2 adds the second-order term of the LSE's expansion around the mean,
+# (s^2 / 2) * sum_d q_d^2 var_d(node), with var_d the per-dimension population variance of the raw keys
+# in the node's span (the summary a pooled pyramid can hold; the pages print no formula).
+# [explainer] 核心方法 §1: pooling may be mean, sum or max (element-wise over the keys in the span).
+# [explainer] 核心方法 §7 and 工程落地 (K starts at about 0.2 x blocks and halves level by level):
+# the "halving" budget keeps K_l = min(n_l, K * 2^l) nodes at level l, i.e. half as many at each finer
+# level, ending with K leaves. [explainer] 工程落地 ⑥: the pool chain can be truncated: with a cap L' the
+# pyramid stops at level L' and the walk starts from all eligible nodes of that level.
+# ----------------------------------------------------------------------------------------------
+def build_pyramid_pooled(k: np.ndarray, C: int, g: int = 2, pool: str = "mean",
+                         n_tokens: int | None = None) -> Pyramid:
+    """Pyramid whose node summary is the mean, the sum or the element-wise max of the raw keys in the
+    node's span (taken straight from the span)."""
+    k = np.asarray(k, dtype=np.float64)
+    n = k.shape[0] if n_tokens is None else int(n_tokens)
+    sizes = level_sizes(n, C, g)
+    means, counts = [], []
+    for l, n_l in enumerate(sizes):
+        m = np.zeros((n_l, k.shape[1]))
+        c = np.zeros(n_l)
+        for j in range(n_l):
+            t0, t1 = node_span(l, j, C, g, n)
+            c[j] = t1 - t0
+            if t1 > t0:
+                span = k[t0:t1]
+                m[j] = {"mean": span.mean(axis=0), "sum": span.sum(axis=0), "max": span.max(axis=0)}[pool]
+        means.append(m)
+        counts.append(c)
+    return Pyramid(means=means, counts=counts, C=C, g=g, n_tokens=n)
+
+
+def pyramid_variances(k: np.ndarray, C: int, g: int = 2, n_tokens: int | None = None) -> list[np.ndarray]:
+    """Per level [n_l, d]: the per-dimension population variance of the raw keys in each node's span."""
+    k = np.asarray(k, dtype=np.float64)
+    n = k.shape[0] if n_tokens is None else int(n_tokens)
+    out = []
+    for l, n_l in enumerate(level_sizes(n, C, g)):
+        v = np.zeros((n_l, k.shape[1]))
+        for j in range(n_l):
+            t0, t1 = node_span(l, j, C, g, n)
+            if t1 > t0:
+                v[j] = k[t0:t1].var(axis=0)
+        out.append(v)
+    return out
+
+
+def level_budget(l: int, n_l: int, K: int, budget: str) -> int:
+    """Nodes kept at level l: K at every level, or (halving) K * 2^l, at most the level's node count."""
+    return K if budget == "fixed" else min(n_l, K * 2 ** l)
+
+
+def variant_node_score(qg: np.ndarray, pyr: Pyramid, l: int, j: int, i: int, scale: float, score: str,
+                       k: np.ndarray, variances=None) -> float:
+    """Head-summed score of candidate node (l, j) under a scoring rule."""
+    if score == "lse":
+        if l == 0:
+            return float(leaf_lse_per_head(qg, k, j, i, pyr.C, scale, pyr.n_tokens).sum())
+        return float(node_lse_per_head(qg, pyr, l, j, i, scale).sum())
+    mu = pyr.means[l][j]
+    x = scale * (qg @ mu)  # [G]
+    if score == "mean_var":
+        x = x + 0.5 * scale * scale * ((qg * qg) @ variances[l][j])
+    return float(x.sum())
+
+
+def select_unit_variant(qg: np.ndarray, k: np.ndarray, pyr: Pyramid, i: int, K: int, scale: float,
+                        score: str = "lse", budget: str = "fixed", max_level: int | None = None,
+                        variances=None) -> UnitSelection:
+    """The coarse-to-fine walk under a scoring rule ("lse", "mean", "mean_var"), a budget ("fixed",
+    "halving") and an optional cap on the starting level. Leaf budget K; the output is the kept leaves."""
+    qg = np.asarray(qg, dtype=np.float64)
+    C, g = pyr.C, pyr.g
+    L = pyr.root_level if max_level is None else min(pyr.root_level, max_level)
+    kept = {}
+    level_margins = {}
+    active = None
+    for l in range(L, -1, -1):
+        n_l = pyr.means[l].shape[0]
+        if l == L:
+            cand = [j for j in range(n_l) if eligible(l, j, i, C, g)]
+        else:
+            cand = sorted(c for p in active for c in children(l + 1, p, pyr) if eligible(l, c, i, C, g))
+        K_l = level_budget(l, n_l, K, budget)
+        if len(cand) <= K_l:
+            active = cand
+        else:
+            scores = np.array([variant_node_score(qg, pyr, l, c, i, scale, score, k, variances) for c in cand])
+            order = _topk_order(cand, scores)
+            level_margins[l] = _level_margin(scores, order, K_l)
+            active = sorted(cand[p] for p in order[:K_l])
+        kept[l] = list(active)
+    sel = np.full(K, -1, dtype=np.int64)
+    sel[:len(active)] = active
+    return UnitSelection(sel=sel, sel_lse=np.full((qg.shape[0], K), NEG_INF), margin=_unit_margin(level_margins),
+                         kept=kept, leaf_scores={}, level_margins=level_margins)
+
+
+# ----------------------------------------------------------------------------------------------
 # Selection quality. [digest] 关键实验: block-selection quality is measured by Recall@K against the
 # blocks a full scoring would pick and by the attention mass ratio (how much of full attention's
 # softmax mass falls inside the selected blocks). Here the reference selection is the flat exact

@@ -26,6 +26,10 @@ def _pins_pass() -> bool:
         lambda: P.test_bsa_matches_dense_mean_key_scores(),
         lambda: P.test_row_lse_and_mass_closed_forms(),
         lambda: P.test_mass_equals_leaf_lse_weights(),
+        lambda: P.test_pooled_summaries_closed_forms(1000),
+        lambda: P.test_mean_scoring_with_k_covering_level1_is_flat_bsa(),
+        lambda: P.test_mean_var_scoring_equals_dense_formula(),
+        lambda: P.test_halving_budget_and_truncation_equal_dense_bruteforce(3, 1),
     ]
     for c in checks:
         try:
@@ -125,6 +129,41 @@ def _mut_row_lse_without_diagonal(qg, k, i, scale):
         O.logsumexp(scale * (np.asarray(qg) @ k[:1].T), axis=-1)
 
 
+_orig_vscore = PO.variant_node_score
+
+
+def _mut_var_term_without_half(qg, pyr, l, j, i, scale, score, k, variances=None):
+    x = _orig_vscore(qg, pyr, l, j, i, scale, score, k, variances)
+    if score == "mean_var":
+        x += float((0.5 * scale * scale * ((qg * qg) @ variances[l][j])).sum())
+    return x
+
+
+def _mut_budget_one_level_off(l, n_l, K, budget):
+    # the doubling starts one level late: K at levels 0 and 1, then K 2^(l-1)
+    return K if budget == "fixed" or l == 0 else min(n_l, K * 2 ** (l - 1))
+
+
+_orig_pooled = PO.build_pyramid_pooled
+
+
+def _mut_max_pool_is_mean(k, C, g=2, pool="mean", n_tokens=None):
+    return _orig_pooled(k, C, g, "mean" if pool == "max" else pool, n_tokens)
+
+
+_orig_variant = PO.select_unit_variant
+
+
+def _mut_truncation_one_level_high(qg, k, pyr, i, K, scale, score="lse", budget="fixed", max_level=None,
+                                   variances=None):
+    return _orig_variant(qg, k, pyr, i, K, scale, score, budget, None if max_level is None else max_level + 1,
+                         variances)
+
+
+def _mut_mean_score_uses_lse(qg, pyr, l, j, i, scale, score, k, variances=None):
+    return _orig_vscore(qg, pyr, l, j, i, scale, "lse" if score == "mean" else score, k, variances)
+
+
 MUTANTS = {
     "topk_ascending": ("_topk_order", _mut_topk_ascending),
     "tiebreak_high_index": ("_topk_order", _mut_tiebreak_high_index),
@@ -141,6 +180,11 @@ MUTANTS = {
     "sel_lse_misaligned_with_sel": ("_selected_lse", _mut_sel_lse_reversed),
     "mass_counts_tokens_past_i": ("attention_mass_unit", _mut_mass_past_i),
     "row_lse_without_diagonal": ("row_lse_unit", _mut_row_lse_without_diagonal),
+    "variance_term_doubled": ("variant_node_score", _mut_var_term_without_half),
+    "halving_budget_one_level_off": ("level_budget", _mut_budget_one_level_off),
+    "max_pooling_as_mean": ("build_pyramid_pooled", _mut_max_pool_is_mean),
+    "truncation_one_level_high": ("select_unit_variant", _mut_truncation_one_level_high),
+    "mean_scoring_as_lse": ("variant_node_score", _mut_mean_score_uses_lse),
 }
 
 

@@ -414,7 +414,7 @@ def test_sel_lse_equals_library_lse_over_selected_tokens(G, keys):
 
 
 # ---------------------------------------------------------------- dense brute force of the whole walk
-def _dense_walk(q, k, C, K, scale):
+def _dense_walk(q, k, C, K, scale, budgets=None, start=None):
     """Independent dense brute force of the walk at every level. Node means come straight from the raw
     keys of each node's span; every node's score for every query is one dense masked matrix (scipy
     LSE over eligible children, or over the leaf's tokens t <= i); the walk is boolean masks over whole
@@ -444,19 +444,21 @@ def _dense_walk(q, k, C, K, scale):
     Tp[:, :, :N] = T
     LH = scipy.special.logsumexp(Tp.reshape(G, N, n[0], C), axis=-1)  # [G, N, n_0], -inf when no token
     S[0] = LH.sum(axis=0)
+    Kl = [K] * (L + 1) if budgets is None else list(budgets)
+    top = L if start is None else start
     out = []
     for i in range(N):
         kept = np.ones(1, dtype=bool)  # the root
         gaps = []
-        for l in range(L - 1, -1, -1):
-            cand = np.repeat(kept, 2)[:n[l]] & elig[l][i]
+        for l in range(top, -1, -1):
+            cand = elig[l][i].copy() if l == top else np.repeat(kept, 2)[:n[l]] & elig[l][i]
             idx = np.flatnonzero(cand)
-            if idx.size > K:
+            if idx.size > Kl[l]:
                 sc = S[l][i, idx]
                 order = np.lexsort((idx, -sc))
-                gaps.append(sc[order[K - 1]] - sc[order[K]])
+                gaps.append(sc[order[Kl[l] - 1]] - sc[order[Kl[l]]])
                 kept = np.zeros(n[l], dtype=bool)
-                kept[idx[order[:K]]] = True
+                kept[idx[order[:Kl[l]]]] = True
             else:
                 kept = cand
         sel = np.flatnonzero(kept)
@@ -536,3 +538,119 @@ def test_recall_of_walk_is_one_when_k_covers_level1():
         r = O.recall_at_k(us4.sel, fe4)
         assert 0.0 <= r <= 1.0
     assert O.recall_at_k(np.array([1, 2, -1]), np.array([2, 5, 7])) == pytest.approx(1 / 3)
+
+
+# ---------------------------------------------------------------- selection variants (ablations)
+def test_variant_defaults_equal_the_walk():
+    """LSE scoring, mean pooling, fixed budget and no cap: the variant walk is the walk itself."""
+    q, k, v, scale = _tiny(N=1500, d=32, C=32, G=2, keys="ar1", seed=71)
+    pyr = O.build_pyramid(k, 32)
+    pooled = O.build_pyramid_pooled(k, 32, pool="mean")
+    for a, b in zip(pyr.means, pooled.means):
+        np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-13)
+    for i in range(0, 1500, 7):
+        a = O.select_unit(q[:, i], k, pyr, i, 4, scale)
+        b = O.select_unit_variant(q[:, i], k, pyr, i, 4, scale)
+        assert a.sel.tolist() == b.sel.tolist() and a.margin == b.margin
+
+
+@pytest.mark.parametrize("N", [1000, 777])
+def test_pooled_summaries_closed_forms(N):
+    """Sum pooling is the mean times the tokens held; max pooling of increasing keys k_t = t e (e > 0)
+    is the key of the span's last token."""
+    C = 32
+    k = _rng(72).standard_normal((N, 8))
+    mean = O.build_pyramid_pooled(k, C, pool="mean")
+    summ = O.build_pyramid_pooled(k, C, pool="sum")
+    for m, s_, c in zip(mean.means, summ.means, mean.counts):
+        np.testing.assert_allclose(s_, m * c[:, None], rtol=1e-12, atol=1e-10)
+    e = np.abs(_rng(73).standard_normal(8)) + 0.1
+    kl = np.arange(N, dtype=np.float64)[:, None] * e[None, :]
+    mx = O.build_pyramid_pooled(kl, C, pool="max")
+    for l, m in enumerate(mx.means):
+        for j in range(m.shape[0]):
+            last = min(N, (j + 1) * C * 2 ** l) - 1
+            np.testing.assert_allclose(m[j], last * e, rtol=1e-14)
+    var = O.pyramid_variances(k, C)
+    for l, vv in enumerate(var):
+        w = C * 2 ** l
+        for j in (0, vv.shape[0] - 1):
+            np.testing.assert_allclose(vv[j], np.var(k[j * w:min(N, (j + 1) * w)], axis=0), rtol=1e-12)
+
+
+def test_mean_scoring_with_k_covering_level1_is_flat_bsa():
+    """PISA-1 (each node scored by s q . its mean) with K >= n_1 keeps every node above the leaves, so
+    it ranks every eligible leaf by s q . mean(leaf): the flat BSA selection."""
+    q, k, v, scale = _tiny(N=900, d=32, C=32, G=3, keys="ar1", seed=74)
+    pyr = O.build_pyramid(k, 32)
+    K = pyr.means[1].shape[0]
+    for i in range(0, 900, 4):
+        a = O.select_unit_variant(q[:, i], k, pyr, i, K, scale, score="mean")
+        b, gap = O.bsa_select_unit(q[:, i], pyr.means[0], i, 32, K, scale)
+        assert _same_margin(a.margin, gap)
+        if gap >= 1e-9:
+            assert a.sel.tolist() == b.tolist(), i
+
+
+def test_mean_var_scoring_equals_dense_formula():
+    """PISA-2 with K >= n_1: every eligible leaf ranked by sum_h [s q_h . mu + (s^2 / 2) sum_d q_hd^2
+    var_d], computed here from reshaped leaf blocks; leaves holding one constant key reduce it to PISA-1."""
+    N, C, G = 1024, 32, 2
+    q, k, v, scale = _tiny(N=N, d=32, C=C, G=G, keys="ar1", seed=75)
+    pyr = O.build_pyramid(k, C)
+    var = O.pyramid_variances(k, C)
+    K = pyr.means[1].shape[0]
+    blocks = k.reshape(N // C, C, -1)
+    mu, vr = blocks.mean(axis=1), blocks.var(axis=1)  # [n_0, d]
+    F = scale * np.einsum("gnd,jd->nj", q, mu) + 0.5 * scale ** 2 * np.einsum("gnd,jd->nj", q * q, vr)
+    for i in range(0, N, 5):
+        e = i // C + 1
+        f = F[i, :e]
+        o = np.lexsort((np.arange(e), -f))
+        want = sorted(o[:K].tolist()) if e > K else list(range(e))
+        gap = f[o[K - 1]] - f[o[K]] if e > K else math.inf
+        a = O.select_unit_variant(q[:, i], k, pyr, i, K, scale, score="mean_var", variances=var)
+        assert _same_margin(a.margin, gap)
+        if gap >= 1e-9:
+            assert [j for j in a.sel.tolist() if j >= 0] == want
+    kc = np.repeat(_rng(76).standard_normal((N // C, 32)), C, axis=0)  # one key per leaf
+    pyr_c, var_c = O.build_pyramid(kc, C), O.pyramid_variances(kc, C)
+    for i in range(0, N, 11):
+        a = O.select_unit_variant(q[:, i], kc, pyr_c, i, K, scale, score="mean_var", variances=var_c)
+        b = O.select_unit_variant(q[:, i], kc, pyr_c, i, K, scale, score="mean")
+        assert a.sel.tolist() == b.sel.tolist()
+
+
+@pytest.mark.parametrize("K,G", [(3, 1), (4, 2)])
+def test_halving_budget_and_truncation_equal_dense_bruteforce(K, G):
+    """The halving budget K_l = min(n_l, K 2^l) and a capped starting level, against the dense brute
+    force of the whole walk run with the same per-level budgets and starting level."""
+    N, C = 2000, 32
+    q, k, v, scale = _tiny(N=N, d=32, C=C, G=G, keys="ar1", seed=77 + K)
+    pyr = O.build_pyramid(k, C)
+    n = [m.shape[0] for m in pyr.means]
+    budgets = [min(n[l], K * 2 ** l) for l in range(len(n))]  # K at the leaves, doubling per coarser level
+    cases = [("halving", None, budgets, None), ("fixed", 3, None, 3), ("halving", 4, budgets, 4)]
+    for budget, cap, bl, st in cases:
+        brute = _dense_walk(q, k, C, K, scale, budgets=bl, start=st)
+        n_ok = 0
+        for i in range(0, N, 3):
+            sel_b, _, gap = brute[i]
+            a = O.select_unit_variant(q[:, i], k, pyr, i, K, scale, budget=budget, max_level=cap)
+            if gap < 1e-9:
+                continue
+            assert [j for j in a.sel.tolist() if j >= 0] == sel_b, (budget, cap, i)
+            assert _same_margin(a.margin, gap)
+            n_ok += 1
+        assert n_ok > 0.9 * len(range(0, N, 3))
+
+
+def test_truncation_that_keeps_every_start_node_changes_nothing():
+    """A cap whose starting level holds at most K nodes keeps all of them, as the full walk does at and
+    above that level: the selection is the full walk's."""
+    q, k, v, scale = _tiny(N=2000, d=32, C=32, G=2, keys="ar1", seed=79)
+    pyr = O.build_pyramid(k, 32)  # 63 leaves, 7 levels; level 4 has 4 nodes
+    for i in range(0, 2000, 9):
+        a = O.select_unit(q[:, i], k, pyr, i, 4, scale)
+        b = O.select_unit_variant(q[:, i], k, pyr, i, 4, scale, max_level=4)
+        assert a.sel.tolist() == b.sel.tolist()
