@@ -296,6 +296,68 @@ def quality_measures(P, torch, pf, positions, q_tile):
     return out
 
 
+ABLATIONS = [  # name, pool, score, budget, max_level (None: from the root)
+    ("method (LSE, mean pooling, fixed K)", "mean", "lse", "fixed", None),
+    ("PISA-1 (mean scoring)", "mean", "mean", "fixed", None),
+    ("PISA-2 (mean + variance scoring)", "mean", "mean_var", "fixed", None),
+    ("sum pooling", "sum", "lse", "fixed", None),
+    ("max pooling", "max", "lse", "fixed", None),
+    ("halving budget", "mean", "lse", "halving", None),
+    ("pool chain truncated at level 4", "mean", "lse", "fixed", 4),
+]
+
+
+def ablations(P, torch, pf, positions, reps=2):
+    """The selection variants on one workload: time of the pooled pyramid + variant walk, and the Recall@K
+    against the flat exact Top-K and the attention mass of each variant's selection at the positions."""
+    pool_id = {"mean": P.PISA_POOL_MEAN, "sum": P.PISA_POOL_SUM, "max": P.PISA_POOL_MAX}
+    score_id = {"lse": P.PISA_SCORE_LSE, "mean": P.PISA_SCORE_MEAN, "mean_var": P.PISA_SCORE_MEAN_VAR}
+    budget_id = {"fixed": P.PISA_BUDGET_FIXED, "halving": P.PISA_BUDGET_HALVING}
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x.data).view(np.int16)).cuda().view(torch.bfloat16)
+    q, k = dev(pf.q), dev(pf.k)
+    s = P.make_shape(batch=pf.B, seq_len=pf.N, n_q_heads=pf.Hq, n_kv_heads=pf.Hkv, head_dim=pf.d, block=pf.C,
+                     top_k=pf.K, q_tile=1, dtype=pf.dtype)
+    rows = P.pyramid_rows(s)
+    summ = torch.empty((rows, pf.d), dtype=torch.float32, device="cuda")
+    var = torch.empty_like(summ)
+    pos = torch.tensor(positions, dtype=torch.int32, device="cuda")
+    n0, npos = -(-pf.N // pf.C), len(positions)
+    leaf = torch.empty((pf.B, pf.Hq, npos, n0), dtype=torch.float32, device="cuda")
+    row = torch.empty((pf.B, pf.Hq, npos), dtype=torch.float32, device="cuda")
+    P.pisa_flat_leaf_lse(s, q, k, pos, leaf, row)
+    flat = torch.empty((pf.B, pf.Hkv, npos, pf.K), dtype=torch.int32, device="cuda")
+    rec = torch.empty((pf.B, pf.Hkv, npos), dtype=torch.float32, device="cuda")
+    mass = torch.empty((pf.B, pf.Hq, npos), dtype=torch.float32, device="cuda")
+    sel = torch.empty((pf.B, pf.Hkv, pf.N, pf.K), dtype=torch.int32, device="cuda")
+    out = {"workload": "prefill_64k" if pf.N == 65536 else f"N={pf.N}", "positions": npos, "variants": {}}
+    for name, pool, score, budget, cap in ABLATIONS:
+        v = P.Variant(score_id[score], budget_id[budget], -1 if cap is None else cap)
+        vv = var if score == "mean_var" else None
+
+        def once():
+            P.pisa_build_pyramid_pooled(s, k, pool_id[pool], summ, vv)
+            P.pisa_select_variant(s, v, q, k, summ, sel, vv)
+
+        once()
+        torch.cuda.synchronize()
+        P.pisa_stage_timing(True)
+        for _ in range(reps):
+            once()
+        torch.cuda.synchronize()
+        st = {n: t / c for n, (t, c) in P.pisa_stage_times().items()}
+        P.pisa_stage_timing(False)
+        P.pisa_selection_quality(s, leaf, row, pos, sel, flat, rec, mass)
+        torch.cuda.synchronize()
+        out["variants"][name] = {"pool": pool, "score": score, "budget": budget, "max_level": cap,
+                                 "ms": round(st.get("pyramid_pooled", 0.0) + st.get("select_variant", 0.0), 3),
+                                 "recall_at_k": round(float(rec.mean()), 4),
+                                 "attention_mass": round(float(mass.mean()), 4)}
+        log(f"[bench] ablation {name}: {out['variants'][name]}")
+    del q, k, summ, var, pos, leaf, row, flat, rec, mass, sel
+    torch.cuda.empty_cache()
+    return out
+
+
 def crossover(P, I, torch, lengths=(16384, 32768, 65536, 131072, 262144), reps=4, oracle_needles=256):
     """Pyramid selection (pyramid + pisa_select, q_tile 4) against the flat selection (bsa_select, its
     own leaf pooling included) on prefixes of the 256K planted-needle workload (32 query / 8 KV heads,
@@ -615,6 +677,8 @@ def main():
         pos64 = sorted(rng.choice(pf.N, 2048, replace=False).tolist()) if args.workload == "prefill_64k" else None
         if pos64 is not None:
             qual["prefill_64k"] = quality_measures(P, torch, pf, pos64, q_tile=4)
+            log("[bench] selection variants at 64K")
+            qual["ablations"] = ablations(P, torch, pf, pos64)
         out["quality"] = qual
         log(f"[bench] quality {json.dumps(qual)}")
     if not args.no_crossover:

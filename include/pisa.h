@@ -184,6 +184,41 @@ pisa_status pisa_selection_quality(const pisa_shape* shape, const float* leaf_ls
                                    const int32_t* positions, int32_t n_pos, const int32_t* sel, int32_t* flat_sel,
                                    float* recall, float* mass, void* stream);
 
+/* Selection variants: the ablations and options that the pages name beside the method. Not the fast
+ * path: the walk scores node summaries with fp32 dot products, one wave per unit, to measure how the
+ * options change the selection.
+ *
+ * pisa_build_pyramid_pooled: a pyramid (pisa_pyramid_layout) whose node summary is the mean, the sum or
+ * the element-wise max of the raw keys in the node's span (explainer 核心方法 §1: mean, sum or max
+ * pooling). variance, nullable (mean or sum pooling only): the per-dimension population variance of
+ * those keys, in the same layout.
+ *
+ * pisa_select_variant: the pisa_select walk with these options (sel out int32 [B, Hkv, N, K]):
+ *   score  PISA_SCORE_LSE: LSE over the eligible children's summaries, exact LSE over raw keys at the
+ *          leaves (the method; with mean pooling and the fixed budget, the selection pisa_select makes);
+ *          PISA_SCORE_MEAN: s * q . the node's own summary (digest 方法关键点, scoring bullet: the
+ *          PISA-1 ablation); PISA_SCORE_MEAN_VAR: that plus (s^2 / 2) * sum_d q_d^2 var_d (PISA-2: mean
+ *          plus variance; needs variance); heads summed at every level.
+ *   budget PISA_BUDGET_FIXED: K nodes kept at every level; PISA_BUDGET_HALVING: K_l = min(n_l, K 2^l),
+ *          half as many at each finer level (explainer 核心方法 §7 and 工程落地), K leaves in the end.
+ *   max_level  -1: the walk starts at the root; else it starts from every eligible node of level
+ *          min(max_level, root) (a truncated pool chain, explainer 工程落地 ⑥).
+ * Candidate lists are held in on-chip memory: the starting level and twice the kept nodes of every level
+ * must not exceed 2048 nodes (PISA_EUNSUPPORTED otherwise). summary/variance come from
+ * pisa_build_pyramid_pooled (or pisa_build_pyramid, which is mean pooling). */
+typedef enum { PISA_POOL_MEAN = 0, PISA_POOL_SUM = 1, PISA_POOL_MAX = 2 } pisa_pool;
+typedef enum { PISA_SCORE_LSE = 0, PISA_SCORE_MEAN = 1, PISA_SCORE_MEAN_VAR = 2 } pisa_score;
+typedef enum { PISA_BUDGET_FIXED = 0, PISA_BUDGET_HALVING = 1 } pisa_budget;
+typedef struct {
+  int32_t score;     /* pisa_score */
+  int32_t budget;    /* pisa_budget */
+  int32_t max_level; /* -1, or the highest pyramid level the walk starts from */
+} pisa_variant;
+pisa_status pisa_build_pyramid_pooled(const pisa_shape* shape, const void* k, int32_t pool, float* summary,
+                                      float* variance, void* stream);
+pisa_status pisa_select_variant(const pisa_shape* shape, const pisa_variant* variant, const void* q, const void* k,
+                                const float* summary, const float* variance, int32_t* sel, void* stream);
+
 const char* pisa_status_string(pisa_status status);
 const char* pisa_last_error(void);
 

@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <algorithm>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -617,6 +618,69 @@ pisa_status pisa_selection_quality(const pisa_shape* shape, const float* leaf_ls
                              (hipStream_t)stream);
   }
   return hip_status(e, "pisa_selection_quality");
+}
+
+pisa_status pisa_build_pyramid_pooled(const pisa_shape* shape, const void* k, int32_t pool, float* summary,
+                                      float* variance, void* stream) {
+  Plan p;
+  pisa_status st = plan(shape, &p);
+  if (st != PISA_OK) return st;
+  PISA_CHECK_PTR(k, "k");
+  PISA_CHECK_PTR(summary, "summary");
+  PISA_CHECK_OPT_PTR(variance, "variance");
+  if (pool != PISA_POOL_MEAN && pool != PISA_POOL_SUM && pool != PISA_POOL_MAX)
+    return fail(PISA_EINVAL, "pool must be PISA_POOL_MEAN, PISA_POOL_SUM or PISA_POOL_MAX");
+  if (variance && pool == PISA_POOL_MAX)
+    return fail(PISA_EUNSUPPORTED, "variances are built with mean or sum pooling only");
+  pisa::PyrDims pd{(int)p.BH, p.sd.N, p.sd.C, p.sd.D, p.sd.lv};
+  hipError_t e;
+  {
+    Stage sc((hipStream_t)stream, "pyramid_pooled");
+    e = pisa::launch_pool_pooled(k, p.sd.bf16, pd, pool, summary, variance, (hipStream_t)stream);
+  }
+  return hip_status(e, "pisa_build_pyramid_pooled");
+}
+
+pisa_status pisa_select_variant(const pisa_shape* shape, const pisa_variant* variant, const void* q, const void* k,
+                                const float* summary, const float* variance, int32_t* sel, void* stream) {
+  Plan p;
+  pisa_status st = plan(shape, &p);
+  if (st != PISA_OK) return st;
+  if (!variant) return fail(PISA_EINVAL, "variant: null pointer");
+  PISA_CHECK_PTR(q, "q");
+  PISA_CHECK_PTR(k, "k");
+  PISA_CHECK_PTR(summary, "summary");
+  PISA_CHECK_OPT_PTR(variance, "variance");
+  PISA_CHECK_PTR(sel, "sel");
+  const int score = variant->score, budget = variant->budget;
+  if (score != PISA_SCORE_LSE && score != PISA_SCORE_MEAN && score != PISA_SCORE_MEAN_VAR)
+    return fail(PISA_EINVAL, "variant.score must be PISA_SCORE_LSE, PISA_SCORE_MEAN or PISA_SCORE_MEAN_VAR");
+  if (budget != PISA_BUDGET_FIXED && budget != PISA_BUDGET_HALVING)
+    return fail(PISA_EINVAL, "variant.budget must be PISA_BUDGET_FIXED or PISA_BUDGET_HALVING");
+  if (score == PISA_SCORE_MEAN_VAR && !variance) return fail(PISA_EINVAL, "mean + variance scoring needs variance");
+  if (variant->max_level < -1) return fail(PISA_EINVAL, "variant.max_level must be -1 (none) or >= 0");
+  const pisa::Levels& lv = p.sd.lv;
+  const int root = lv.n_levels - 1;
+  const int start = variant->max_level < 0 || variant->max_level > root ? root : variant->max_level;
+  // candidate lists held in LDS: every node of the starting level, then twice the kept nodes of the
+  // level above
+  auto kept_max = [&](int l) -> long long {
+    const long long Kl = budget == PISA_BUDGET_FIXED ? p.sd.K : std::min((long long)lv.n[l], (long long)p.sd.K << l);
+    return std::min((long long)lv.n[l], Kl);
+  };
+  if (lv.n[start] > pisa::kVariantLdsCand)
+    return fail(PISA_EUNSUPPORTED, "the starting level has %d nodes; at most %d candidates per level", lv.n[start],
+                pisa::kVariantLdsCand);
+  for (int l = start; l >= 1; --l)
+    if (2 * kept_max(l) > pisa::kVariantLdsCand)
+      return fail(PISA_EUNSUPPORTED, "level %d would have %lld candidates; at most %d per level", l - 1,
+                  2 * kept_max(l), pisa::kVariantLdsCand);
+  hipError_t e;
+  {
+    Stage sc((hipStream_t)stream, "select_variant");
+    e = pisa::launch_variant(p.sd, score, budget, start, q, k, summary, variance, sel, (hipStream_t)stream);
+  }
+  return hip_status(e, "pisa_select_variant");
 }
 
 pisa_status pisa_stage_timing(int32_t enable) {

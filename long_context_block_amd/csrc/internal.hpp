@@ -80,6 +80,16 @@ hipError_t launch_flat_leaf_lse(const SelDims& sd, const void* q, const void* k,
 hipError_t launch_quality(const SelDims& sd, const float* leaf_lse, const float* row_lse, const int* pos, int n_pos,
                           const int* sel, int* flat_sel, float* recall, float* mass, hipStream_t st);
 
+// Selection variants: a pyramid of pooled summaries (pool 0 mean, 1 sum, 2 max; variance nullable),
+// and the walk under a scoring rule (0 LSE, 1 mean, 2 mean + variance), a budget (0 fixed, 1 halving)
+// from the starting level `start` (at most the root). Candidate lists live in LDS: at most
+// kVariantLdsCand candidates per level.
+constexpr int kVariantLdsCand = 2048;
+hipError_t launch_pool_pooled(const void* k, bool bf16, const PyrDims& pd, int pool, float* summary, float* variance,
+                              hipStream_t st);
+hipError_t launch_variant(const SelDims& sd, int score, int budget, int start, const void* q, const void* k,
+                          const float* summary, const float* variance, int* sel, hipStream_t st);
+
 // Decode step.
 struct DecodeArgs {
   int B, Hq, Hkv, G, Nmax, D, C, K;

@@ -21,7 +21,7 @@ PISA_OP_SELECT, PISA_OP_ATTN, PISA_OP_DECODE, PISA_OP_BSA = 1, 2, 3, 4
 EXPORTED = ["pisa_pyramid_layout", "pisa_workspace_size", "pisa_build_pyramid", "pisa_select", "pisa_sparse_attn",
             "pisa_decode_step", "bsa_select", "pisa_status_string", "pisa_last_error", "pisa_stage_timing",
             "pisa_stage_times", "pisa_select_noalloc", "pisa_select_noalloc_max_bytes", "pisa_flat_leaf_lse",
-            "pisa_selection_quality"]
+            "pisa_selection_quality", "pisa_build_pyramid_pooled", "pisa_select_variant"]
 
 
 class Shape(ctypes.Structure):
@@ -35,6 +35,15 @@ def make_shape(*, batch, seq_len, n_q_heads, n_kv_heads, head_dim, block, top_k,
                dtype="bf16") -> Shape:
     dt = {"bf16": PISA_BF16, "fp32": PISA_FP32}.get(dtype, dtype)
     return Shape(batch, seq_len, n_q_heads, n_kv_heads, head_dim, block, top_k, branch, q_tile, scale, dt)
+
+
+PISA_POOL_MEAN, PISA_POOL_SUM, PISA_POOL_MAX = 0, 1, 2
+PISA_SCORE_LSE, PISA_SCORE_MEAN, PISA_SCORE_MEAN_VAR = 0, 1, 2
+PISA_BUDGET_FIXED, PISA_BUDGET_HALVING = 0, 1
+
+
+class Variant(ctypes.Structure):
+    _fields_ = [("score", ctypes.c_int32), ("budget", ctypes.c_int32), ("max_level", ctypes.c_int32)]
 
 
 class PisaError(RuntimeError):
@@ -69,6 +78,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "bsa_select": [_SP, _P, _P, _P, _P, sz, _P],
         "pisa_flat_leaf_lse": [_SP, _P, _P, _P, i32, _P, _P, _P],
         "pisa_selection_quality": [_SP, _P, _P, _P, i32, _P, _P, _P, _P, _P],
+        "pisa_build_pyramid_pooled": [_SP, _P, i32, _P, _P, _P],
+        "pisa_select_variant": [_SP, ctypes.POINTER(Variant), _P, _P, _P, _P, _P, _P],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -183,6 +194,16 @@ def pisa_selection_quality(shape, leaf_lse, row_lse, positions, sel, flat_sel, r
     _check(load().pisa_selection_quality(ctypes.byref(shape), _ptr(leaf_lse), _ptr(row_lse), _ptr(positions),
                                          int(positions.numel()), _ptr(sel), _ptr(flat_sel), _ptr(recall), _ptr(mass),
                                          _stream(stream)), "pisa_selection_quality")
+
+
+def pisa_build_pyramid_pooled(shape, k, pool, summary, variance=None, stream=None):
+    _check(load().pisa_build_pyramid_pooled(ctypes.byref(shape), _ptr(k), int(pool), _ptr(summary), _ptr(variance),
+                                            _stream(stream)), "pisa_build_pyramid_pooled")
+
+
+def pisa_select_variant(shape, variant, q, k, summary, sel, variance=None, stream=None):
+    _check(load().pisa_select_variant(ctypes.byref(shape), ctypes.byref(variant), _ptr(q), _ptr(k), _ptr(summary),
+                                      _ptr(variance), _ptr(sel), _stream(stream)), "pisa_select_variant")
 
 
 def pisa_stage_timing(enable: bool):
