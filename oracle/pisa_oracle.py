@@ -269,6 +269,39 @@ def attend_unit(qg: np.ndarray, k: np.ndarray, v: np.ndarray, sel: np.ndarray, i
 
 
 # ----------------------------------------------------------------------------------------------
+# Backward of block-sparse attention. [digest] 工作参考价值 fourth bullet: in training the gradients pass
+# only through the selected attention; the discrete selection is not differentiated. [abstract]: the
+# kernels serve training and inference. For one KV head, given the selection and the upstream gradient
+# dO of the attention output, the gradients of q, k and v of softmax attention restricted to the tokens
+# T(i) of each query's selected leaves (t <= i): with p = softmax_T(s q . k), o = p v,
+# dp_t = dO . v_t, D = dO . o, ds_t = p_t (dp_t - D): dq = s sum_t ds_t k_t, dk_t += s ds_t q,
+# dv_t += p_t dO, summed over the group's query heads and over every query that attends t.
+# ----------------------------------------------------------------------------------------------
+def attention_backward_head(qg: np.ndarray, k: np.ndarray, v: np.ndarray, sel: np.ndarray, C: int, scale: float,
+                            do: np.ndarray):
+    """qg [G, N, d], k and v [N, d], sel [N, K] (leaf indices per position, -1 padded), do [G, N, d].
+    Returns (dq [G, N, d], dk [N, d], dv [N, d]) in float64."""
+    qg, k, v, do = (np.asarray(x, dtype=np.float64) for x in (qg, k, v, do))
+    G, N, d = qg.shape
+    dq = np.zeros_like(qg)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for i in range(N):
+        toks = sorted(t for j in sel[i] if j >= 0 for t in range(j * C, min(N, (j + 1) * C, i + 1)))
+        toks = np.array(toks, dtype=np.int64)
+        z = scale * (qg[:, i] @ k[toks].T)  # [G, T]
+        p = np.exp(z - logsumexp(z, axis=-1)[:, None])
+        o = p @ v[toks]  # [G, d]
+        dp = do[:, i] @ v[toks].T  # [G, T]
+        D = np.sum(do[:, i] * o, axis=-1)  # [G]
+        ds = p * (dp - D[:, None])
+        dq[:, i] = scale * (ds @ k[toks])
+        dk[toks] += scale * (ds.T @ qg[:, i])
+        dv[toks] += p.T @ do[:, i]
+    return dq, dk, dv
+
+
+# ----------------------------------------------------------------------------------------------
 # Flat block selection of ordinary block-sparse attention. [digest] 动机: it scores every
 # (query, key block) pair, O(N^2/C). Reading: one score per block, s * q . mu(leaf), summed over the
 # GQA heads; the Top-K order is the same as the walk's.

@@ -30,6 +30,8 @@ def _pins_pass() -> bool:
         lambda: P.test_mean_scoring_with_k_covering_level1_is_flat_bsa(),
         lambda: P.test_mean_var_scoring_equals_dense_formula(),
         lambda: P.test_halving_budget_and_truncation_equal_dense_bruteforce(3, 1),
+        lambda: P.test_backward_equals_autograd_of_dense_masked_attention(),
+        lambda: P.test_backward_finite_differences(),
     ]
     for c in checks:
         try:
@@ -164,6 +166,19 @@ def _mut_mean_score_uses_lse(qg, pyr, l, j, i, scale, score, k, variances=None):
     return _orig_vscore(qg, pyr, l, j, i, scale, "lse" if score == "mean" else score, k, variances)
 
 
+_orig_bwd = PO.attention_backward_head
+
+
+def _mut_bwd_dk_unscaled(qg, k, v, sel, C, scale, do):
+    dq, dk, dv = _orig_bwd(qg, k, v, sel, C, scale, do)
+    return dq, dk / scale, dv
+
+
+def _mut_bwd_dv_head_mean(qg, k, v, sel, C, scale, do):
+    dq, dk, dv = _orig_bwd(qg, k, v, sel, C, scale, do)
+    return dq, dk, dv / qg.shape[0]
+
+
 MUTANTS = {
     "topk_ascending": ("_topk_order", _mut_topk_ascending),
     "tiebreak_high_index": ("_topk_order", _mut_tiebreak_high_index),
@@ -185,6 +200,8 @@ MUTANTS = {
     "max_pooling_as_mean": ("build_pyramid_pooled", _mut_max_pool_is_mean),
     "truncation_one_level_high": ("select_unit_variant", _mut_truncation_one_level_high),
     "mean_scoring_as_lse": ("variant_node_score", _mut_mean_score_uses_lse),
+    "backward_dk_unscaled": ("attention_backward_head", _mut_bwd_dk_unscaled),
+    "backward_dv_head_mean": ("attention_backward_head", _mut_bwd_dv_head_mean),
 }
 
 

@@ -654,3 +654,85 @@ def test_truncation_that_keeps_every_start_node_changes_nothing():
         a = O.select_unit(q[:, i], k, pyr, i, 4, scale)
         b = O.select_unit_variant(q[:, i], k, pyr, i, 4, scale, max_level=4)
         assert a.sel.tolist() == b.sel.tolist()
+
+
+# ---------------------------------------------------------------- backward of block-sparse attention
+def _dense_masked_attention(qg, k, v, sel, C, scale):
+    """Block-sparse attention written densely in torch (float64): scores masked to each query's selected
+    tokens t <= i, so that autograd gives the gradients of the definition."""
+    G, N, d = qg.shape
+    mask = np.zeros((N, N), dtype=bool)
+    for i in range(N):
+        for j in sel[i]:
+            if j >= 0:
+                mask[i, j * C:min(N, (j + 1) * C, i + 1)] = True
+    m = torch.from_numpy(mask)
+
+    def f(q_, k_, v_):
+        z = scale * torch.einsum("gnd,td->gnt", q_, k_)
+        z = z.masked_fill(~m[None], float("-inf"))
+        return torch.einsum("gnt,td->gnd", torch.softmax(z, dim=-1), v_)
+
+    return f
+
+
+def test_backward_equals_autograd_of_dense_masked_attention():
+    q, k, v, scale = _tiny(N=300, d=16, C=32, G=3, keys="ar1", seed=81)
+    pyr = O.build_pyramid(k, 32)
+    sel = np.stack([O.select_unit(q[:, i], k, pyr, i, 3, scale).sel for i in range(300)])
+    do = _rng(82).standard_normal(q.shape)
+    dq, dk, dv = O.attention_backward_head(q, k, v, sel, 32, scale, do)
+    f = _dense_masked_attention(q, k, v, sel, 32, scale)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    out = f(tq, tk, tv)
+    # the forward itself is the oracle's attention
+    o_ref = np.stack([O.attend_unit(q[:, i], k, v, sel[i], i, 32, scale, 300)[0] for i in range(300)], axis=1)
+    np.testing.assert_allclose(out.detach().numpy(), o_ref, rtol=0, atol=1e-12)
+    out.backward(torch.from_numpy(do))
+    np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=0, atol=1e-11)
+
+
+def test_backward_with_every_block_is_dense_causal_sdpa_backward():
+    q, k, v, scale = _tiny(N=200, d=16, C=32, G=2, keys="iid", seed=83)
+    n0 = -(-200 // 32)
+    sel = np.tile(np.arange(n0), (200, 1))
+    sel = np.where(sel * 32 <= np.arange(200)[:, None], sel, -1)
+    do = _rng(84).standard_normal(q.shape)
+    dq, dk, dv = O.attention_backward_head(q, k, v, sel, 32, scale, do)
+    tq = torch.tensor(q[None], requires_grad=True)
+    tk = torch.tensor(k[None, None], requires_grad=True)
+    tv = torch.tensor(v[None, None], requires_grad=True)
+    out = torch.nn.functional.scaled_dot_product_attention(tq, tk.expand(1, 2, 200, 16), tv.expand(1, 2, 200, 16),
+                                                           is_causal=True, scale=scale)
+    out.backward(torch.from_numpy(do[None]))
+    np.testing.assert_allclose(dq, tq.grad.numpy()[0], rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dk, tk.grad.numpy()[0, 0], rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dv, tv.grad.numpy()[0, 0], rtol=0, atol=1e-11)
+
+
+def test_backward_finite_differences():
+    """Central differences of L = sum(dO * O) with the selection held fixed."""
+    q, k, v, scale = _tiny(N=80, d=8, C=16, G=2, keys="ar1", seed=85)
+    pyr = O.build_pyramid(k, 16)
+    sel = np.stack([O.select_unit(q[:, i], k, pyr, i, 2, scale).sel for i in range(80)])
+    do = _rng(86).standard_normal(q.shape)
+
+    def loss(q_, k_, v_):
+        o = np.stack([O.attend_unit(q_[:, i], k_, v_, sel[i], i, 16, scale, 80)[0] for i in range(80)], axis=1)
+        return float(np.sum(do * o))
+
+    dq, dk, dv = O.attention_backward_head(q, k, v, sel, 16, scale, do)
+    rng = _rng(87)
+    h = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for _ in range(6):
+            idx = tuple(rng.integers(0, s_) for s_ in x.shape)
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = {"q": (xp, k, v), "k": (q, xp, v), "v": (q, k, xp)}[name]
+            args_m = {"q": (xm, k, v), "k": (q, xm, v), "v": (q, k, xm)}[name]
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * h)
+            assert fd == pytest.approx(g[idx], rel=1e-6, abs=1e-7), (name, idx)
