@@ -494,6 +494,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-crossover", action="store_true")
     ap.add_argument("--no-quality", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes three times (the reference kernel that "
                          "scales the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -661,7 +662,36 @@ def main():
                      "frac": round(achieved / peak, 4),
                      "traffic": round(traffic[dom]) if traffic and dom in traffic else None},
     }
-    del q, k, v, o, ws_sel, ws_att, ws_bsa, pyr, sel, bsel
+    if not args.no_backward and pf.dtype == "bf16":
+        # backward of the sparse attention on this step's selection: forward with its LSE once, then the
+        # timed backward passes (seeded dO)
+        o_lse = torch.empty((pf.B, pf.Hq, pf.N), dtype=torch.float32, device="cuda")
+        P.pisa_sparse_attn(s, q, k, v, sel, o, o_lse, ws_att)
+        del ws_att, ws_sel, ws_bsa
+        torch.cuda.empty_cache()
+        gen = torch.Generator(device="cuda").manual_seed(7)
+        d_o = torch.randn(q.shape, generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws_b = P.alloc_workspace(s, P.PISA_OP_ATTN_BWD)
+        P.pisa_sparse_attn_backward(s, q, k, v, sel, o, o_lse, d_o, dq, dk, dv, ws_b)
+        torch.cuda.synchronize()
+        P.pisa_stage_timing(True)
+        for _ in range(max(2, args.steps // 2)):
+            P.pisa_sparse_attn_backward(s, q, k, v, sel, o, o_lse, d_o, dq, dk, dv, ws_b)
+        torch.cuda.synchronize()
+        stb = {n_: t_ / c_ for n_, (t_, c_) in P.pisa_stage_times().items()}
+        P.pisa_stage_timing(False)
+        b_ms = stb.get("regroup_attn_bwd", 0.0) + stb.get("attn_backward", 0.0)
+        b_flops = 10 * pf.d * w["attended_keys"]  # S, dP, dV, dK and dQ: five products of 2 d per attended key
+        out["backward"] = {"ms": round(b_ms, 4), "algorithmic_flops": b_flops,
+                           "TFLOP/s": round(b_flops / (b_ms * 1e-3) / 1e12, 2),
+                           "frac_mfma": round(b_flops / (b_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                           "stages_ms": {n_: round(t_, 4) for n_, t_ in sorted(stb.items())}}
+        log(f"[bench] backward {out['backward']}")
+        del o_lse, d_o, dq, dk, dv, ws_b
+    else:
+        del ws_att, ws_sel, ws_bsa
+    del q, k, v, o, pyr, sel, bsel
     torch.cuda.empty_cache()
     if not args.no_decode:
         log("[bench] decode: generating the 8 x 128K cache and timing 256 steps")

@@ -56,7 +56,7 @@ typedef enum {
 typedef enum { PISA_FP32 = 0, PISA_BF16 = 1 } pisa_dtype;
 
 /* Operation codes for pisa_workspace_size. */
-enum { PISA_OP_SELECT = 1, PISA_OP_ATTN = 2, PISA_OP_DECODE = 3, PISA_OP_BSA = 4 };
+enum { PISA_OP_SELECT = 1, PISA_OP_ATTN = 2, PISA_OP_DECODE = 3, PISA_OP_BSA = 4, PISA_OP_ATTN_BWD = 5 };
 
 /* Problem shape, passed by pointer to every call.
  * Limits of these kernels (PISA_EUNSUPPORTED otherwise): head_dim in {64, 128}; block C in
@@ -135,6 +135,21 @@ size_t pisa_select_noalloc_max_bytes(void);
  *   o        out [B, Hq, N, d] (dtype). o_lse out, nullable, fp32 [B, Hq, N]: LSE over T. */
 pisa_status pisa_sparse_attn(const pisa_shape* shape, const void* q, const void* k, const void* v, const int32_t* sel,
                              void* o, float* o_lse, void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of pisa_sparse_attn (digest 工作参考价值 fourth bullet: the gradients pass only through the
+ * selected attention; the selection itself gets no gradient). For each (b, h, i) with T = the tokens
+ * t <= i of the leaves in sel[b, h/G, i, :], p_t = exp(s q . k_t - o_lse), dp_t = dO . v_t,
+ * D = dO . o, ds_t = p_t (dp_t - D):
+ *   d_q[b, h, i] = s sum_t ds_t k_t;  d_k[b, r, t] = s sum ds_t q;  d_v[b, r, t] = sum p_t dO
+ * (the last two summed over every query head of KV head r and every query that attends t).
+ *   sel, o, o_lse: the selection and the outputs of the forward call (o_lse is required here).
+ *   d_o [B, Hq, N, d]: the gradient of o. d_q [B, Hq, N, d], d_k and d_v [B, Hkv, N, d]: out.
+ *   bfloat16 inputs and outputs only (fp32 accumulation); PISA_EUNSUPPORTED for fp32.
+ *   ws: pisa_workspace_size(shape, PISA_OP_ATTN_BWD) bytes. d_k and d_v are summed with floating-point
+ *   atomics, so their last bits may differ from run to run. */
+pisa_status pisa_sparse_attn_backward(const pisa_shape* shape, const void* q, const void* k, const void* v,
+                                      const int32_t* sel, const void* o, const float* o_lse, const void* d_o,
+                                      void* d_q, void* d_k, void* d_v, void* ws, size_t ws_bytes, void* stream);
 
 /* One fused decode step (digest 工作参考价值 second bullet; 方法关键点 Kernel bullet). For every
  * sequence b with p = host_lens[b] tokens cached (shape.seq_len = capacity Nmax, p < Nmax): append

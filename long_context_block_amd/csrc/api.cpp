@@ -251,6 +251,32 @@ size_t carve_attn(const Plan& p, void* ws, AttnWs* w) {
   return c.off;
 }
 
+struct AttnBwdWs {
+  int* counts;
+  int* offsets;
+  int* ranks;
+  uint32_t* pairs;
+  float* dsum;
+  float* acc;  // dk accumulators, then dv accumulators
+  void* part;
+};
+
+size_t carve_attn_bwd(const Plan& p, void* ws, AttnBwdWs* w) {
+  Carver c(ws);
+  AttnBwdWs x{};
+  const size_t pairs = (size_t)p.U * p.sd.K;
+  const size_t NB = (size_t)p.BH * p.nch * p.sd.lv.n[0];
+  x.counts = (int*)c.take(NB * 4);
+  x.offsets = (int*)c.take((NB + 1) * 4);
+  x.ranks = (int*)c.take(pairs * 4);
+  x.pairs = (uint32_t*)c.take(pairs * 4);
+  x.dsum = (float*)c.take((size_t)p.sd.B * p.sd.Hq * p.sd.N * 4);
+  x.acc = (float*)c.take((size_t)2 * p.U * p.sd.D * 4);
+  x.part = c.take(pairs * p.sd.G * p.sd.D * 2);
+  if (w) *w = x;
+  return c.off;
+}
+
 struct BsaWs {
   float* mean;
   uint16_t* hilo;
@@ -359,6 +385,7 @@ pisa_status pisa_workspace_size(const pisa_shape* shape, int32_t op, size_t* byt
     case PISA_OP_ATTN: *bytes = carve_attn(p, nullptr, nullptr); break;
     case PISA_OP_DECODE: *bytes = 0; break;
     case PISA_OP_BSA: *bytes = carve_bsa(p, nullptr, nullptr); break;
+    case PISA_OP_ATTN_BWD: *bytes = carve_attn_bwd(p, nullptr, nullptr); break;
     default: return fail(PISA_EINVAL, "unknown op %d", op);
   }
   return ok();
@@ -498,6 +525,45 @@ pisa_status pisa_sparse_attn(const pisa_shape* shape, const void* q, const void*
     e = pisa::launch_attn_merge(p.sd, sel, w.ranks, w.part, w.part_lse, o, o_lse, s);
   }
   return hip_status(e, "attn_merge");
+}
+
+pisa_status pisa_sparse_attn_backward(const pisa_shape* shape, const void* q, const void* k, const void* v,
+                                      const int32_t* sel, const void* o, const float* o_lse, const void* d_o,
+                                      void* d_q, void* d_k, void* d_v, void* ws, size_t ws_bytes, void* stream) {
+  Plan p;
+  pisa_status st = plan(shape, &p);
+  if (st != PISA_OK) return st;
+  if (!p.sd.bf16) return fail(PISA_EUNSUPPORTED, "pisa_sparse_attn_backward: bfloat16 inputs only");
+  PISA_CHECK_PTR(q, "q");
+  PISA_CHECK_PTR(k, "k");
+  PISA_CHECK_PTR(v, "v");
+  PISA_CHECK_PTR(sel, "sel");
+  PISA_CHECK_PTR(o, "o");
+  PISA_CHECK_PTR(o_lse, "o_lse");
+  PISA_CHECK_PTR(d_o, "d_o");
+  PISA_CHECK_PTR(d_q, "d_q");
+  PISA_CHECK_PTR(d_k, "d_k");
+  PISA_CHECK_PTR(d_v, "d_v");
+  const size_t need = carve_attn_bwd(p, nullptr, nullptr);
+  st = check_ws(need, ws, ws_bytes);
+  if (st != PISA_OK) return st;
+  AttnBwdWs w;
+  carve_attn_bwd(p, ws, &w);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  {
+    Stage sc(s, "regroup_attn_bwd");
+    e = pisa::launch_regroup(sel, p.U, p.sd.K, p.sd.N, p.sd.lv.n[0], (int)p.BH, p.sd.chunk_log2, w.counts,
+                             w.offsets, w.ranks, true, w.pairs, s);
+  }
+  if (e != hipSuccess) return hip_status(e, "regroup");
+  const int* total = w.offsets + p.BH * p.nch * p.sd.lv.n[0];
+  {
+    Stage sc(s, "attn_backward");
+    e = pisa::launch_attn_backward(p.sd, q, k, v, sel, o, o_lse, d_o, w.pairs, total, w.ranks, w.dsum, w.acc,
+                                   w.acc + (size_t)p.U * p.sd.D, w.part, d_q, d_k, d_v, s);
+  }
+  return hip_status(e, "pisa_sparse_attn_backward");
 }
 
 pisa_status pisa_decode_step(const pisa_shape* shape, const int32_t* host_lens, const void* q_new, const void* k_new,

@@ -267,6 +267,29 @@ __device__ __forceinline__ void stage_kv_wg(const uint16_t* kbh, const uint16_t*
   }
 }
 
+// Cooperative staging of C rows (tokens t0 .. t0 + C - 1, past N: token N - 1) into a swizzled [C][D]
+// tile, the layout stage_kv_wg gives the keys.
+template <int D, int C>
+__device__ __forceinline__ void stage_rows_wg(const uint16_t* src, long long t0, long long N, uint16_t (*sk)[D]) {
+  const int tid = threadIdx.x;
+  constexpr int CHR = D / 8;
+  constexpr int KN = C * CHR;
+  constexpr int KIT = (KN + 255) / 256;
+  uint4 kk[KIT];
+#pragma unroll
+  for (int it = 0; it < KIT; ++it) {
+    const int x = it * 256 + tid, t = x / CHR, c = x % CHR;
+    long long tt = t0 + t;
+    tt = tt < N ? tt : N - 1;
+    if (KN % 256 == 0 || x < KN) kk[it] = *reinterpret_cast<const uint4*>(src + tt * D + 8 * c);
+  }
+#pragma unroll
+  for (int it = 0; it < KIT; ++it) {
+    const int x = it * 256 + tid, t = x / CHR, c = x % CHR;
+    if (KN % 256 == 0 || x < KN) *reinterpret_cast<uint4*>(&sk[t][8 * (c ^ kswz<D>(t))]) = kk[it];
+  }
+}
+
 // K A-fragment (S M-tile m, k step s) from the swizzled shared tile.
 template <int D>
 __device__ __forceinline__ Frag<uint16_t> k_frag_wg(const uint16_t (*sk)[D], int m, int s) {

@@ -16,12 +16,13 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpisa.so"
 
 PISA_OK, PISA_EINVAL, PISA_EUNSUPPORTED, PISA_EWORKSPACE, PISA_EHIP = 0, -1, -2, -3, -4
 PISA_FP32, PISA_BF16 = 0, 1
-PISA_OP_SELECT, PISA_OP_ATTN, PISA_OP_DECODE, PISA_OP_BSA = 1, 2, 3, 4
+PISA_OP_SELECT, PISA_OP_ATTN, PISA_OP_DECODE, PISA_OP_BSA, PISA_OP_ATTN_BWD = 1, 2, 3, 4, 5
 
 EXPORTED = ["pisa_pyramid_layout", "pisa_workspace_size", "pisa_build_pyramid", "pisa_select", "pisa_sparse_attn",
             "pisa_decode_step", "bsa_select", "pisa_status_string", "pisa_last_error", "pisa_stage_timing",
             "pisa_stage_times", "pisa_select_noalloc", "pisa_select_noalloc_max_bytes", "pisa_flat_leaf_lse",
-            "pisa_selection_quality", "pisa_build_pyramid_pooled", "pisa_select_variant"]
+            "pisa_selection_quality", "pisa_build_pyramid_pooled", "pisa_select_variant",
+            "pisa_sparse_attn_backward"]
 
 
 class Shape(ctypes.Structure):
@@ -80,6 +81,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "pisa_selection_quality": [_SP, _P, _P, _P, i32, _P, _P, _P, _P, _P],
         "pisa_build_pyramid_pooled": [_SP, _P, i32, _P, _P, _P],
         "pisa_select_variant": [_SP, ctypes.POINTER(Variant), _P, _P, _P, _P, _P, _P],
+        "pisa_sparse_attn_backward": [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, sz, _P],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -169,6 +171,13 @@ def pisa_sparse_attn(shape, q, k, v, sel, o, o_lse=None, ws=None, stream=None):
     nbytes = ws.numel() * ws.element_size() if ws is not None else 0
     _check(load().pisa_sparse_attn(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(sel), _ptr(o), _ptr(o_lse),
                                    _ptr(ws), nbytes, _stream(stream)), "pisa_sparse_attn")
+
+
+def pisa_sparse_attn_backward(shape, q, k, v, sel, o, o_lse, d_o, d_q, d_k, d_v, ws=None, stream=None):
+    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _check(load().pisa_sparse_attn_backward(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(sel), _ptr(o),
+                                            _ptr(o_lse), _ptr(d_o), _ptr(d_q), _ptr(d_k), _ptr(d_v), _ptr(ws), nbytes,
+                                            _stream(stream)), "pisa_sparse_attn_backward")
 
 
 def pisa_decode_step(shape, host_lens, q_new, k_new, v_new, k_cache, v_cache, pyr_sum, pyr_mean, o, sel_out=None,

@@ -153,3 +153,16 @@ def test_noalloc_rejects_oversized_shape_before_any_hip_call():
     assert b"scratch" in lib.pisa_last_error()
     assert lib.pisa_select_noalloc(ctypes.byref(_shape(head_dim=96)), fake, fake, fake, fake, None, None) == \
         P.PISA_EUNSUPPORTED
+
+
+def test_backward_rejects_fp32_before_any_hip_call():
+    lib = P.load()
+    s = _shape(dtype="fp32")
+    fake = ctypes.c_void_p(1 << 20)
+    st = lib.pisa_sparse_attn_backward(ctypes.byref(s), fake, fake, fake, fake, fake, fake, fake, fake, fake, fake,
+                                       fake, 1 << 30, None)
+    assert st == P.PISA_EUNSUPPORTED
+    need = P.pisa_workspace_size(_shape(), P.PISA_OP_ATTN_BWD)
+    assert need > 0
+    assert lib.pisa_sparse_attn_backward(ctypes.byref(_shape()), fake, fake, fake, fake, fake, fake, fake, fake, fake,
+                                         fake, fake, need - 1, None) == P.PISA_EWORKSPACE
