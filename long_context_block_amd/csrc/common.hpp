@@ -285,22 +285,48 @@ __device__ __forceinline__ float readlane(float v, int c) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), c));
 }
 
+// Max / min over all 64 lanes of the wave (every lane gets the result): DPP row reductions, then the
+// four row results read back with readlane.
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_rot<0x128>(v));
+  v = fmaxf(v, dpp_rot<0x124>(v));
+  v = fmaxf(v, dpp_rot<0x122>(v));
+  v = fmaxf(v, dpp_rot<0x121>(v));
+  return fmaxf(fmaxf(readlane(v, 0), readlane(v, 16)), fmaxf(readlane(v, 32), readlane(v, 48)));
+}
+__device__ __forceinline__ float wave_min(float v) {
+  v = fminf(v, dpp_rot<0x128>(v));
+  v = fminf(v, dpp_rot<0x124>(v));
+  v = fminf(v, dpp_rot<0x122>(v));
+  v = fminf(v, dpp_rot<0x121>(v));
+  return fminf(fminf(readlane(v, 0), readlane(v, 16)), fminf(readlane(v, 32), readlane(v, 48)));
+}
+
+
 // Top-K ranking key of candidate c with score v: the order-preserving unsigned image of the float with
 // its 6 low bits replaced by 63 - c, so that a larger key means a higher score, and exactly equal
-// scores order by the lower index. Scores closer than 2^-17 relative also order by index; only such
-// near-ties can rank differently from an exact float comparison.
+// scores order by the lower index. Scores closer than 2^-17 relative also order by index. Callers key
+// v = score - ref, with ref the score of the ranking's first candidate (topk_ref): the quantum is then
+// relative to a candidate's distance from that one, 64 ulp < 1e-3 whenever the distance is below 256,
+// whatever the size of the scores themselves (a unit's candidates differ by far less).
 __device__ __forceinline__ uint32_t topk_key(float v, int c) {
   const uint32_t u = __float_as_uint(v);
   const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
   return (o & ~63u) | (uint32_t)(63 - c);
 }
 
+// The reference of a ranking whose candidate c sits in lane c: lane 0's value if finite, else 0.
+__device__ __forceinline__ float topk_ref(float v) {
+  const float r = readlane(v, 0);
+  return __builtin_isfinite(r) ? r : 0.f;
+}
+
 // Candidates c in [0, n) (ascending node order, one per lane) with scores `score`. True for the lanes
-// among the K best (score descending, index ascending). keys: this wave's 64-entry LDS slice. n, K are
-// wave-uniform.
-__device__ __forceinline__ bool topk_keep(float score, int n, int K, uint32_t* keys) {
+// among the K best (score descending, index ascending), keyed relative to `ref` (wave-uniform). keys:
+// this wave's 64-entry LDS slice. n, K are wave-uniform.
+__device__ __forceinline__ bool topk_keep_ref(float score, int n, int K, uint32_t* keys, float ref) {
   const int lane = lane_id();
-  const uint32_t mine = lane < n ? topk_key(score, lane) : 0u;
+  const uint32_t mine = lane < n ? topk_key(score - ref, lane) : 0u;
   keys[lane] = mine;
   __threadfence_block();
   int rank = 0;
@@ -310,6 +336,11 @@ __device__ __forceinline__ bool topk_keep(float score, int n, int K, uint32_t* k
   }
   __threadfence_block();
   return lane < n && rank < K;
+}
+
+// The same, keyed relative to the first candidate's score.
+__device__ __forceinline__ bool topk_keep(float score, int n, int K, uint32_t* keys) {
+  return topk_keep_ref(score, n, K, keys, topk_ref(score));
 }
 
 // Same, with the scores already in s[0, n) (LDS).
@@ -358,24 +389,6 @@ struct PairRun {
     return end;
   }
 };
-
-// Max / min over all 64 lanes of the wave (every lane gets the result): DPP row reductions, then the
-// four row results read back with readlane.
-__device__ __forceinline__ float wave_max(float v) {
-  v = fmaxf(v, dpp_rot<0x128>(v));
-  v = fmaxf(v, dpp_rot<0x124>(v));
-  v = fmaxf(v, dpp_rot<0x122>(v));
-  v = fmaxf(v, dpp_rot<0x121>(v));
-  return fmaxf(fmaxf(readlane(v, 0), readlane(v, 16)), fmaxf(readlane(v, 32), readlane(v, 48)));
-}
-__device__ __forceinline__ float wave_min(float v) {
-  v = fminf(v, dpp_rot<0x128>(v));
-  v = fminf(v, dpp_rot<0x124>(v));
-  v = fminf(v, dpp_rot<0x122>(v));
-  v = fminf(v, dpp_rot<0x121>(v));
-  return fminf(fminf(readlane(v, 0), readlane(v, 16)), fminf(readlane(v, 32), readlane(v, 48)));
-}
-
 
 // Work-group index remapped so that consecutive logical indices run on the same XCD (dispatch
 // places work-group w on XCD w % 8), keeping each XCD's L2 on a contiguous slice of the work.

@@ -58,6 +58,7 @@ __global__ __launch_bounds__(group_waves<KM>() * 64) void route_group_kernel(Gro
   // a unit's keys (padded by 4 words: the units' 16-byte reads fall on different banks)
   __shared__ __align__(16) uint32_t s_key[kGroupWaves][UG][NC + 4];
   __shared__ unsigned long long s_mask[kGroupWaves][UG];
+  __shared__ float s_ref[kGroupWaves][UG];  // per unit: the reference of its Top-K keys at this level
   const int lane = lane_id(), wave = threadIdx.x >> 6, col = lane & 15, g = lane >> 4;
   const int xo = col / G, h = col % G;  // this lane's unit and head
   const int cb = 2 * (col >> 2) + ((col >> 1) & 1);  // candidate of row col in M-tile 0
@@ -236,6 +237,11 @@ __global__ __launch_bounds__(group_waves<KM>() * 64) void route_group_kernel(Gro
         };
         float sc[KM][2];
         head_scores(sc, ~0u);
+        // keys relative to the unit's first candidate's hi score (the reference topk_keep takes): lane
+        // x G of lane group 0 holds the head sum of candidate 0 (m = 0, a = 0) of unit x
+        float ref1 = __shfl(sc[0][0], xo * G);
+        ref1 = __builtin_isfinite(ref1) ? ref1 : 0.f;
+        if (h == 0 && g == 0) s_ref[wave][xo] = ref1;  // read back by pass 2
         // ---- owned candidates: hi score, hi Top-K
         float own_s[OWN][2];
         bool own_v[OWN][2], in[OWN][2];
@@ -250,9 +256,16 @@ __global__ __launch_bounds__(group_waves<KM>() * 64) void route_group_kernel(Gro
             const int c = 8 * m + 2 * g + a;
             own_v[j][a] = m < KM && c < my_nc;
             own_s[j][a] = s;
+          }
+#pragma unroll
+        for (int j = 0; j < OWN; ++j)
+#pragma unroll
+          for (int a = 0; a < 2; ++a) {
+            const int m = h + j * G;
+            const int c = 8 * m + 2 * g + a;
             // every slot below NC has an owner: slots past the unit's candidates hold 0, which ranks
             // below every key (keys of finite and infinite scores are positive)
-            if (m < KM) s_key[wave][xo][c] = own_v[j][a] ? topk_key(s, c) : 0u;
+            if (m < KM) s_key[wave][xo][c] = own_v[j][a] ? topk_key(own_s[j][a] - ref1, c) : 0u;
           }
         __threadfence_block();
         // in-flags of the owned candidates (fewer than K of the unit's keys above theirs), all owned
@@ -264,7 +277,9 @@ __global__ __launch_bounds__(group_waves<KM>() * 64) void route_group_kernel(Gro
           for (int j = 0; j < OWN; ++j)
 #pragma unroll
             for (int a = 0; a < 2; ++a) {
-              key[j][a] = topk_key(own_s[j][a], 8 * (h + j * G) + 2 * g + a);
+              // the owned candidate's own key, stored in its slot above (0 for a slot without one)
+              const int m = h + j * G;
+              key[j][a] = m < KM ? s_key[wave][xo][8 * m + 2 * g + a] : 0u;
               rank[j][a] = 0;
             }
 #pragma unroll 2
@@ -384,6 +399,7 @@ __global__ __launch_bounds__(group_waves<KM>() * 64) void route_group_kernel(Gro
               n_ref += __popcll(rb[j][a] & umask);
             }
           uint32_t rkey[OWN][2];
+          const float ref2 = s_ref[wave][xo];  // pass 1's reference (keys of both passes share it)
 #pragma unroll
           for (int j = 0; j < OWN; ++j)
 #pragma unroll
@@ -392,7 +408,7 @@ __global__ __launch_bounds__(group_waves<KM>() * 64) void route_group_kernel(Gro
               float sv = 0.f;
 #pragma unroll
               for (int mm = 0; mm < KM; ++mm) sv = mm == m ? sc[mm][a] : sv;
-              rkey[j][a] = topk_key(sv, 8 * m + 2 * g + a);
+              rkey[j][a] = topk_key(sv - ref2, 8 * m + 2 * g + a);
               if (refine[j][a]) s_key[wave][xo][pos[j][a]] = rkey[j][a];
             }
           if (h == 0 && g == 0) {  // one lane per unit pads the slots after its undecided keys

@@ -554,8 +554,12 @@ __global__ __launch_bounds__(256) void finalize_half_kernel(FinParams<float> p) 
     const int leaf_c = 2 * kp[it] + (cl & 1);
     const bool valid = kp[it] >= 0 && (long long)leaf_c * p.C <= (long long)i;
     const int n_cand = __popcll(__ballot(valid) & hmask);  // valid candidates are a prefix
-    // Top-K by key (score descending, index ascending); slots past the candidates hold 0
-    const uint32_t mine = cl < n_cand ? topk_key(sc[it], cl) : 0u;
+    // Top-K by key (score descending, index ascending; keyed relative to the unit's first candidate, as
+    // topk_keep does); slots past the candidates hold 0
+    const float r0 = readlane(sc[it], 0), r1 = readlane(sc[it], 32);
+    const float hr = half ? r1 : r0;
+    const float ref = __builtin_isfinite(hr) ? hr : 0.f;
+    const uint32_t mine = cl < n_cand ? topk_key(sc[it] - ref, cl) : 0u;
     keys[cl] = mine;
     __threadfence_block();
     bool keep = cl < n_cand;

@@ -342,7 +342,10 @@ __device__ bool select_level_refine(const Rows& rows, const float* norms, int le
   const float e = lane < n_cand ? scale * qnorm_sum * fmaxf(nb0, nb1) : 0.f;
   __threadfence_block();
   const float sh = lane < n_cand ? s_sc[lane] : kNegInf;
-  const bool in = topk_keep_lds(s_sc, n_cand, K, keys);
+  // both passes key relative to the first candidate's hi score (the routing kernels that walk several
+  // units per wave use the same reference)
+  const float ref = topk_ref(sh);
+  const bool in = topk_keep_ref(sh, n_cand, K, keys, ref);
   const float lo_b = sh - e, hi_b = sh + e;
   const float u_out = wave_max(!in && lane < n_cand ? hi_b : kNegInf);
   const float l_in = wave_min(in ? lo_b : -kNegInf);
@@ -365,7 +368,7 @@ __device__ bool select_level_refine(const Rows& rows, const float* norms, int le
   }
   __threadfence_block();
   const float key = refine ? s_sc[lane < n_cand ? lane : 0] : (in ? -kNegInf : kNegInf);
-  return topk_keep(key, n_cand, K, keys);
+  return topk_keep_ref(key, n_cand, K, keys, ref);
 }
 
 // Walk from the root to level 1 for query position i. Level l has e_l = (i >> (log2 C + l)) + 1
