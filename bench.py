@@ -208,6 +208,7 @@ def decode_latency(P, I, torch, steps_cap=None):
     sel = torch.empty((dec.B, dec.Hkv, dec.K), dtype=torch.int32, device="cuda")
     lens0 = [int(x) for x in dec.lens0]
     steps = dec.steps if steps_cap is None else min(steps_cap, dec.steps)
+    ws = P.alloc_workspace(s, P.PISA_OP_DECODE)
 
     def run(record):
         P.pisa_build_pyramid(s, kc, pmean, psum, host_lens=lens0)
@@ -217,7 +218,7 @@ def decode_latency(P, I, torch, steps_cap=None):
             if record:
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 a.record()
-            P.pisa_decode_step(s, lens, qn[st], kn[st], vn[st], kc, vc, psum, pmean, o, sel)
+            P.pisa_decode_step(s, lens, qn[st], kn[st], vn[st], kc, vc, psum, pmean, o, sel, ws=ws)
             if record:
                 b.record()
                 evs.append((a, b))

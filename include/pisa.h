@@ -160,7 +160,12 @@ pisa_status pisa_sparse_attn_backward(const pisa_shape* shape, const void* q, co
  *   q_new [B, Hq, d]; k_new, v_new [B, Hkv, d]; k_cache, v_cache [B, Hkv, Nmax, d] (updated);
  *   pyr_sum, pyr_mean: the decode pyramid (layout of shape), initialised by pisa_build_pyramid with
  *   pyr_sum set and host_lens = the cached lengths; o out [B, Hq, d]; sel_out out, nullable, int32
- *   [B, Hkv, K]. ws may be NULL when pisa_workspace_size(PISA_OP_DECODE) is 0. */
+ *   [B, Hkv, K].
+ *   ws: pisa_workspace_size(shape, PISA_OP_DECODE) bytes, 16-byte aligned, all zero before its first
+ *   decode step (for example from hipMemset once). It holds per-unit arrival counters that every step
+ *   leaves at zero again, so one zeroed workspace serves every later step of the same shape; other
+ *   calls must not write it in between, and steps that share it must not overlap in time (one
+ *   workspace per stream). PISA_EWORKSPACE when it is missing or too small. */
 pisa_status pisa_decode_step(const pisa_shape* shape, const int32_t* host_lens, const void* q_new, const void* k_new,
                              const void* v_new, void* k_cache, void* v_cache, float* pyr_sum, float* pyr_mean, void* o,
                              int32_t* sel_out, void* ws, size_t ws_bytes, void* stream);

@@ -292,6 +292,25 @@ size_t carve_bsa(const Plan& p, void* ws, BsaWs* w) {
   return c.off;
 }
 
+struct DecodeWs {
+  int* ticket;
+  float* part_lse;
+  float* part_o;
+};
+
+// Decode workspace: the arrival counters first (the part that must be zero before the first step),
+// then the per-candidate-leaf partial results.
+size_t carve_decode(const Plan& p, void* ws, DecodeWs* w) {
+  Carver c(ws);
+  DecodeWs x{};
+  const size_t cand = (size_t)p.BH * 2 * p.sd.K;
+  x.ticket = (int*)c.take(p.BH * 4);
+  x.part_lse = (float*)c.take(cand * p.sd.G * 4);
+  x.part_o = (float*)c.take(cand * p.sd.G * p.sd.D * 4);
+  if (w) *w = x;
+  return c.off;
+}
+
 pisa_status check_ws(size_t need, const void* ws, size_t ws_bytes) {
   if (need == 0) return PISA_OK;
   if (!ws) return fail(PISA_EWORKSPACE, "workspace is null, %zu bytes needed", need);
@@ -383,7 +402,7 @@ pisa_status pisa_workspace_size(const pisa_shape* shape, int32_t op, size_t* byt
   switch (op) {
     case PISA_OP_SELECT: *bytes = carve_select(p, nullptr, nullptr); break;
     case PISA_OP_ATTN: *bytes = carve_attn(p, nullptr, nullptr); break;
-    case PISA_OP_DECODE: *bytes = 0; break;
+    case PISA_OP_DECODE: *bytes = carve_decode(p, nullptr, nullptr); break;
     case PISA_OP_BSA: *bytes = carve_bsa(p, nullptr, nullptr); break;
     case PISA_OP_ATTN_BWD: *bytes = carve_attn_bwd(p, nullptr, nullptr); break;
     default: return fail(PISA_EINVAL, "unknown op %d", op);
@@ -569,8 +588,6 @@ pisa_status pisa_sparse_attn_backward(const pisa_shape* shape, const void* q, co
 pisa_status pisa_decode_step(const pisa_shape* shape, const int32_t* host_lens, const void* q_new, const void* k_new,
                              const void* v_new, void* k_cache, void* v_cache, float* pyr_sum, float* pyr_mean, void* o,
                              int32_t* sel_out, void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   Plan p;
   pisa_status st = plan(shape, &p);
   if (st != PISA_OK) return st;
@@ -598,6 +615,14 @@ pisa_status pisa_decode_step(const pisa_shape* shape, const int32_t* host_lens, 
   da.scale = p.sd.scale;
   da.bf16 = p.sd.bf16;
   da.lv = p.sd.lv;
+  const size_t need = carve_decode(p, nullptr, nullptr);
+  st = check_ws(need, ws, ws_bytes);
+  if (st != PISA_OK) return st;
+  DecodeWs w;
+  carve_decode(p, ws, &w);
+  da.ticket = w.ticket;
+  da.part_o = w.part_o;
+  da.part_lse = w.part_lse;
   hipError_t e;
   {
     Stage sc((hipStream_t)stream, "decode_step");

@@ -104,7 +104,12 @@ struct DecodeArgs {
   bool bf16;
   Levels lv;
   LensArg lens;
+  int* ticket;      // [B*Hkv] arrival counters, zero before the step (the step leaves them zero)
+  float* part_o;    // [B*Hkv, 2K, G, D]
+  float* part_lse;  // [B*Hkv, 2K, G]
 };
+// Work-groups per decode unit for top-k K (the candidate leaves, 2K, one per wave).
+int decode_splits(int K);
 hipError_t launch_decode(const DecodeArgs& da, const void* q_new, const void* k_new, const void* v_new, void* k_cache,
                          void* v_cache, float* pyr_sum, float* pyr_mean, void* o, int* sel_out, hipStream_t st);
 

@@ -238,7 +238,10 @@ def torch_dtype(shape: Shape):
 
 
 def alloc_workspace(shape: Shape, op: int, device="cuda"):
+    """Workspace for `op`; the decode step's starts zeroed, as its counters require."""
     n = pisa_workspace_size(shape, op)
+    if op == PISA_OP_DECODE:
+        return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
 

@@ -55,7 +55,8 @@ def test_workspace_sizes():
     assert P.pisa_workspace_size(_shape(dtype="fp32", q_tile=1), P.PISA_OP_SELECT) == 0
     assert P.pisa_workspace_size(s, P.PISA_OP_ATTN) >= U * 16 * 4 * 128 * 2
     assert P.pisa_workspace_size(s, P.PISA_OP_BSA) >= 8 * 1024 * 128 * 4
-    assert P.pisa_workspace_size(s, P.PISA_OP_DECODE) == 0
+    # decode: one arrival counter per unit, then each candidate leaf's (2K per unit) per-head LSE and output
+    assert P.pisa_workspace_size(s, P.PISA_OP_DECODE) >= 8 * 4 + 8 * 32 * 4 * (128 + 1) * 4
     with pytest.raises(P.PisaError) as e:
         P.pisa_workspace_size(s, 99)
     assert e.value.status == P.PISA_EINVAL
@@ -135,6 +136,10 @@ def test_host_lens_validated():
     full = (ctypes.c_int32 * 2)(1024, 3)  # decode needs len < capacity
     assert lib.pisa_decode_step(ctypes.byref(s), full, g, g, g, g, g, g, g, g, None, None, 0, None) == P.PISA_EINVAL
     assert lib.pisa_decode_step(ctypes.byref(s), None, g, g, g, g, g, g, g, g, None, None, 0, None) == P.PISA_EINVAL
+    ok = (ctypes.c_int32 * 2)(1000, 3)
+    assert lib.pisa_decode_step(ctypes.byref(s), ok, g, g, g, g, g, g, g, g, None, None, 0, None) == P.PISA_EWORKSPACE
+    need = P.pisa_workspace_size(s, P.PISA_OP_DECODE)
+    assert lib.pisa_decode_step(ctypes.byref(s), ok, g, g, g, g, g, g, g, g, None, g, need - 1, None) == P.PISA_EWORKSPACE
 
 
 def test_status_strings():

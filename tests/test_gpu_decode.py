@@ -101,14 +101,17 @@ def _run_decode(dec: I.Decode, min_decided: float, label: str):
     sel = torch.empty((dec.B, dec.Hkv, dec.K), dtype=torch.int32, device="cuda")
     sels = np.empty((dec.steps, dec.B, dec.Hkv, dec.K), dtype=np.int32)
     outs = np.empty((dec.steps, dec.B, dec.Hq, dec.d), dtype=np.float32)
+    ws = P.alloc_workspace(s, P.PISA_OP_DECODE)
     for step in range(dec.steps):
-        P.pisa_decode_step(s, lens, qn[step], kn[step], vn[step], kc, vc, psum, pmean, o, sel)
+        P.pisa_decode_step(s, lens, qn[step], kn[step], vn[step], kc, vc, psum, pmean, o, sel, ws=ws)
         sels[step] = sel.cpu().numpy()
         outs[step] = o.float().cpu().numpy()
         lens = [x + 1 for x in lens]
         if step % 64 == 0:
             say(f"[decode] {label}: GPU step {step} of {dec.steps}")
     torch.cuda.synchronize()
+    # the per-unit arrival counters at the head of the workspace are back at zero after every step
+    assert int(ws[:4 * dec.B * dec.Hkv].view(torch.int32).abs().sum().item()) == 0
     n, offs, nodes = P.pisa_pyramid_layout(s)
     pm = pmean.cpu().numpy()
     k_app = np.empty((dec.B, dec.Hkv, dec.steps, dec.d), dtype=np.float32)
@@ -117,7 +120,7 @@ def _run_decode(dec: I.Decode, min_decided: float, label: str):
         n0 = int(dec.lens0[b])
         k_app[b] = kc[b, :, n0:n0 + dec.steps].float().cpu().numpy()
         v_app[b] = vc[b, :, n0:n0 + dec.steps].float().cpu().numpy()
-    del kc, vc, psum, pmean, qn, kn, vn, o, sel
+    del kc, vc, psum, pmean, qn, kn, vn, o, sel, ws
     torch.cuda.empty_cache()
     units = [(b, r) for b in range(dec.B) for r in range(dec.Hkv)]
     GC._CTX.update(dec=dec, sels=sels, outs=outs, pm=pm, offs=offs, nodes=nodes, k_app=k_app, v_app=v_app)
