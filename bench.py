@@ -214,6 +214,10 @@ def decode_latency(P, I, torch, steps_cap=None):
         P.pisa_build_pyramid(s, kc, pmean, psum, host_lens=lens0)
         lens = list(lens0)
         evs = []
+        if record:
+            # a device-side delay first, so that the host has queued every step before the GPU reaches
+            # it: the events then bracket the kernel alone, not the host's launch cadence
+            torch.cuda._sleep(100_000_000)
         for st in range(steps):
             if record:
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

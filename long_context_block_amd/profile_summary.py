@@ -41,6 +41,12 @@ STAGE_KERNELS = {
     "attn_merge": ["attn_merge_kernel"],
     "bsa_select": ["bsa_kernel"],
     "decode_step": ["decode_kernel"],
+    "attn_backward": ["bwd_prep_kernel", "attn_bwd_dq_kernel", "attn_bwd_dkdv_kernel", "bwd_dq_merge_kernel",
+                      "bwd_finish_kernel"],
+    "flat_leaf_lse": ["flat_leaf_lse_kernel"],
+    "selection_quality": ["quality_kernel"],
+    "pyramid_pooled": ["pool_leaf_kernel", "pool_level_kernel"],
+    "select_variant": ["variant_walk_kernel"],
 }
 
 
