@@ -78,7 +78,7 @@ typedef struct {
   int32_t dtype;      /* pisa_dtype of Q, K, V, O                                          */
 } pisa_shape;
 
-/* Pyramid layout for a shape (host only, enqueues nothing). Level l has n_l = ceil(n_{l-1}/2)
+/* Pyramid layout for a shape (host only, enqueues nothing; each output pointer may be NULL). Level l has n_l = ceil(n_{l-1}/2)
  * nodes, n_0 = ceil(seq_len / C), up to a single root; levels are stored leaf-first, so node
  * (l, j) of head (b, r) is row ((b*Hkv + r) * nodes_per_head + level_offset[l] + j) of a
  * [B*Hkv*nodes_per_head, d] fp32 array. n_levels counts the root. level_offset has room for 32
@@ -239,7 +239,8 @@ pisa_status pisa_build_pyramid_pooled(const pisa_shape* shape, const void* k, in
 pisa_status pisa_select_variant(const pisa_shape* shape, const pisa_variant* variant, const void* q, const void* k,
                                 const float* summary, const float* variance, int32_t* sel, void* stream);
 
-const char* pisa_status_string(pisa_status status);
+/* A message for a status value (any int; values that are not a pisa_status get a generic message). */
+const char* pisa_status_string(int32_t status);
 const char* pisa_last_error(void);
 
 /* Stage timing for profiling, off by default. While enabled (per calling thread), every call
@@ -248,7 +249,7 @@ const char* pisa_last_error(void);
  * the recorded events, adds each stage's elapsed time to a per-name total and count, forgets the
  * events and writes up to `cap` entries: names (NUL-terminated, at most 31 characters),
  * total milliseconds and launch counts. It returns the number of distinct stage names (which may
- * exceed cap), or a negative pisa_status. pisa_stage_timing(0) also discards the totals. Event
+ * exceed cap), or a negative pisa_status (PISA_EINVAL for cap < 0). pisa_stage_timing(0) also discards the totals. Event
  * creation happens here, so do not enable it under stream capture. */
 pisa_status pisa_stage_timing(int32_t enable);
 int32_t pisa_stage_times(char (*names)[32], double* total_ms, int32_t* count, int32_t cap);

@@ -369,8 +369,8 @@ pisa_status scratch_address(void** out) {
 
 extern "C" {
 
-const char* pisa_status_string(pisa_status s) {
-  switch (s) {
+const char* pisa_status_string(int32_t s) {
+  switch (s) {  // any int: callers may pass a value that is not a pisa_status
     case PISA_OK: return "PISA_OK";
     case PISA_EINVAL: return "PISA_EINVAL: invalid argument";
     case PISA_EUNSUPPORTED: return "PISA_EUNSUPPORTED: unsupported shape";
@@ -789,6 +789,7 @@ pisa_status pisa_stage_timing(int32_t enable) {
 }
 
 int32_t pisa_stage_times(char (*names)[32], double* total_ms, int32_t* count, int32_t cap) {
+  if (cap < 0) return fail(PISA_EINVAL, "cap must be >= 0");
   for (auto& e : g_timer.pending) {
     if (hipEventSynchronize(e.b) != hipSuccess) return fail(PISA_EHIP, "hipEventSynchronize failed");
     float ms = 0.f;

@@ -23,11 +23,12 @@
 
 namespace pisa {
 
-// waves per work-group: the per-wave LDS lists grow with the candidate tiles (KM)
-constexpr int kGroupWavesK16 = 16;  // KM <= 4 (K <= 16): LDS holds the lists of 16 waves
-template <int KM>
+// waves per work-group: 16 (128 registers each) for the hot shape (d = 128, K <= 16, GQA 4); fewer where
+// a wave's state grows (more candidate tiles, more units' heads per column block, or d = 64's longer
+// per-row loops), so that no variant spills registers
+template <int D, int G, int KM>
 constexpr int group_waves() {
-  return KM <= 4 ? kGroupWavesK16 : 12;
+  return (KM > 4 || G == 16) ? 8 : (D == 128 && G == 4) ? 16 : 12;
 }
 constexpr int kGroupLdsBytes = 128 * 1024;
 constexpr int kRowRound = 4;  // M-tiles of one unit whose hi rows are in flight together
@@ -44,14 +45,14 @@ struct GroupRouteParams {
 };
 
 template <int D, int C, int G, int KM>
-__global__ __launch_bounds__(group_waves<KM>() * 64) void route_group_kernel(GroupRouteParams p, int lds_first,
+__global__ __launch_bounds__((group_waves<D, G, KM>() * 64)) void route_group_kernel(GroupRouteParams p, int lds_first,
                                                                       int wg_per_head) {
   constexpr int UG = 16 / G;             // units per wave
   constexpr int LOG2C = C == 64 ? 6 : 5;
   constexpr int NS = D / 32;             // k steps
   constexpr int OWN = (KM + G - 1) / G;  // owned M-tile slots per lane (x2 candidates)
   constexpr int NC = 8 * KM;             // candidate slots per unit (>= 2K)
-  constexpr int kGroupWaves = group_waves<KM>();
+  constexpr int kGroupWaves = group_waves<D, G, KM>();
   __shared__ __align__(16) uint16_t s_hi[kGroupLdsBytes / 2];
   __shared__ float s_bound[kGroupLdsBytes / 128];
   __shared__ int s_kept[kGroupWaves][2][UG][NC / 2];
@@ -506,7 +507,7 @@ static hipError_t route_group_t(const SelDims& sd, const void* q, const void* hi
   const long long groups = (sd.N + 16 / G - 1) / (16 / G);
   long long wph = 256 / BH;  // about one work-group per CU
   if (wph < 1) wph = 1;
-  constexpr int kGroupWaves = group_waves<KM>();
+  constexpr int kGroupWaves = group_waves<D, G, KM>();
   if (wph > (groups + kGroupWaves - 1) / kGroupWaves) wph = (groups + kGroupWaves - 1) / kGroupWaves;
   hipLaunchKernelGGL((route_group_kernel<D, C, G, KM>), dim3((unsigned)(BH * wph)), dim3(kGroupWaves * 64), 0, st, p,
                      (int)sd.lv.roff[lcut], (int)wph);

@@ -174,13 +174,22 @@ __global__ __launch_bounds__(256, FUSED ? 2 : 4) void route_kernel(RouteParams<T
 constexpr int kRouteLdsBytes = 128 * 1024;
 constexpr int kRouteUnits = 4;
 
+// waves per work-group: 16 for up to 4 candidate tiles, 8 (256 registers each) for 8 tiles (K > 16), so that
+// the larger walk state does not spill
+template <int KM>
+constexpr int route_lds_waves() {
+  return KM <= 4 ? 16 : 8;
+}
+
 template <int D, int C, int KM>
-__global__ __launch_bounds__(1024) void route_lds_kernel(RouteParams<uint16_t> p, int lds_first, int wg_per_head) {
+__global__ __launch_bounds__(route_lds_waves<KM>() * 64) void route_lds_kernel(RouteParams<uint16_t> p, int lds_first,
+                                                                                int wg_per_head) {
   constexpr int kLog2C = C == 64 ? 6 : 5;
+  constexpr int NW = route_lds_waves<KM>();
   __shared__ __align__(16) uint16_t s_hi[kRouteLdsBytes / 2];
   __shared__ float s_bound[kRouteLdsBytes / 128];  // one per staged row (rows of >= 64 values)
-  __shared__ __align__(16) float s_sc[16][64];
-  __shared__ __align__(16) uint32_t s_key[16][64];
+  __shared__ __align__(16) float s_sc[NW][64];
+  __shared__ __align__(16) uint32_t s_key[NW][64];
   const int lane = lane_id(), wave = threadIdx.x >> 6, r16 = lane & 15, grp = lane >> 4;
   const int BH = p.B * p.Hkv;
   const int bh = blockIdx.x % BH, w = blockIdx.x / BH;  // consecutive work-groups: different heads
@@ -196,7 +205,7 @@ __global__ __launch_bounds__(1024) void route_lds_kernel(RouteParams<uint16_t> p
   const int b = bh / p.Hkv, r = bh % p.Hkv;
   const bool hv = r16 < p.G;
   const int groups = (p.N + kRouteUnits - 1) / kRouteUnits;
-  for (int gi = w * 16 + wave; gi < groups; gi += wg_per_head * 16) {
+  for (int gi = w * NW + wave; gi < groups; gi += wg_per_head * NW) {
     for (int it = 0; it < kRouteUnits; ++it) {
       const int i = gi * kRouteUnits + it;
       if (i >= p.N) break;
@@ -738,23 +747,29 @@ static hipError_t route_t(const SelDims& sd, const void* q, const void* k, const
     const long long groups = (sd.N + kRouteUnits - 1) / kRouteUnits;
     long long wph = 256 / BH;  // about one work-group per CU
     if (wph < 1) wph = 1;
-    if (wph > (groups + 15) / 16) wph = (groups + 15) / 16;
-    if (sd.K <= 16)
-      hipLaunchKernelGGL((route_lds_kernel<D, C, 4>), dim3((unsigned)(BH * wph)), dim3(1024), 0, st, p, lds_first,
+    if (sd.K <= 16) {
+      constexpr int NW = route_lds_waves<4>();
+      if (wph > (groups + NW - 1) / NW) wph = (groups + NW - 1) / NW;
+      hipLaunchKernelGGL((route_lds_kernel<D, C, 4>), dim3((unsigned)(BH * wph)), dim3(NW * 64), 0, st, p, lds_first,
                          (int)wph);
-    else
-      hipLaunchKernelGGL((route_lds_kernel<D, C, 8>), dim3((unsigned)(BH * wph)), dim3(1024), 0, st, p, lds_first,
+    } else {
+      constexpr int NW = route_lds_waves<8>();
+      if (wph > (groups + NW - 1) / NW) wph = (groups + NW - 1) / NW;
+      hipLaunchKernelGGL((route_lds_kernel<D, C, 8>), dim3((unsigned)(BH * wph)), dim3(NW * 64), 0, st, p, lds_first,
                          (int)wph);
+    }
     return hipGetLastError();
   }
-  p.upw = 4;
-  const long long waves = (U + p.upw - 1) / p.upw;
-  const long long blocks = (waves + 3) / 4;
-  if (sd.K <= 16)
-    hipLaunchKernelGGL((route_kernel<T, D, C, FUSED, 4>), dim3((unsigned)blocks), dim3(256), 0, st, p);
-  else
-    hipLaunchKernelGGL((route_kernel<T, D, C, FUSED, 8>), dim3((unsigned)blocks), dim3(256), 0, st, p);
-  return hipGetLastError();
+  else {
+    p.upw = 4;
+    const long long waves = (U + p.upw - 1) / p.upw;
+    const long long blocks = (waves + 3) / 4;
+    if (sd.K <= 16)
+      hipLaunchKernelGGL((route_kernel<T, D, C, FUSED, 4>), dim3((unsigned)blocks), dim3(256), 0, st, p);
+    else
+      hipLaunchKernelGGL((route_kernel<T, D, C, FUSED, 8>), dim3((unsigned)blocks), dim3(256), 0, st, p);
+    return hipGetLastError();
+  }
 }
 
 template <typename T, bool FUSED>
