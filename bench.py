@@ -349,7 +349,7 @@ def ablations(P, torch, pf, positions, reps=2):
         for _ in range(reps):
             once()
         torch.cuda.synchronize()
-        st = {n: t / c for n, (t, c) in P.pisa_stage_times().items()}
+        st = {n: t / reps for n, (t, c) in P.pisa_stage_times().items()}  # per call (a stage may launch per chunk)
         P.pisa_stage_timing(False)
         P.pisa_selection_quality(s, leaf, row, pos, sel, flat, rec, mass)
         torch.cuda.synchronize()
@@ -398,7 +398,7 @@ def crossover(P, I, torch, lengths=(16384, 32768, 65536, 131072, 262144), reps=4
         for _ in range(reps):
             once()
         torch.cuda.synchronize()
-        st = {n: tot / c for n, (tot, c) in P.pisa_stage_times().items()}
+        st = {n: tot / reps for n, (tot, c) in P.pisa_stage_times().items()}  # per call
         P.pisa_stage_timing(False)
         pisa_ms = sum(st.get(n, 0.0) for n in ("pyramid", "route_planes", "route", "regroup_select", "leaf_lse",
                                                 "finalize"))
@@ -574,7 +574,9 @@ def main():
     step_ms = e0.elapsed_time(e1) / args.steps
     stages = P.pisa_stage_times()
     P.pisa_stage_timing(False)
-    st_ms = {name: tot / cnt for name, (tot, cnt) in stages.items()}
+    # per step: a stage's launches in one step add up (the attention launches once per chunk of slices)
+    st_ms = {name: tot / args.steps for name, (tot, cnt) in stages.items()}
+    launches = {name: cnt // args.steps for name, (tot, cnt) in stages.items()}
     log(f"[bench] step {step_ms:.3f} ms (wall {wall / args.steps * 1e3:.3f} ms); stages " +
         ", ".join(f"{n}={v:.3f}" for n, v in sorted(st_ms.items())))
 
@@ -596,7 +598,7 @@ def main():
         torch.cuda.synchronize()
         st1 = P.pisa_stage_times()
         P.pisa_stage_timing(False)
-        sel_q1_ms = sum(tot / cnt for name, (tot, cnt) in st1.items())
+        sel_q1_ms = sum(tot / n1 for name, (tot, cnt) in st1.items())
         del ws1, sel1
     sel_np = sel.cpu().numpy()
     w = work_counts(pf, sel_np)
@@ -629,8 +631,9 @@ def main():
         if kms <= 0:
             continue
         if traffic and n in traffic:
-            per_kernel.setdefault(n, {})["hbm_bytes_measured"] = round(traffic[n])
-            per_kernel[n]["hbm_GB/s_measured"] = round(traffic[n] / (kms * 1e-3) / 1e9, 1)
+            # the counter summary is per launch; a stage may launch once per chunk of slices in a step
+            per_kernel.setdefault(n, {})["hbm_bytes_measured"] = round(traffic[n] * launches.get(n, 1))
+            per_kernel[n]["hbm_GB/s_measured"] = round(traffic[n] * launches.get(n, 1) / (kms * 1e-3) / 1e9, 1)
         if bd == "hbm":
             per_kernel.setdefault(n, {}).update({"ms": round(kms, 4), "GB/s": round(amt / (kms * 1e-3) / 1e9, 1),
                                                  "frac_hbm": round(amt / (kms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)})
@@ -665,7 +668,8 @@ def main():
         "work": w,
         "roofline": {"kernel": dom, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4),
-                     "traffic": round(traffic[dom]) if traffic and dom in traffic else None},
+                     "traffic": round(traffic[dom]) if traffic and dom in traffic else None,
+                     "launches_per_step": launches.get(dom, 1)},
     }
     if not args.no_backward and pf.dtype == "bf16":
         # backward of the sparse attention on this step's selection: forward with its LSE once, then the
@@ -681,10 +685,11 @@ def main():
         P.pisa_sparse_attn_backward(s, q, k, v, sel, o, o_lse, d_o, dq, dk, dv, ws_b)
         torch.cuda.synchronize()
         P.pisa_stage_timing(True)
-        for _ in range(max(2, args.steps // 2)):
+        nb = max(2, args.steps // 2)
+        for _ in range(nb):
             P.pisa_sparse_attn_backward(s, q, k, v, sel, o, o_lse, d_o, dq, dk, dv, ws_b)
         torch.cuda.synchronize()
-        stb = {n_: t_ / c_ for n_, (t_, c_) in P.pisa_stage_times().items()}
+        stb = {n_: t_ / nb for n_, (t_, c_) in P.pisa_stage_times().items()}  # per call
         P.pisa_stage_timing(False)
         b_ms = stb.get("regroup_attn_bwd", 0.0) + stb.get("attn_backward", 0.0)
         b_flops = 10 * pf.d * w["attended_keys"]  # S, dP, dV, dK and dQ: five products of 2 d per attended key

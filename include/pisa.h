@@ -127,6 +127,13 @@ pisa_status pisa_select_noalloc(const pisa_shape* shape, const void* q, const vo
                                 int32_t* sel, float* sel_lse, void* stream);
 size_t pisa_select_noalloc_max_bytes(void);
 
+/* pisa_sparse_attn and pisa_sparse_attn_backward process the batch in chunks of consecutive (sequence,
+ * KV head) slices, the fewest whose workspace fits 16 GiB (at least one slice each), so their
+ * pisa_workspace_size is that of one chunk, not of the whole batch. The environment variable
+ * PISA_ATTN_CHUNK_MIB, if set to a smaller positive number of MiB, lowers the budget; it is read at every
+ * call, so keep it unchanged between the workspace query and the call. Results do not depend on the
+ * chunking. */
+
 /* Block-sparse attention over the selected leaves (explainer 核心方法 §7, last step). For each
  * (b, h, i): O = sum over t in T of softmax_t(s * q_{h,i} . k_t) v_t, T = the tokens t <= i of the
  * leaves in sel[b, h/G, i, :]; the softmax normalises over T only.

@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <algorithm>
+#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -292,6 +293,82 @@ size_t carve_bsa(const Plan& p, void* ws, BsaWs* w) {
   return c.off;
 }
 
+// The attention and its backward run over chunks of consecutive (sequence, KV head) slices, so that
+// their workspace (which holds a partial row per selected leaf, K times the slice's output) stays near
+// kAttnChunkBytes whatever the batch and head count. Q, K, V, sel, O and the gradients are contiguous per
+// slice ([B, H, N, ...] with the G query heads of KV head r at r G .. r G + G - 1), so a chunk of S
+// slices starting at flat slice f is the shape (B = S, Hkv = 1, Hq = G) on pointers offset by f slices;
+// every kernel computes a (unit, leaf) pair and a unit's merge independently of how units are grouped.
+// The budget is a few percent of the device memory: a 64K-token prefill with 8 KV heads is one chunk,
+// a batch of eight 256K-token sequences takes 22 chunks of 3 slices (13 GB instead of 280 GB).
+constexpr size_t kAttnChunkBytes = size_t(16) << 30;
+
+// The chunk budget: kAttnChunkBytes, or less when the environment variable PISA_ATTN_CHUNK_MIB holds a
+// smaller positive number of MiB (read at every call, so the workspace query and the call agree as long
+// as it does not change in between).
+size_t attn_chunk_bytes() {
+  const char* e = std::getenv("PISA_ATTN_CHUNK_MIB");
+  if (!e || !*e) return kAttnChunkBytes;
+  char* end = nullptr;
+  const unsigned long long mib = std::strtoull(e, &end, 10);
+  if (end == e || *end || mib == 0 || mib >= (kAttnChunkBytes >> 20)) return kAttnChunkBytes;
+  return (size_t)mib << 20;
+}
+
+struct AttnChunks {
+  long long slices;  // B * Hkv
+  long long per;     // slices per chunk
+  Plan cp;           // plan of a full chunk
+};
+
+// Chunking of shape s for a workspace carve function: the fewest chunks whose workspace fits
+// kAttnChunkBytes (at least one slice per chunk), with the slices spread evenly over them.
+template <class Carve>
+pisa_status attn_chunks(const pisa_shape* s, Carve carve, AttnChunks* out) {
+  pisa_shape one = *s;
+  one.batch = 1;
+  one.n_kv_heads = 1;
+  one.n_q_heads = s->n_q_heads / s->n_kv_heads;
+  Plan p1;
+  pisa_status st = plan(&one, &p1);
+  if (st != PISA_OK) return st;
+  AttnChunks c;
+  c.slices = (long long)s->batch * s->n_kv_heads;
+  const size_t per_slice = carve(p1);
+  long long fit = per_slice ? (long long)(attn_chunk_bytes() / per_slice) : c.slices;
+  if (fit < 1) fit = 1;
+  if (fit > c.slices) fit = c.slices;
+  const long long chunks = (c.slices + fit - 1) / fit;
+  c.per = (c.slices + chunks - 1) / chunks;
+  pisa_shape full = one;
+  full.batch = (int32_t)c.per;
+  st = plan(&full, &c.cp);
+  if (st != PISA_OK) return st;
+  *out = c;
+  return PISA_OK;
+}
+
+// Plan of the chunk of n slices (n <= per).
+pisa_status chunk_plan(const AttnChunks& c, long long n, Plan* p) {
+  if (n == c.per) {
+    *p = c.cp;
+    return PISA_OK;
+  }
+  pisa_shape sub{};
+  sub.batch = (int32_t)n;
+  sub.seq_len = c.cp.sd.N;
+  sub.n_q_heads = c.cp.sd.G;
+  sub.n_kv_heads = 1;
+  sub.head_dim = c.cp.sd.D;
+  sub.block = c.cp.sd.C;
+  sub.top_k = c.cp.sd.K;
+  sub.branch = 2;
+  sub.q_tile = c.cp.sd.q_tile;
+  sub.scale = c.cp.sd.scale;
+  sub.dtype = c.cp.sd.bf16 ? PISA_BF16 : PISA_FP32;
+  return plan(&sub, p);
+}
+
 struct DecodeWs {
   int* ticket;
   float* part_lse;
@@ -401,10 +478,22 @@ pisa_status pisa_workspace_size(const pisa_shape* shape, int32_t op, size_t* byt
   if (st != PISA_OK) return st;
   switch (op) {
     case PISA_OP_SELECT: *bytes = carve_select(p, nullptr, nullptr); break;
-    case PISA_OP_ATTN: *bytes = carve_attn(p, nullptr, nullptr); break;
+    case PISA_OP_ATTN: {
+      AttnChunks c;
+      st = attn_chunks(shape, [](const Plan& q) { return carve_attn(q, nullptr, nullptr); }, &c);
+      if (st != PISA_OK) return st;
+      *bytes = carve_attn(c.cp, nullptr, nullptr);
+      break;
+    }
     case PISA_OP_DECODE: *bytes = carve_decode(p, nullptr, nullptr); break;
     case PISA_OP_BSA: *bytes = carve_bsa(p, nullptr, nullptr); break;
-    case PISA_OP_ATTN_BWD: *bytes = carve_attn_bwd(p, nullptr, nullptr); break;
+    case PISA_OP_ATTN_BWD: {
+      AttnChunks c;
+      st = attn_chunks(shape, [](const Plan& q) { return carve_attn_bwd(q, nullptr, nullptr); }, &c);
+      if (st != PISA_OK) return st;
+      *bytes = carve_attn_bwd(c.cp, nullptr, nullptr);
+      break;
+    }
     default: return fail(PISA_EINVAL, "unknown op %d", op);
   }
   return ok();
@@ -520,30 +609,46 @@ pisa_status pisa_sparse_attn(const pisa_shape* shape, const void* q, const void*
   PISA_CHECK_PTR(sel, "sel");
   PISA_CHECK_PTR(o, "o");
   PISA_CHECK_OPT_PTR(o_lse, "o_lse");
-  const size_t need = carve_attn(p, nullptr, nullptr);
-  st = check_ws(need, ws, ws_bytes);
+  AttnChunks ch;
+  st = attn_chunks(shape, [](const Plan& q) { return carve_attn(q, nullptr, nullptr); }, &ch);
   if (st != PISA_OK) return st;
-  AttnWs w;
-  carve_attn(p, ws, &w);
+  st = check_ws(carve_attn(ch.cp, nullptr, nullptr), ws, ws_bytes);
+  if (st != PISA_OK) return st;
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e;
-  {
-    Stage sc(s, "regroup_attn");
-    e = pisa::launch_regroup(sel, p.U, p.sd.K, p.sd.N, p.sd.lv.n[0], (int)p.BH, p.sd.chunk_log2, w.counts,
-                             w.offsets, w.ranks, true, w.pairs, s);
+  const long long G = p.sd.G, N = p.sd.N, D = p.sd.D, K = p.sd.K;
+  for (long long f = 0; f < ch.slices; f += ch.per) {
+    const long long n = ch.slices - f < ch.per ? ch.slices - f : ch.per;
+    Plan cp;
+    st = chunk_plan(ch, n, &cp);
+    if (st != PISA_OK) return st;
+    const char* qc = (const char*)q + f * G * N * D * p.elem;
+    const char* kc = (const char*)k + f * N * D * p.elem;
+    const char* vc = (const char*)v + f * N * D * p.elem;
+    const int32_t* selc = sel + f * N * K;
+    char* oc = (char*)o + f * G * N * D * p.elem;
+    float* lsec = o_lse ? o_lse + f * G * N : nullptr;
+    AttnWs w;
+    carve_attn(cp, ws, &w);
+    hipError_t e;
+    {
+      Stage sc(s, "regroup_attn");
+      e = pisa::launch_regroup(selc, cp.U, cp.sd.K, cp.sd.N, cp.sd.lv.n[0], (int)cp.BH, cp.sd.chunk_log2, w.counts,
+                               w.offsets, w.ranks, true, w.pairs, s);
+    }
+    if (e != hipSuccess) return hip_status(e, "regroup");
+    const int* total = w.offsets + cp.BH * cp.nch * cp.sd.lv.n[0];
+    {
+      Stage sc(s, "attn_leaf");
+      e = pisa::launch_attn_leaf(cp.sd, qc, kc, vc, selc, w.pairs, total, w.part, w.part_lse, s);
+    }
+    if (e != hipSuccess) return hip_status(e, "attn_leaf");
+    {
+      Stage sc(s, "attn_merge");
+      e = pisa::launch_attn_merge(cp.sd, selc, w.ranks, w.part, w.part_lse, oc, lsec, s);
+    }
+    if (e != hipSuccess) return hip_status(e, "attn_merge");
   }
-  if (e != hipSuccess) return hip_status(e, "regroup");
-  const int* total = w.offsets + p.BH * p.nch * p.sd.lv.n[0];
-  {
-    Stage sc(s, "attn_leaf");
-    e = pisa::launch_attn_leaf(p.sd, q, k, v, sel, w.pairs, total, w.part, w.part_lse, s);
-  }
-  if (e != hipSuccess) return hip_status(e, "attn_leaf");
-  {
-    Stage sc(s, "attn_merge");
-    e = pisa::launch_attn_merge(p.sd, sel, w.ranks, w.part, w.part_lse, o, o_lse, s);
-  }
-  return hip_status(e, "attn_merge");
+  return ok();
 }
 
 pisa_status pisa_sparse_attn_backward(const pisa_shape* shape, const void* q, const void* k, const void* v,
@@ -563,26 +668,43 @@ pisa_status pisa_sparse_attn_backward(const pisa_shape* shape, const void* q, co
   PISA_CHECK_PTR(d_q, "d_q");
   PISA_CHECK_PTR(d_k, "d_k");
   PISA_CHECK_PTR(d_v, "d_v");
-  const size_t need = carve_attn_bwd(p, nullptr, nullptr);
-  st = check_ws(need, ws, ws_bytes);
+  AttnChunks ch;
+  st = attn_chunks(shape, [](const Plan& q) { return carve_attn_bwd(q, nullptr, nullptr); }, &ch);
   if (st != PISA_OK) return st;
-  AttnBwdWs w;
-  carve_attn_bwd(p, ws, &w);
+  st = check_ws(carve_attn_bwd(ch.cp, nullptr, nullptr), ws, ws_bytes);
+  if (st != PISA_OK) return st;
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e;
-  {
-    Stage sc(s, "regroup_attn_bwd");
-    e = pisa::launch_regroup(sel, p.U, p.sd.K, p.sd.N, p.sd.lv.n[0], (int)p.BH, p.sd.chunk_log2, w.counts,
-                             w.offsets, w.ranks, true, w.pairs, s);
+  const long long G = p.sd.G, N = p.sd.N, D = p.sd.D, K = p.sd.K;
+  for (long long f = 0; f < ch.slices; f += ch.per) {
+    const long long n = ch.slices - f < ch.per ? ch.slices - f : ch.per;
+    Plan cp;
+    st = chunk_plan(ch, n, &cp);
+    if (st != PISA_OK) return st;
+    const long long qo = f * G * N * D, ko = f * N * D;  // element offsets of the chunk's first slice
+    const uint16_t* q16 = (const uint16_t*)q;
+    const uint16_t* k16 = (const uint16_t*)k;
+    const uint16_t* v16 = (const uint16_t*)v;
+    const int32_t* selc = sel + f * N * K;
+    AttnBwdWs w;
+    carve_attn_bwd(cp, ws, &w);
+    hipError_t e;
+    {
+      Stage sc(s, "regroup_attn_bwd");
+      e = pisa::launch_regroup(selc, cp.U, cp.sd.K, cp.sd.N, cp.sd.lv.n[0], (int)cp.BH, cp.sd.chunk_log2, w.counts,
+                               w.offsets, w.ranks, true, w.pairs, s);
+    }
+    if (e != hipSuccess) return hip_status(e, "regroup");
+    const int* total = w.offsets + cp.BH * cp.nch * cp.sd.lv.n[0];
+    {
+      Stage sc(s, "attn_backward");
+      e = pisa::launch_attn_backward(cp.sd, q16 + qo, k16 + ko, v16 + ko, selc, (const uint16_t*)o + qo,
+                                     o_lse + f * G * N, (const uint16_t*)d_o + qo, w.pairs, total, w.ranks, w.dsum,
+                                     w.acc, w.acc + (size_t)cp.U * cp.sd.D, w.part, (uint16_t*)d_q + qo,
+                                     (uint16_t*)d_k + ko, (uint16_t*)d_v + ko, s);
+    }
+    if (e != hipSuccess) return hip_status(e, "pisa_sparse_attn_backward");
   }
-  if (e != hipSuccess) return hip_status(e, "regroup");
-  const int* total = w.offsets + p.BH * p.nch * p.sd.lv.n[0];
-  {
-    Stage sc(s, "attn_backward");
-    e = pisa::launch_attn_backward(p.sd, q, k, v, sel, o, o_lse, d_o, w.pairs, total, w.ranks, w.dsum, w.acc,
-                                   w.acc + (size_t)p.U * p.sd.D, w.part, d_q, d_k, d_v, s);
-  }
-  return hip_status(e, "pisa_sparse_attn_backward");
+  return ok();
 }
 
 pisa_status pisa_decode_step(const pisa_shape* shape, const int32_t* host_lens, const void* q_new, const void* k_new,

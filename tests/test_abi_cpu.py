@@ -53,6 +53,7 @@ def test_workspace_sizes():
     s1 = _shape(seq_len=65536, n_q_heads=32, n_kv_heads=8, q_tile=1)
     assert 0 < P.pisa_workspace_size(s1, P.PISA_OP_SELECT) < sel  # only the hi/lo pyramid
     assert P.pisa_workspace_size(_shape(dtype="fp32", q_tile=1), P.PISA_OP_SELECT) == 0
+    # attention: the 8 (sequence, KV head) slices at 64K fit one chunk (16 GiB budget)
     assert P.pisa_workspace_size(s, P.PISA_OP_ATTN) >= U * 16 * 4 * 128 * 2
     assert P.pisa_workspace_size(s, P.PISA_OP_BSA) >= 8 * 1024 * 128 * 4
     # decode: one arrival counter per unit, then each candidate leaf's (2K per unit) per-head LSE and output
@@ -140,6 +141,22 @@ def test_host_lens_validated():
     assert lib.pisa_decode_step(ctypes.byref(s), ok, g, g, g, g, g, g, g, g, None, None, 0, None) == P.PISA_EWORKSPACE
     need = P.pisa_workspace_size(s, P.PISA_OP_DECODE)
     assert lib.pisa_decode_step(ctypes.byref(s), ok, g, g, g, g, g, g, g, g, None, g, need - 1, None) == P.PISA_EWORKSPACE
+
+
+def test_attention_workspace_is_bounded_by_the_chunk():
+    """The attention workspace holds one chunk of (sequence, KV head) slices, not the whole batch: a
+    batch of 8 sequences of 256K tokens (64 slices of 4.4 GB of partials) runs in 22 chunks of 3 slices
+    within the 16 GiB budget, not 280 GB at once."""
+    big = _shape(batch=8, seq_len=262144, n_q_heads=32, n_kv_heads=8)
+    three = _shape(batch=3, seq_len=262144, n_q_heads=4, n_kv_heads=1)
+    assert P.pisa_workspace_size(big, P.PISA_OP_ATTN) == P.pisa_workspace_size(three, P.PISA_OP_ATTN)
+    assert P.pisa_workspace_size(big, P.PISA_OP_ATTN) <= 16 << 30
+    two = _shape(batch=2, seq_len=262144, n_q_heads=4, n_kv_heads=1)
+    assert P.pisa_workspace_size(big, P.PISA_OP_ATTN_BWD) in (P.pisa_workspace_size(two, P.PISA_OP_ATTN_BWD),
+                                                            P.pisa_workspace_size(three, P.PISA_OP_ATTN_BWD))
+    small = _shape(batch=2, seq_len=1024, n_q_heads=8, n_kv_heads=2)
+    four = _shape(batch=4, seq_len=1024, n_q_heads=4, n_kv_heads=1)
+    assert P.pisa_workspace_size(small, P.PISA_OP_ATTN) == P.pisa_workspace_size(four, P.PISA_OP_ATTN)
 
 
 def test_status_strings():

@@ -96,3 +96,43 @@ def test_backward_small(name):
 def test_backward_16k():
     pf = I.make_workload("prefill_16k")
     check_backward(pf, 2, "prefill_16k")
+
+
+def test_chunked_attention_equals_one_chunk(monkeypatch):
+    """The attention and its backward cut the batch into chunks of (sequence, KV head) slices. Forced to one
+    slice per chunk (a 1 MiB budget), they give the same forward bits (O and its LSE) and the same dq bits
+    as the single-chunk run; dk and dv, summed with floating-point atomics in either run, agree to the
+    last bits of their bf16 outputs."""
+    pf = I.make_prefill(B=2, Hq=8, Hkv=2, N=1500, d=128, C=64, K=6, dtype="bf16", keys="ar1", seed=0,
+                        workload_id=710)
+    s = shape_of(pf, 4)
+    q, k, v = to_device(pf.q), to_device(pf.k), to_device(pf.v)
+    pyr = torch.empty((P.pyramid_rows(s), pf.d), dtype=torch.float32, device="cuda")
+    P.pisa_build_pyramid(s, k, pyr)
+    sel = torch.empty((pf.B, pf.Hkv, pf.N, pf.K), dtype=torch.int32, device="cuda")
+    P.pisa_select(s, q, k, pyr, sel, None, P.alloc_workspace(s, P.PISA_OP_SELECT))
+    rng = np.random.default_rng(11)
+    d_o = torch.from_numpy(I.bf16_bits(rng.standard_normal(q.shape, dtype=np.float32)).view(np.int16)).cuda()
+    d_o = d_o.view(torch.bfloat16)
+
+    def run():
+        o = torch.empty_like(q)
+        o_lse = torch.empty((pf.B, pf.Hq, pf.N), dtype=torch.float32, device="cuda")
+        P.pisa_sparse_attn(s, q, k, v, sel, o, o_lse, P.alloc_workspace(s, P.PISA_OP_ATTN))
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        P.pisa_sparse_attn_backward(s, q, k, v, sel, o, o_lse, d_o, dq, dk, dv,
+                                    P.alloc_workspace(s, P.PISA_OP_ATTN_BWD))
+        torch.cuda.synchronize()
+        return [x.float().cpu().numpy() for x in (o, o_lse, dq, dk, dv)]
+
+    one = run()
+    whole = P.pisa_workspace_size(s, P.PISA_OP_ATTN)
+    monkeypatch.setenv("PISA_ATTN_CHUNK_MIB", "1")
+    assert P.pisa_workspace_size(s, P.PISA_OP_ATTN) * 4 == pytest.approx(whole, rel=0.01)  # one of 4 slices
+    chunked = run()
+    for name, a, b in zip(("o", "o_lse", "dq"), one[:3], chunked[:3]):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), name
+    for name, a, b in zip(("dk", "dv"), one[3:], chunked[3:]):
+        assert np.abs(a - b).max() <= 2 ** -7 * max(1.0, float(np.abs(a).max())), name
+    summary(f"[attention chunking] 4 one-slice chunks equal one chunk: O, LSE and dq bit for bit, dk/dv within bf16 "
+            f"rounding (max diff {max(float(np.abs(a - b).max()) for a, b in zip(one[3:], chunked[3:])):.3g})")
