@@ -7,7 +7,7 @@
 // so that a batch of a few units still spreads over every CU (a unit's work-groups are consecutive
 // logical blocks on one XCD, sharing its L2). With p = cached length and i = p:
 //   1. walk (every work-group, redundantly; the waves share a level's M-tiles, one barrier per
-//      level, and every wave takes the same Top-K by a ballot radix select): from the top scored
+//      level, and every wave takes the same Top-K by counting ranks over LDS): from the top scored
 //      level down to level 1, each candidate's child means come straight from memory into MFMA
 //      fragments (fp32, split into bf16 hi + lo for bf16 inputs). The new token's ancestors are read
 //      as (stored sum + k_new) / tokens held, the value the step writes back at its end, so the walk
@@ -101,24 +101,6 @@ __device__ __forceinline__ float load_device(const float* a) {
   return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Top-K keep flags of candidates c < n (one per lane, ascending), keyed like topk_keep relative to
-// lane 0's score. The keys are distinct (the low bits hold the index), so the K-th largest one, T, is
-// found bit by bit from the top: a bit stays set when at least K keys are at or above the prefix with
-// it set (a ballot and a population count per bit, no LDS); the kept lanes are those with key >= T.
-__device__ __forceinline__ bool topk_keep_select(float score, int n, int K) {
-  const int lane = lane_id();
-  if (n <= K) return lane < n;
-  const float ref = topk_ref(score);
-  const uint32_t key = lane < n ? topk_key(score - ref, lane) : 0u;
-  uint32_t t = 0u;
-#pragma unroll
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t c = t | (1u << bit);
-    if (__popcll(__ballot(key >= c)) >= K) t = c;
-  }
-  return lane < n && key >= t;
-}
-
 // Sum over the 64 lanes (every lane gets it): row sums by DPP rotations, then the four rows.
 __device__ __forceinline__ float wave_sum(float v) {
   v = row_sum16(v);
@@ -142,6 +124,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_kernel(DecodeParams<
   __shared__ __align__(16) float s_sc[2][64];
   __shared__ float s_knew[D];
   __shared__ float s_w[64][17];
+  __shared__ __align__(16) uint32_t s_keys[NW][64];  // each wave's Top-K keys (rank counting)
   __shared__ int s_last;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6, r16 = lane & 15, grp = lane >> 4;
   // unit and split: a unit's S work-groups are consecutive logical blocks, which share an XCD
@@ -250,7 +233,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_kernel(DecodeParams<
       }
     }
     __syncthreads();
-    const bool keep = topk_keep_select(sc[lane < n_cand ? lane : 0], n_cand, K);
+    const bool keep = topk_keep(sc[lane < n_cand ? lane : 0], n_cand, K, s_keys[wave]);
     int cnt;
     kept = compact_lanes(keep, cn, &cnt);
     kept = lane < cnt ? kept : -1;
@@ -340,7 +323,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_kernel(DecodeParams<
 #pragma unroll
       for (int h = 0; h < kDecodeMaxG; ++h)
         if (h < p.G) sc += lh[h];
-      keep = topk_keep_select(sc, n_leaf, K);
+      keep = topk_keep(sc, n_leaf, K, s_keys[wave]);
     }
     int nsel;
     const int csel = compact_lanes(keep, lane, &nsel);
