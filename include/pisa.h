@@ -56,7 +56,7 @@ typedef enum {
 typedef enum { PISA_FP32 = 0, PISA_BF16 = 1 } pisa_dtype;
 
 /* Operation codes for pisa_workspace_size. */
-enum { PISA_OP_SELECT = 1, PISA_OP_ATTN = 2, PISA_OP_DECODE = 3, PISA_OP_BSA = 4, PISA_OP_ATTN_BWD = 5 };
+enum { PISA_OP_SELECT = 1, PISA_OP_ATTN = 2, PISA_OP_DECODE = 3, PISA_OP_BSA = 4, PISA_OP_ATTN_BWD = 5, PISA_OP_TRACE = 6 };
 
 /* Problem shape, passed by pointer to every call.
  * Limits of these kernels (PISA_EUNSUPPORTED otherwise): head_dim in {64, 128}; block C in
@@ -126,6 +126,24 @@ pisa_status pisa_select(const pisa_shape* shape, const void* q, const void* k, c
 pisa_status pisa_select_noalloc(const pisa_shape* shape, const void* q, const void* k, const float* pyr_mean,
                                 int32_t* sel, float* sel_lse, void* stream);
 size_t pisa_select_noalloc_max_bytes(void);
+
+/* The traceable selection path (explainer 亮点 5: which nodes the walk kept at every level can be read
+ * back): pisa_select's walk for a list of units, returning the kept nodes of every level, so that a
+ * unit's whole path can be inspected or checked level by level against another implementation. It
+ * runs the one-unit-per-wave walk and leaf stage of pisa_select with q_tile 1 (shape->q_tile is ignored;
+ * pisa_select gives the same selection at every q_tile), so its kept sets are pisa_select's.
+ *   units    int64 [n_units]: unit indices u = (b * Hkv + r) * N + i, in any order, repeats allowed; an
+ *            index outside [0, B * Hkv * N) gives rows of -1 (it is not an error).
+ *   trace    out int32 [n_units, n_levels, K] (n_levels from pisa_pyramid_layout): row (t, l) holds the
+ *            nodes of level l kept for unit units[t], ascending, -1 padded; a level with at most K
+ *            eligible nodes (every level above the walk's first scored one) lists all of them; row
+ *            (t, 0), the leaves, equals the unit's row of pisa_select's sel.
+ *   ws       workspace of at least pisa_workspace_size(shape, PISA_OP_TRACE) bytes (the bf16 routing
+ *            planes; none for fp32).
+ * n_units = 0 enqueues nothing (units and trace may then be NULL); n_units < 0 is PISA_EINVAL. */
+pisa_status pisa_select_trace(const pisa_shape* shape, const void* q, const void* k, const float* pyr_mean,
+                              const int64_t* units, int64_t n_units, int32_t* trace, void* ws, size_t ws_bytes,
+                              void* stream);
 
 /* pisa_sparse_attn and pisa_sparse_attn_backward process the batch in chunks of consecutive (sequence,
  * KV head) slices, the fewest whose workspace fits 16 GiB (at least one slice each), so their

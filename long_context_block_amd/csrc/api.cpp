@@ -471,10 +471,18 @@ pisa_status pisa_pyramid_layout(const pisa_shape* shape, int32_t* n_levels, int6
   return ok();
 }
 
+// The traced walk's plan: the shape at q_tile 1 (its workspace is the routing planes alone).
+static pisa_status trace_plan(const pisa_shape* shape, Plan* p) {
+  if (!shape) return fail(PISA_EINVAL, "shape: null pointer");
+  pisa_shape s1 = *shape;
+  s1.q_tile = 1;
+  return plan(&s1, p);
+}
+
 pisa_status pisa_workspace_size(const pisa_shape* shape, int32_t op, size_t* bytes) {
   if (!bytes) return fail(PISA_EINVAL, "bytes: null pointer");
   Plan p;
-  pisa_status st = plan(shape, &p);
+  pisa_status st = op == PISA_OP_TRACE ? trace_plan(shape, &p) : plan(shape, &p);
   if (st != PISA_OK) return st;
   switch (op) {
     case PISA_OP_SELECT: *bytes = carve_select(p, nullptr, nullptr); break;
@@ -486,6 +494,7 @@ pisa_status pisa_workspace_size(const pisa_shape* shape, int32_t op, size_t* byt
       break;
     }
     case PISA_OP_DECODE: *bytes = carve_decode(p, nullptr, nullptr); break;
+    case PISA_OP_TRACE: *bytes = carve_select(p, nullptr, nullptr); break;
     case PISA_OP_BSA: *bytes = carve_bsa(p, nullptr, nullptr); break;
     case PISA_OP_ATTN_BWD: {
       AttnChunks c;
@@ -597,6 +606,37 @@ pisa_status pisa_select_noalloc(const pisa_shape* shape, const void* q, const vo
 }
 
 size_t pisa_select_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+pisa_status pisa_select_trace(const pisa_shape* shape, const void* q, const void* k, const float* pyr_mean,
+                              const int64_t* units, int64_t n_units, int32_t* trace, void* ws, size_t ws_bytes,
+                              void* stream) {
+  Plan p;
+  pisa_status st = trace_plan(shape, &p);
+  if (st != PISA_OK) return st;
+  if (n_units < 0) return fail(PISA_EINVAL, "n_units must be >= 0 (got %lld)", (long long)n_units);
+  if (n_units > 4LL * 0x7fffffffLL) return fail(PISA_EINVAL, "n_units too large (%lld)", (long long)n_units);
+  if (n_units == 0) return ok();
+  PISA_CHECK_PTR(q, "q");
+  PISA_CHECK_PTR(k, "k");
+  PISA_CHECK_PTR(pyr_mean, "pyr_mean");
+  PISA_CHECK_PTR(units, "units");
+  PISA_CHECK_PTR(trace, "trace");
+  st = check_ws(carve_select(p, nullptr, nullptr), ws, ws_bytes);
+  if (st != PISA_OK) return st;
+  SelectWs w;
+  carve_select(p, ws, &w);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  const void* nodes = pyr_mean;
+  if (p.sd.bf16) {
+    e = pisa::launch_route_planes(pyr_mean, p.BH, p.sd.lv, p.sd.D, w.part_max, w.hexp, w.hilo, w.norms, s);
+    if (e != hipSuccess) return hip_status(e, "route_planes");
+    nodes = w.hilo;
+  }
+  e = pisa::launch_route_trace(p.sd, q, k, nodes, w.norms, w.hexp, (const long long*)units, (long long)n_units, trace,
+                               s);
+  return hip_status(e, "route (traced walk)");
+}
 
 pisa_status pisa_sparse_attn(const pisa_shape* shape, const void* q, const void* k, const void* v, const int32_t* sel,
                              void* o, float* o_lse, void* ws, size_t ws_bytes, void* stream) {

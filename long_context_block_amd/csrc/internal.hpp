@@ -39,6 +39,11 @@ hipError_t launch_split_hilo(const float* mean, long long rows, int D, uint16_t*
 // Selection. `nodes` is the bf16 hi/lo pyramid (bf16 inputs) or the fp32 means (fp32 inputs).
 hipError_t launch_route(const SelDims& sd, const void* q, const void* k, const void* nodes, const float* norms,
                         const int* hexp, bool fused, int* kept, int* sel, float* sel_lse, hipStream_t st);
+// The walk of launch_route (fused) for a list of units, writing every level's kept nodes to trace
+// [n_units, n_levels, K] (level 0: the selection); a unit index outside [0, U) gives rows of -1.
+hipError_t launch_route_trace(const SelDims& sd, const void* q, const void* k, const void* nodes, const float* norms,
+                              const int* hexp, const long long* units, long long n_units, int* trace,
+                              hipStream_t st);
 // Routing with 16 / G units per wave (bf16 inputs, G in {4, 8, 16}, K <= 32); same kept sets as
 // launch_route. Writes the kept level-1 nodes [U, K].
 bool route_group_supported(const SelDims& sd);

@@ -42,6 +42,10 @@ struct RouteParams {
   int* kept;      // [U, K] (tiled path)
   int* sel;       // [U, K] (fused path)
   float* sel_lse; // [B, Hq, N, K] or null (fused path)
+  // traced walk: the units to walk, and per unit and level its kept nodes [n_units, n_levels, K]
+  const long long* units;
+  long long n_units;
+  int* trace;
 };
 
 // Top-K of the leaf candidates and the outputs. Lane c < n_cand is candidate c = 2*slot + bit
@@ -74,8 +78,11 @@ __device__ __forceinline__ void leaf_topk_write(int n_cand, int leaf_c, int G, i
   leaf_topk_write_sc(n_cand, leaf_c, sc, G, K, u, qrow0, qstride, ell, sel, sel_lse, keys);
 }
 
-template <typename T, int D, int C, bool FUSED, int KM>
+// TRACE (with FUSED): the units come from p.units, and every level's kept nodes, the leaves' included,
+// go to p.trace instead of sel; the arithmetic is the same.
+template <typename T, int D, int C, bool FUSED, int KM, bool TRACE = false>
 __global__ __launch_bounds__(256, FUSED ? 2 : 4) void route_kernel(RouteParams<T> p) {
+  static_assert(!TRACE || FUSED, "the traced walk includes the leaf stage");
   constexpr int kLog2C = C == 64 ? 6 : 5;
   __shared__ float s_ell[FUSED ? 4 : 1][64][17];
   __shared__ __align__(16) float s_sc[4][64];
@@ -85,8 +92,19 @@ __global__ __launch_bounds__(256, FUSED ? 2 : 4) void route_kernel(RouteParams<T
   const int lb = xcd_logical_block(gridDim.x);
   const long long first = ((long long)lb * 4 + wave) * p.upw;
   for (int it = 0; it < p.upw; ++it) {
-    const long long u = first + it;
-    if (u >= U) break;
+    long long u = first + it;
+    long long trow = 0;  // TRACE: this unit's first trace row (level 0)
+    if constexpr (TRACE) {
+      if (u >= p.n_units) break;
+      trow = u * p.lv.n_levels;
+      u = p.units[u];
+      if (u < 0 || u >= U) {  // not a unit of this shape: every level reads -1
+        for (int x = lane; x < p.lv.n_levels * p.K; x += 64) p.trace[trow * p.K + x] = -1;
+        continue;
+      }
+    } else {
+      if (u >= U) break;
+    }
     const long long bh = u / p.N;
     const long long i = u % p.N;
     const int b = (int)(bh / p.Hkv), r = (int)(bh % p.Hkv);
@@ -103,6 +121,11 @@ __global__ __launch_bounds__(256, FUSED ? 2 : 4) void route_kernel(RouteParams<T
     }
     int kept;
     int nk;
+    auto trace_hook = [&](int l, int kept_l, int nk_l) {
+      if constexpr (TRACE) {
+        if (lane < p.K) p.trace[(trow + l) * p.K + lane] = lane < nk_l ? kept_l : -1;
+      }
+    };
     if constexpr (sizeof(T) == 2) {
       RoutePlanes<D> rows;
       rows.base = (const uint16_t*)p.nodes + bh * p.lv.rnodes * 2 * D;
@@ -121,17 +144,23 @@ __global__ __launch_bounds__(256, FUSED ? 2 : 4) void route_kernel(RouteParams<T
       Frag<uint16_t> qh[D / 32];
       const int te = route_q_f16<D>(qf, qh);
       const float col_scale = ldexpf(p.scale, -(te + p.hexp[bh]));
-      nk = walk_to_level1<T, D, KM>(p.lv, kLog2C, p.K, (int)i, &kept, [&](int lc, int cn, int n_cand, int e_child) {
-        return select_level_refine<D, KM>(rows, norms, (int)p.lv.roff[lc], qh, qn, cn, n_cand, e_child, p.G, p.scale,
-                                          col_scale, p.K, s_sc[wave], s_key[wave]);
-      });
+      nk = walk_to_level1<T, D, KM>(
+          p.lv, kLog2C, p.K, (int)i, &kept,
+          [&](int lc, int cn, int n_cand, int e_child) {
+            return select_level_refine<D, KM>(rows, norms, (int)p.lv.roff[lc], qh, qn, cn, n_cand, e_child, p.G,
+                                              p.scale, col_scale, p.K, s_sc[wave], s_key[wave]);
+          },
+          trace_hook);
     } else {
       NodeRows<T, D> rows;
       rows.base = (const float*)p.nodes + bh * p.lv.nodes * D;
-      nk = walk_to_level1<T, D, KM>(p.lv, kLog2C, p.K, (int)i, &kept, [&](int lc, int cn, int n_cand, int e_child) {
-        score_candidates<T, D, KM>(rows, (int)p.lv.off[lc], qf, cn, n_cand, e_child, p.G, p.scale, s_sc[wave]);
-        return topk_keep_lds(s_sc[wave], n_cand, p.K, s_key[wave]);
-      });
+      nk = walk_to_level1<T, D, KM>(
+          p.lv, kLog2C, p.K, (int)i, &kept,
+          [&](int lc, int cn, int n_cand, int e_child) {
+            score_candidates<T, D, KM>(rows, (int)p.lv.off[lc], qf, cn, n_cand, e_child, p.G, p.scale, s_sc[wave]);
+            return topk_keep_lds(s_sc[wave], n_cand, p.K, s_key[wave]);
+          },
+          trace_hook);
     }
     if constexpr (!FUSED) {
       if (lane < p.K) p.kept[u * p.K + lane] = lane < nk ? kept : -1;
@@ -159,8 +188,9 @@ __global__ __launch_bounds__(256, FUSED ? 2 : 4) void route_kernel(RouteParams<T
         __threadfence_block();
       }
       leaf_topk_write(
-          n_cand, leaf_c, p.G, p.K, u, qrow0, p.N, [&](int c, int h) { return s_ell[FUSED ? wave : 0][c][h]; }, p.sel,
-          p.sel_lse, s_key[wave]);
+          n_cand, leaf_c, p.G, p.K, TRACE ? trow : u, qrow0, p.N,
+          [&](int c, int h) { return s_ell[FUSED ? wave : 0][c][h]; }, TRACE ? p.trace : p.sel,
+          TRACE ? nullptr : p.sel_lse, s_key[wave]);
       __threadfence_block();
     }
   }
@@ -737,6 +767,9 @@ static hipError_t route_t(const SelDims& sd, const void* q, const void* k, const
   p.kept = kept;
   p.sel = sel;
   p.sel_lse = sel_lse;
+  p.units = nullptr;
+  p.n_units = 0;
+  p.trace = nullptr;
   const long long U = (long long)sd.B * sd.Hkv * sd.N;
   if constexpr (sizeof(T) == 2 && !FUSED) {
     // LDS-resident upper levels: the smallest level whose rows up to the root fit in kRouteLdsBytes
@@ -781,6 +814,60 @@ static hipError_t route_dc(const SelDims& sd, const void* q, const void* k, cons
   }
   if (sd.C == 64) return route_t<T, 64, 64, FUSED>(sd, q, k, nodes, norms, hexp, kept, sel, sel_lse, st);
   return route_t<T, 64, 32, FUSED>(sd, q, k, nodes, norms, hexp, kept, sel, sel_lse, st);
+}
+
+// The traced walk: one wave per listed unit, route_kernel's fused walk and leaf stage.
+template <typename T, int D, int C>
+static hipError_t route_trace_t(const SelDims& sd, const void* q, const void* k, const void* nodes,
+                                const float* norms, const int* hexp, const long long* units, long long n_units,
+                                int* trace, hipStream_t st) {
+  RouteParams<T> p;
+  p.hexp = hexp;
+  p.q = (const T*)q;
+  p.k = (const T*)k;
+  p.nodes = nodes;
+  p.norms = norms;
+  p.B = sd.B;
+  p.Hq = sd.Hq;
+  p.Hkv = sd.Hkv;
+  p.G = sd.G;
+  p.N = sd.N;
+  p.K = sd.K;
+  p.scale = sd.scale;
+  p.lv = sd.lv;
+  p.kept = nullptr;
+  p.sel = nullptr;
+  p.sel_lse = nullptr;
+  p.units = units;
+  p.n_units = n_units;
+  p.trace = trace;
+  p.upw = 1;
+  const long long blocks = (n_units + 3) / 4;
+  if (sd.K <= 16)
+    hipLaunchKernelGGL((route_kernel<T, D, C, true, 4, true>), dim3((unsigned)blocks), dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL((route_kernel<T, D, C, true, 8, true>), dim3((unsigned)blocks), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t route_trace_dc(const SelDims& sd, const void* q, const void* k, const void* nodes,
+                                 const float* norms, const int* hexp, const long long* units, long long n_units,
+                                 int* trace, hipStream_t st) {
+  if (sd.D == 128) {
+    if (sd.C == 64) return route_trace_t<T, 128, 64>(sd, q, k, nodes, norms, hexp, units, n_units, trace, st);
+    return route_trace_t<T, 128, 32>(sd, q, k, nodes, norms, hexp, units, n_units, trace, st);
+  }
+  if (sd.C == 64) return route_trace_t<T, 64, 64>(sd, q, k, nodes, norms, hexp, units, n_units, trace, st);
+  return route_trace_t<T, 64, 32>(sd, q, k, nodes, norms, hexp, units, n_units, trace, st);
+}
+
+hipError_t launch_route_trace(const SelDims& sd, const void* q, const void* k, const void* nodes, const float* norms,
+                              const int* hexp, const long long* units, long long n_units, int* trace,
+                              hipStream_t st) {
+  if (n_units == 0) return hipSuccess;
+  if (sd.bf16) return route_trace_dc<uint16_t>(sd, q, k, nodes, norms, hexp, units, n_units, trace, st);
+  return route_trace_dc<float>(sd, q, k, nodes, norms, hexp, units, n_units, trace, st);
 }
 
 hipError_t launch_route(const SelDims& sd, const void* q, const void* k, const void* nodes, const float* norms,

@@ -376,8 +376,11 @@ __device__ bool select_level_refine(const Rows& rows, const float* norms, int le
 // with more than K. level_select(child level, candidate node, n_cand, eligible children) scores one
 // level. Returns the number of kept level-1 nodes; lane c < n holds the c-th (ascending).
 // A pyramid of one leaf has the virtual level-1 node 0.
-template <typename T, int D, int KM, class LevelSelect>
-__device__ int walk_to_level1(const Levels& lv, int log2c, int K, int i, int* kept_out, LevelSelect&& level_select) {
+// level_hook(l, kept, nk), if given, sees every level l >= 1 once, from the top: lane c < nk holds
+// the c-th kept node of level l (ascending); where a level has at most K eligible nodes, all of them.
+template <typename T, int D, int KM, class LevelSelect, class LevelHook>
+__device__ int walk_to_level1(const Levels& lv, int log2c, int K, int i, int* kept_out, LevelSelect&& level_select,
+                              LevelHook&& level_hook) {
   const int lane = lane_id();
   const int L = lv.n_levels - 1;
   int lstar = 0;
@@ -386,6 +389,10 @@ __device__ int walk_to_level1(const Levels& lv, int log2c, int K, int i, int* ke
       lstar = l;
       break;
     }
+  }
+  for (int l = L; l > lstar; --l) {  // levels with at most K eligible nodes keep them all
+    const int n_l = (i >> (log2c + l)) + 1;
+    level_hook(l, lane < n_l ? lane : -1, n_l);
   }
   int nk, kept;
   if (lstar == 0) {
@@ -404,6 +411,7 @@ __device__ int walk_to_level1(const Levels& lv, int log2c, int K, int i, int* ke
     if (n_cand <= K) {
       kept = lane < n_cand ? cn : -1;
       nk = n_cand;
+      level_hook(l, kept, nk);
       continue;
     }
     const bool keep = level_select(l - 1, cn, n_cand, (i >> (log2c + l - 1)) + 1);
@@ -411,9 +419,15 @@ __device__ int walk_to_level1(const Levels& lv, int log2c, int K, int i, int* ke
     const int nxt = compact_lanes(keep, cn, &cnt);
     kept = lane < cnt ? nxt : -1;
     nk = cnt;
+    level_hook(l, kept, nk);
   }
   *kept_out = kept;
   return nk;
+}
+
+template <typename T, int D, int KM, class LevelSelect>
+__device__ int walk_to_level1(const Levels& lv, int log2c, int K, int i, int* kept_out, LevelSelect&& level_select) {
+  return walk_to_level1<T, D, KM>(lv, log2c, K, i, kept_out, level_select, [](int, int, int) {});
 }
 
 // Key tile of leaves 2p and 2p+1: rows = tokens t0 .. t0+2C-1 of one KV head. Rows past N repeat token

@@ -16,13 +16,13 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpisa.so"
 
 PISA_OK, PISA_EINVAL, PISA_EUNSUPPORTED, PISA_EWORKSPACE, PISA_EHIP = 0, -1, -2, -3, -4
 PISA_FP32, PISA_BF16 = 0, 1
-PISA_OP_SELECT, PISA_OP_ATTN, PISA_OP_DECODE, PISA_OP_BSA, PISA_OP_ATTN_BWD = 1, 2, 3, 4, 5
+PISA_OP_SELECT, PISA_OP_ATTN, PISA_OP_DECODE, PISA_OP_BSA, PISA_OP_ATTN_BWD, PISA_OP_TRACE = 1, 2, 3, 4, 5, 6
 
 EXPORTED = ["pisa_pyramid_layout", "pisa_workspace_size", "pisa_build_pyramid", "pisa_select", "pisa_sparse_attn",
             "pisa_decode_step", "bsa_select", "pisa_status_string", "pisa_last_error", "pisa_stage_timing",
             "pisa_stage_times", "pisa_select_noalloc", "pisa_select_noalloc_max_bytes", "pisa_flat_leaf_lse",
             "pisa_selection_quality", "pisa_build_pyramid_pooled", "pisa_select_variant",
-            "pisa_sparse_attn_backward"]
+            "pisa_sparse_attn_backward", "pisa_select_trace"]
 
 
 class Shape(ctypes.Structure):
@@ -82,6 +82,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "pisa_build_pyramid_pooled": [_SP, _P, i32, _P, _P, _P],
         "pisa_select_variant": [_SP, ctypes.POINTER(Variant), _P, _P, _P, _P, _P, _P],
         "pisa_sparse_attn_backward": [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, sz, _P],
+        "pisa_select_trace": [_SP, _P, _P, _P, _P, i64, _P, _P, sz, _P],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -156,6 +157,14 @@ def pisa_select(shape, q, k, pyr_mean, sel, sel_lse=None, ws=None, stream=None):
     nbytes = ws.numel() * ws.element_size() if ws is not None else 0
     _check(load().pisa_select(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(pyr_mean), _ptr(sel), _ptr(sel_lse),
                               _ptr(ws), nbytes, _stream(stream)), "pisa_select")
+
+
+def pisa_select_trace(shape, q, k, pyr_mean, units, trace, ws=None, stream=None):
+    """units: int64 [n] unit indices; trace: int32 [n, n_levels, K] (level 0 = the selection)."""
+    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
+    n = units.numel() if units is not None else 0
+    _check(load().pisa_select_trace(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(pyr_mean), _ptr(units), n,
+                                    _ptr(trace), _ptr(ws), nbytes, _stream(stream)), "pisa_select_trace")
 
 
 def pisa_select_noalloc(shape, q, k, pyr_mean, sel, sel_lse=None, stream=None):

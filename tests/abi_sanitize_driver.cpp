@@ -193,6 +193,20 @@ int main() {
     v = pisa_variant{9, PISA_BUDGET_FIXED, -1};
     expect(pisa_select_variant(&s, &v, g, g, gf, gf, gi, nullptr) == PISA_EINVAL, "variant unknown score");
     expect(pisa_select_variant(&s, nullptr, g, g, gf, gf, gi, nullptr) == PISA_EINVAL, "variant null options");
+    const int64_t* gu = static_cast<const int64_t*>(g);
+    size_t tneed = 0, sneed = 0;
+    pisa_shape s1 = shape(1, 1024, 4, 1, 128, 64, 16, 1);
+    expect(pisa_workspace_size(&s, PISA_OP_TRACE, &tneed) == PISA_OK &&
+               pisa_workspace_size(&s1, PISA_OP_SELECT, &sneed) == PISA_OK && tneed == sneed && tneed > 0,
+           "trace workspace is the q_tile 1 select workspace");
+    expect(pisa_select_trace(&s, g, g, gf, gu, -1, gi, g, big, nullptr) == PISA_EINVAL, "trace negative count");
+    expect(pisa_select_trace(&s, nullptr, nullptr, nullptr, nullptr, 0, nullptr, nullptr, 0, nullptr) == PISA_OK,
+           "trace of no units");
+    expect(pisa_select_trace(&s, g, g, gf, nullptr, 4, gi, g, big, nullptr) == PISA_EINVAL, "trace null units");
+    expect(pisa_select_trace(&s, g, g, gf, gu, 4, nullptr, g, big, nullptr) == PISA_EINVAL, "trace null output");
+    expect(pisa_select_trace(&s, g, g, gf, gu, 4, gi, g, tneed - 1, nullptr) == PISA_EWORKSPACE,
+           "trace short workspace");
+    expect(pisa_select_trace(nullptr, g, g, gf, gu, 4, gi, g, big, nullptr) == PISA_EINVAL, "trace null shape");
   }
 
   // ---- status strings, last error, stage timing

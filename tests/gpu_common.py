@@ -322,6 +322,113 @@ def compare(pf: I.Prefill, g: GpuOut, units, oc: OracleCache | None = None, chec
     return rep
 
 
+def check_path(pf: I.Prefill, oc: "OracleCache", b: int, r: int, i: int, rows: np.ndarray, tol: float = MARGIN,
+               ref=None):
+    """One unit's traced selection path (rows: int [n_levels, K], row l = the nodes kept at level l)
+    checked level by level, from the top, against the oracle's float64 scores of the path's own
+    candidates: the candidates of level l are the eligible children of the nodes kept at level l + 1
+    (every eligible node at the top level); if there are at most K, all of them must be kept; else
+    exactly K of them, such that every kept candidate scores at least as high as every dropped one up to
+    tol. This validates an undecided unit's whole path, not just its final selection.
+    Returns (problems, same, gap): problems lists the violated levels, same is True if every level equals
+    the oracle's own walk (ref: its UnitSelection, computed if not given), gap is the smallest
+    (lowest kept - highest dropped) over the scored levels."""
+    k, _, pyr = oc.head(b, r)
+    qg = oc.q(b, r, i)
+    C, g, K, L = pf.C, 2, pf.K, pyr.root_level
+    problems = []
+    gap = math.inf
+    if rows.shape[0] != L + 1:
+        return [f"{rows.shape[0]} trace levels for a pyramid of {L + 1}"], False, gap
+    got = {l: [int(x) for x in rows[l] if x >= 0] for l in range(L + 1)}
+    for l in range(L + 1):
+        pad = rows[l][len(got[l]):]
+        if (pad != -1).any() or got[l] != sorted(set(got[l])):
+            problems.append(f"level {l}: not an ascending, left-packed, -1 padded list: {rows[l].tolist()}")
+    if problems:
+        return problems, False, gap
+    for l in range(L, -1, -1):
+        if l == L:
+            cand = [j for j in range(pyr.means[L].shape[0]) if O.eligible(L, j, i, C, g)]
+        else:
+            cand = sorted(c for p in got[l + 1] for c in O.children(l + 1, p, pyr) if O.eligible(l, c, i, C, g))
+        if len(cand) <= K:
+            if got[l] != cand:
+                problems.append(f"level {l}: {len(cand)} candidates must all be kept, got {got[l]}")
+            continue
+        if len(got[l]) != K or not set(got[l]) <= set(cand):
+            problems.append(f"level {l}: kept {got[l]} is not K of the candidates {cand}")
+            continue
+        if l == 0:
+            score = {j: float(O.leaf_lse_per_head(qg, k, j, i, C, pf.scale, pf.N).sum()) for j in cand}
+        else:
+            score = {j: float(O.node_lse_per_head(qg, pyr, l, j, i, pf.scale).sum()) for j in cand}
+        low_kept = min(score[j] for j in got[l])
+        high_dropped = max(score[j] for j in cand if j not in set(got[l]))
+        gap = min(gap, low_kept - high_dropped)
+        if low_kept < high_dropped - tol:
+            problems.append(f"level {l}: kept score {low_kept:.6g} below dropped {high_dropped:.6g} - {tol}")
+    ref = ref if ref is not None else O.select_unit(qg, k, pyr, i, K, pf.scale)
+    same = all(got[l] == list(ref.kept[l]) for l in range(L + 1) if l in ref.kept)
+    return problems, same, gap
+
+
+@dataclasses.dataclass
+class PathReport:
+    n_units: int = 0
+    n_same: int = 0  # paths equal to the oracle's walk at every level
+    n_decided: int = 0
+    decided_differ: list = dataclasses.field(default_factory=list)  # decided units whose path differs
+    invalid: list = dataclasses.field(default_factory=list)  # paths that fail check_path
+    min_gap: float = math.inf
+
+    def merge(self, o: "PathReport"):
+        self.n_units += o.n_units
+        self.n_same += o.n_same
+        self.n_decided += o.n_decided
+        self.decided_differ += o.decided_differ[:20]
+        self.invalid += o.invalid[:20]
+        self.min_gap = min(self.min_gap, o.min_gap)
+
+
+def _path_chunk(task) -> PathReport:
+    pf, oc, trace = _CTX["pf"], _CTX["oc"], _CTX["trace"]
+    rep = PathReport()
+    for t, (b, r, i) in task:
+        k, _, pyr = oc.head(b, r)
+        ref = O.select_unit(oc.q(b, r, i), k, pyr, i, pf.K, pf.scale)
+        problems, same, gap = check_path(pf, oc, b, r, i, trace[t], ref=ref)
+        margin = ref.margin
+        rep.n_units += 1
+        rep.n_same += int(same)
+        rep.min_gap = min(rep.min_gap, gap)
+        if problems:
+            rep.invalid.append((b, r, i, problems))
+        if margin >= MARGIN:
+            rep.n_decided += 1
+            if not same:
+                rep.decided_differ.append((b, r, i, margin))
+    return rep
+
+
+def compare_paths(pf: I.Prefill, trace: np.ndarray, units, oc: "OracleCache | None" = None, chunk=64) -> PathReport:
+    """check_path over every traced unit (trace[t] is the path of units[t] = (b, r, i)) in the worker pool."""
+    oc = oc or OracleCache(pf)
+    for (b, r) in sorted({(b, r) for (b, r, _) in units}):
+        oc.head(b, r)
+    items = list(enumerate(units))
+    tasks = [items[x:x + chunk] for x in range(0, len(items), chunk)]
+    _CTX.update(pf=pf, oc=oc, trace=trace)
+    try:
+        reps = pool_map(_path_chunk, tasks)
+    finally:
+        _CTX.clear()
+    rep = PathReport()
+    for r_ in reps:
+        rep.merge(r_)
+    return rep
+
+
 def assert_report(rep: Report, dtype: str, check_attn=True, min_decided=0.9, label=""):
     msg = (f"{label} units={rep.n_units} decided={rep.n_decided} ({rep.decided_frac:.4f}, floor {min_decided}) "
            f"undecided_equal={rep.n_undecided_equal} sel_mismatch={len(rep.sel_mismatch)} "

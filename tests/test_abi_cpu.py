@@ -188,3 +188,28 @@ def test_backward_rejects_fp32_before_any_hip_call():
     assert need > 0
     assert lib.pisa_sparse_attn_backward(ctypes.byref(_shape()), fake, fake, fake, fake, fake, fake, fake, fake, fake,
                                          fake, fake, need - 1, None) == P.PISA_EWORKSPACE
+
+
+def test_trace_arguments_validated_before_any_hip_call():
+    lib = P.load()
+    s = _shape()
+    g = ctypes.c_void_p(1 << 20)
+    big = 1 << 40
+    # the traced walk's workspace is the routing planes alone: pisa_select's at q_tile 1
+    need = P.pisa_workspace_size(s, P.PISA_OP_TRACE)
+    assert need == P.pisa_workspace_size(_shape(q_tile=1), P.PISA_OP_SELECT) > 0
+    assert P.pisa_workspace_size(_shape(dtype="fp32"), P.PISA_OP_TRACE) == 0
+    # q_tile is ignored, also where q_tile * G would be refused by pisa_select
+    assert P.pisa_workspace_size(_shape(q_tile=8), P.PISA_OP_TRACE) == need
+    assert lib.pisa_select_trace(ctypes.byref(s), g, g, g, g, -1, g, g, big, None) == P.PISA_EINVAL
+    assert b"n_units" in lib.pisa_last_error()
+    assert lib.pisa_select_trace(ctypes.byref(s), None, None, None, None, 0, None, None, 0, None) == P.PISA_OK
+    assert lib.pisa_select_trace(ctypes.byref(s), g, g, g, None, 4, g, g, big, None) == P.PISA_EINVAL
+    assert b"units" in lib.pisa_last_error()
+    assert lib.pisa_select_trace(ctypes.byref(s), g, g, g, g, 4, None, g, big, None) == P.PISA_EINVAL
+    assert b"trace" in lib.pisa_last_error()
+    assert lib.pisa_select_trace(ctypes.byref(s), None, g, g, g, 4, g, g, big, None) == P.PISA_EINVAL
+    assert lib.pisa_select_trace(ctypes.byref(s), g, g, g, g, 4, g, g, need - 1, None) == P.PISA_EWORKSPACE
+    assert lib.pisa_select_trace(None, g, g, g, g, 4, g, g, big, None) == P.PISA_EINVAL
+    assert lib.pisa_select_trace(ctypes.byref(_shape(head_dim=96)), g, g, g, g, 4, g, g, big, None) == \
+        P.PISA_EUNSUPPORTED

@@ -1,0 +1,91 @@
+"""The traceable selection path on the GPU (pisa_select_trace, explainer 亮点 5).
+
+For every traced unit: the leaf row equals pisa_select's selection bit for bit (at q_tile 1 and at the
+largest q_tile), the whole path passes check_path against the oracle's float64 scores level by level
+(undecided units included, which the final-selection parity can only check by invariants), and the
+path of every decided unit equals the oracle's walk at every level. A unit index outside the shape gives
+rows of -1."""
+import numpy as np
+import pytest
+import torch
+
+from long_context_block_amd import inputs as I
+from long_context_block_amd import pisa as P
+
+from gpu_common import (DEV, OracleCache, compare_paths, say, shape_of, summary, to_device, units_all,
+                        units_stratified)
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    "fp32_gqa_ragged": dict(B=2, Hq=4, Hkv=2, N=700, d=64, C=32, K=5, dtype="fp32", keys="ar1"),
+    "tiny_fp32_k_n1": dict(B=1, Hq=1, Hkv=1, N=1024, d=64, C=32, K=16, dtype="fp32", keys="iid"),
+    "bf16_batch2": dict(B=2, Hq=8, Hkv=2, N=1100, d=128, C=64, K=5, dtype="bf16", keys="ar1"),
+    "bf16_d64_c32": dict(B=1, Hq=4, Hkv=2, N=777, d=64, C=32, K=6, dtype="bf16", keys="ar1"),
+    "single_leaf": dict(B=1, Hq=4, Hkv=1, N=40, d=128, C=64, K=4, dtype="bf16", keys="ar1"),
+    "bf16_k32_gqa8": dict(B=1, Hq=16, Hkv=2, N=3000, d=128, C=32, K=32, dtype="bf16", keys="ar1"),
+}
+
+
+def _run(pf, units, q_tile):
+    """pisa_select at q_tile (sel [B, Hkv, N, K]) and the traced walk of `units` ([T, n_levels, K])."""
+    s = shape_of(pf, q_tile)
+    q, k = to_device(pf.q), to_device(pf.k)
+    pyr = torch.empty((P.pyramid_rows(s), pf.d), dtype=torch.float32, device=DEV)
+    P.pisa_build_pyramid(s, k, pyr)
+    sel = torch.empty((pf.B, pf.Hkv, pf.N, pf.K), dtype=torch.int32, device=DEV)
+    ws = P.alloc_workspace(s, P.PISA_OP_SELECT)
+    P.pisa_select(s, q, k, pyr, sel, None, ws)
+    del ws
+    n_levels = P.pisa_pyramid_layout(s)[0]
+    u = torch.tensor(units, dtype=torch.int64, device=DEV)
+    trace = torch.full((len(units), n_levels, pf.K), -7, dtype=torch.int32, device=DEV)
+    wt = P.alloc_workspace(s, P.PISA_OP_TRACE)
+    P.pisa_select_trace(s, q, k, pyr, u, trace, wt)
+    torch.cuda.synchronize()
+    out = sel.cpu().numpy(), trace.cpu().numpy()
+    del q, k, pyr, sel, u, trace, wt
+    torch.cuda.empty_cache()
+    return out
+
+
+def _flat(pf, units):
+    return [(b * pf.Hkv + r) * pf.N + i for (b, r, i) in units]
+
+
+def _check(pf, units, q_tile, label, min_same):
+    U = pf.B * pf.Hkv * pf.N
+    idx = _flat(pf, units) + [-5, U, U + 3]  # three indices outside the shape
+    sel, trace = _run(pf, idx, q_tile)
+    assert (trace[-3:] == -1).all(), "an index outside the shape must give rows of -1"
+    trace = trace[:-3]
+    assert (trace != -7).all(), "every row of every traced unit is written"
+    leaf = np.stack([sel[b, r, i] for (b, r, i) in units])
+    assert np.array_equal(trace[:, 0, :], leaf), "the traced leaf level differs from pisa_select's sel"
+    rep = compare_paths(pf, trace, units, OracleCache(pf))
+    msg = (f"[trace {label}] q_tile {q_tile}: {rep.n_units} units, paths valid {rep.n_units - len(rep.invalid)}, "
+           f"equal to the oracle's walk at every level {rep.n_same}, decided {rep.n_decided} "
+           f"(all equal: {not rep.decided_differ}), undecided {rep.n_units - rep.n_decided} validated level by "
+           f"level, smallest kept-dropped gap {rep.min_gap:.3g}")
+    summary(msg)
+    assert not rep.invalid, rep.invalid[:3]
+    assert not rep.decided_differ, rep.decided_differ[:5]
+    assert rep.n_same >= min_same * rep.n_units, msg
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_trace_small_all_units(name):
+    spec = SMALL[name]
+    say(f"[trace small] {name} {spec}")
+    pf = I.make_prefill(seed=0, workload_id=100, **spec)
+    qt = max(t for t in (1, 2, 4, 8, 16) if t * pf.G <= 16)
+    _check(pf, units_all(pf), qt, name, min_same=0.9)
+
+
+@pytest.mark.timeout(900)
+def test_trace_64k_sample():
+    say("[trace 64k] generating prefill_64k")
+    pf = I.make_workload("prefill_64k")
+    units = units_stratified(pf, 0.005, seed=11)
+    say(f"[trace 64k] {len(units)} units")
+    _check(pf, units, 4, "prefill_64k", min_same=0.8)
