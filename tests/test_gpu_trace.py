@@ -89,3 +89,12 @@ def test_trace_64k_sample():
     units = units_stratified(pf, 0.005, seed=11)
     say(f"[trace 64k] {len(units)} units")
     _check(pf, units, 4, "prefill_64k", min_same=0.8)
+
+
+@pytest.mark.timeout(900)
+def test_trace_256k_needles_sample():
+    say("[trace 256k] generating prefill_256k_needles")
+    pf = I.make_workload("prefill_256k_needles")
+    units = units_stratified(pf, 0.001, seed=13)
+    say(f"[trace 256k] {len(units)} units")
+    _check(pf, units, 4, "prefill_256k_needles", min_same=0.6)
