@@ -27,9 +27,23 @@ __device__ __forceinline__ int attn_vt_row(int d) {
   return 16 * mt + 4 * grp + j;
 }
 
+// 16 bytes at p; NT: a non-temporal load, for data read once per kernel (a streamed cache tile), so
+// that it does not displace data that is read again.
+template <bool NT>
+__device__ __forceinline__ uint4 load16(const uint16_t* p) {
+  if constexpr (NT) {
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(x.x, x.y, x.z, x.w);
+  } else {
+    return *reinterpret_cast<const uint4*>(p);
+  }
+}
+
 // K tile of the leaf starting at token t0, rows permuted (attn_token). Rows past N repeat row N - 1:
-// those tokens are later than every query, so the causal mask drops them before any use.
-template <typename T, int D, int C>
+// those tokens are later than every query, so the causal mask drops them before any use. NT (bf16):
+// non-temporal loads.
+template <typename T, int D, int C, bool NT = false>
 __device__ __forceinline__ void load_attn_k(const T* kbh, long long t0, long long N, Frag<T> (&kf)[C / 16][D / 32]) {
   const int r16 = lane_id() & 15, grp = lane_id() >> 4;
 #pragma unroll
@@ -37,14 +51,19 @@ __device__ __forceinline__ void load_attn_k(const T* kbh, long long t0, long lon
     long long t = t0 + attn_token(m, r16 >> 2, r16 & 3);
     t = t < N ? t : N - 1;
 #pragma unroll
-    for (int s = 0; s < D / 32; ++s) kf[m][s].load(kbh + t * D + 32 * s + 8 * grp);
+    for (int s = 0; s < D / 32; ++s) {
+      if constexpr (sizeof(T) == 2)
+        kf[m][s].u = load16<NT>(reinterpret_cast<const uint16_t*>(kbh) + t * D + 32 * s + 8 * grp);
+      else
+        kf[m][s].load(kbh + t * D + 32 * s + 8 * grp);
+    }
   }
 }
 
 // Stage the bf16 V tile of the leaf at t0 transposed into vt, this wave's [D][C + 8] LDS scratch:
 // dimension d goes to row attn_vt_row(d). Tokens past N repeat token N - 1 (their probabilities are
 // exactly zero). Each lane writes (token 2tp, token 2tp + 1) pairs as 32-bit words.
-template <int D, int C>
+template <int D, int C, bool NT = false>
 __device__ __forceinline__ void stage_attn_vt(const uint16_t* vbh, long long t0, long long N, uint16_t (*vt)[C + 8]) {
   const int lane = lane_id();
   constexpr int CHR = D / 8;               // 8-element chunks per V row
@@ -58,8 +77,8 @@ __device__ __forceinline__ void stage_attn_vt(const uint16_t* vbh, long long t0,
     long long ta = t0 + 2 * tp, tb = ta + 1;
     ta = ta < N ? ta : N - 1;
     tb = tb < N ? tb : N - 1;
-    f0[it] = *reinterpret_cast<const uint4*>(vbh + ta * D + c0);
-    f1[it] = *reinterpret_cast<const uint4*>(vbh + tb * D + c0);
+    f0[it] = load16<NT>(vbh + ta * D + c0);
+    f1[it] = load16<NT>(vbh + tb * D + c0);
   }
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
@@ -86,14 +105,15 @@ __device__ __forceinline__ Frag<uint16_t> vt_frag(const uint16_t (*vt)[C + 8], i
   return f;
 }
 
-// All V^T fragments in registers (bf16 staged through vt; fp32 loaded directly).
-template <typename T, int D, int C>
+// All V^T fragments in registers (bf16 staged through vt, with non-temporal loads if NT; fp32 loaded
+// directly).
+template <typename T, int D, int C, bool NT = false>
 __device__ __forceinline__ void load_attn_vt(const T* vbh, long long t0, long long N, uint16_t (*vt)[C + 8],
                                              Frag<T> (&vf)[D / 16][C / 32]) {
   constexpr int MO = D / 16, KS = C / 32;
   const int lane = lane_id(), r16 = lane & 15, grp = lane >> 4;
   if constexpr (sizeof(T) == 2) {
-    stage_attn_vt<D, C>((const uint16_t*)vbh, t0, N, vt);
+    stage_attn_vt<D, C, NT>((const uint16_t*)vbh, t0, N, vt);
 #pragma unroll
     for (int mt = 0; mt < MO; ++mt)
 #pragma unroll

@@ -260,9 +260,11 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_kernel(DecodeParams<
     }
     const long long t0 = (long long)leaf * C;
     Frag<T> kf[C / 16][D / 32];
-    load_attn_k<T, D, C>(kbh, t0, len, kf);
+    // the step reads each candidate leaf's K and V once: non-temporal loads, so that they pass through
+    // the caches without displacing the pyramid rows the next step's walk reads
+    load_attn_k<T, D, C, true>(kbh, t0, len, kf);
     Frag<T> vf[D / 16][C / 32];
-    load_attn_vt<T, D, C>(vbh, t0, len, vt, vf);
+    load_attn_vt<T, D, C, true>(vbh, t0, len, vt, vf);
     f32x4 oacc[MO];
     float lse, inv;
     attend_tile<T, D, C>(kf, vf, qf, t0, hv ? i : -1, p.scale, oacc, lse, inv);
