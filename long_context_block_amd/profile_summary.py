@@ -8,12 +8,16 @@ Reads the files rocprofv3 writes with ``--output-format csv`` (``*_kernel_stats.
   counter reads for a plain device copy of known size (``bench.py --copy-calibration BYTES``), as
   Markdown plus a JSON file that ``bench.py`` reads. The JSON records a digest of the kernel sources;
   ``bench.py`` ignores it once the sources have changed.
+* SQ and texture counters per launch from two ``--pmc`` passes (instruction counts, VALU, MFMA and
+  texture-address busy fractions, LDS bank conflicts), as Markdown.
 
 Usage (from the repository root, on the host, after the GPU runs)::
 
     python -m long_context_block_amd.profile_summary stats DIR --title T --command C --out profiles/x.md
     python -m long_context_block_amd.profile_summary traffic --fetch DIR --write DIR --copy-fetch DIR \\
         --copy-write DIR --copy-bytes N --title T --command C --out-md profiles/y.md --out-json profiles/y.json
+    python -m long_context_block_amd.profile_summary counters --pass-a DIR --pass-b DIR --title T \\
+        --command C --out profiles/z.md
 """
 from __future__ import annotations
 
@@ -169,6 +173,67 @@ def cmd_traffic(a):
     print(f"wrote {a.out_md} and {a.out_json}")
 
 
+# counters of the two passes (pass a: the SQ_WAVES row carries the launch's timestamps)
+COUNTER_COLUMNS = ["SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_BUSY_CU_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA",
+                   "SQ_ACTIVE_INST_VALU", "SQ_INSTS_VALU_TRANS_F32", "SQ_LDS_BANK_CONFLICT",
+                   "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_LDS", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "TA_BUSY_avr",
+                   "TD_TD_BUSY_avr"]
+
+
+def counter_means(dirs: list[str]) -> tuple[dict, dict]:
+    """Per kernel short name: the mean over its launches of every counter (summed over the counter's
+    instances within a launch), and the mean launch duration in us (from the SQ_WAVES rows)."""
+    per = defaultdict(lambda: defaultdict(lambda: defaultdict(float)))
+    dur = defaultdict(dict)
+    for d in dirs:
+        with open(_one(os.path.join(d, "**", "*counter_collection.csv"))) as f:
+            for r in csv.DictReader(f):
+                k = short_name(r["Kernel_Name"])
+                per[k][r["Counter_Name"]][(d, r["Dispatch_Id"])] += float(r["Counter_Value"])
+                if r["Counter_Name"] == "SQ_WAVES":
+                    dur[k][r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    means = {k: {c: sum(v.values()) / len(v) for c, v in cs.items()} for k, cs in per.items()}
+    durs = {k: sum(v.values()) / len(v) for k, v in dur.items() if v}
+    return means, durs
+
+
+def cmd_counters(a):
+    means, durs = counter_means([a.pass_a, a.pass_b])
+    lines = [f"# SQ and texture counters per launch: {a.title}", "",
+             "Commands (run from the repository root on one MI355X; each pass is one bench step, and the "
+             "launches of the step are averaged per kernel):", "", "```", a.command, "```", "",
+             "Derived columns, read this way: *CU cycles* = SQ_BUSY_CU_CYCLES / 256 (cycles each CU was busy); "
+             "*VALU busy* = 4 · SQ_ACTIVE_INST_VALU / (1024 SIMDs · CU cycles), with SQ_ACTIVE_INST_VALU counted "
+             "in 4-cycle units (a wave64 VALU instruction issues over 4 cycles on a 16-lane SIMD; the counter "
+             "tracks SQ_INSTS_VALU one to one); *MFMA busy* = SQ_VALU_MFMA_BUSY_CYCLES / (1024 · CU cycles); "
+             "*TA busy* = TA_BUSY_avr / CU cycles; *LDS conflict* = SQ_LDS_BANK_CONFLICT / (256 · CU cycles). "
+             "The fractions are relative to the cycles the CUs were busy, so for short launches with a ragged "
+             "tail (finalize) they overstate the steady state. The launch time here is under the profiler and "
+             "is slightly longer than in the timed bench.", "",
+             "| Kernel | Launch (us) | VALU instr. (M) | of which MFMA (M) | transcendental (M) | VALU busy | "
+             "MFMA busy | TA busy | LDS conflict |", "|---|---|---|---|---|---|---|---|---|"]
+    order = sorted(means, key=lambda k: -durs.get(k, 0.0))
+    for k in order:
+        m = means[k]
+        cu = m.get("SQ_BUSY_CU_CYCLES", 0.0) / 256
+        if cu <= 0:
+            continue
+        g = lambda c: m.get(c, 0.0)
+        lines.append(f"| `{k}` | {durs.get(k, 0.0):.0f} | {g('SQ_INSTS_VALU') / 1e6:.0f} | "
+                     f"{g('SQ_INSTS_MFMA') / 1e6:.1f} | {g('SQ_INSTS_VALU_TRANS_F32') / 1e6:.1f} | "
+                     f"{4 * g('SQ_ACTIVE_INST_VALU') / (1024 * cu):.0%} | "
+                     f"{g('SQ_VALU_MFMA_BUSY_CYCLES') / (1024 * cu):.0%} | {g('TA_BUSY_avr') / cu:.0%} | "
+                     f"{g('SQ_LDS_BANK_CONFLICT') / (256 * cu):.0%} |")
+    cols = [c for c in COUNTER_COLUMNS if any(c in m for m in means.values())]
+    lines += ["", "Raw averages per launch:", "", "| Kernel | " + " | ".join(cols) + " |",
+              "|---|" + "---|" * len(cols)]
+    for k in order:
+        lines.append(f"| `{k}` | " + " | ".join(f"{means[k].get(c, 0.0):.4g}" for c in cols) + " |")
+    with open(a.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(f"wrote {a.out}")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -188,8 +253,14 @@ def main():
     t.add_argument("--command", required=True)
     t.add_argument("--out-md", required=True)
     t.add_argument("--out-json", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("--pass-a", dest="pass_a", required=True)
+    c.add_argument("--pass-b", dest="pass_b", required=True)
+    c.add_argument("--title", required=True)
+    c.add_argument("--command", required=True)
+    c.add_argument("--out", required=True)
     a = ap.parse_args()
-    {"stats": cmd_stats, "traffic": cmd_traffic}[a.cmd](a)
+    {"stats": cmd_stats, "traffic": cmd_traffic, "counters": cmd_counters}[a.cmd](a)
 
 
 if __name__ == "__main__":
