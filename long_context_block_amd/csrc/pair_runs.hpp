@@ -7,10 +7,11 @@
 namespace pisa {
 
 // kTask pairs per task, 256 threads. key(pair) is the pair's bucket key; runs are maximal ranges of
-// equal keys. Returns the number of runs r; s_run[0..r] holds their starts and s_run[r] = n.
-template <int kTask, typename KeyFn>
+// equal keys. Returns the number of runs r; s_run[0..r] holds their starts and s_run[r] = n (RunT: any
+// integer type that holds kTask).
+template <int kTask, typename KeyFn, typename RunT>
 __device__ __forceinline__ int stage_pair_runs(const uint32_t* __restrict__ pairs, long long base, int n, KeyFn key,
-                                               uint32_t* s_pair, long long* s_key, int* s_run, int* s_wcount) {
+                                               uint32_t* s_pair, long long* s_key, RunT* s_run, int* s_wcount) {
   static_assert(kTask % 256 == 0, "task size");
   constexpr int J = kTask / 256;  // 64-entry chunks per wave
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;

@@ -391,15 +391,17 @@ __global__ __launch_bounds__(256) void leaf_lse_kernel(LeafParams<T> p) {
 // for each run (one KV head and level-1 node) the 256 threads stage the node's two leaves (2C keys)
 // into LDS, then the four waves take the run's tiles of q_tile units x G heads round-robin, reading
 // every K fragment from LDS. The per-column arithmetic (fragment values, MFMA order, LSE code) is the
-// unit-major leaf stage's, so both give the same bits.
-constexpr int kLeafWgTask = 1024;
+// unit-major leaf stage's, so both give the same bits. Four work-groups share a CU (at most 128
+// registers per lane and 40 KiB of LDS each: 512-pair tasks, 16-bit run offsets), so that many waves
+// cover the query gathers' latency, each with one register set of queries in flight.
+constexpr int kLeafWgTask = 512;
 
 template <int D, int C>
-__global__ __launch_bounds__(256, 3) void leaf_lse_wg_kernel(LeafParams<uint16_t> p) {
+__global__ __launch_bounds__(256, 4) void leaf_lse_wg_kernel(LeafParams<uint16_t> p) {
   __shared__ __align__(16) uint16_t s_k[2 * C][D];
   __shared__ uint32_t s_pair[kLeafWgTask];
   __shared__ long long s_key[kLeafWgTask];
-  __shared__ int s_run[kLeafWgTask + 1];
+  __shared__ uint16_t s_run[kLeafWgTask + 1];
   __shared__ int s_wcount[4];
   const int lane = lane_id(), wave = threadIdx.x >> 6, r16 = lane & 15, grp = lane >> 4;
   const long long total = *p.total;
@@ -464,21 +466,15 @@ __global__ __launch_bounds__(256, 3) void leaf_lse_wg_kernel(LeafParams<uint16_t
       dst[p.G] = out.l1;
     };
     if (wave < ntiles) {
-      // two register sets in turn: this wave's tiles t and t + 4 run while the queries of t + 8 and
-      // t + 12 are in flight
-      Frag<uint16_t> qa[D / 32], qb[D / 32];
-      uint32_t pa, pb;
+      // the queries of this wave's next tile (t + 4) are requested as soon as tile t has read its own
+      Frag<uint16_t> qa[D / 32];
+      uint32_t pa;
       fetch(wave, qa, pa);
-      fetch(wave + 4, qb, pb);
       opaque_frags(qa);
-      opaque_frags(qb);
-      for (int t = wave; t < ntiles; t += 8) {
+      for (int t = wave; t < ntiles; t += 4) {
         Out out;
         score(qa, pa, out);
-        fetch(t + 8, qa, pa);
-        store(out);
-        score(qb, pb, out);
-        fetch(t + 12, qb, pb);
+        fetch(t + 4, qa, pa);
         store(out);
       }
     }
