@@ -60,7 +60,8 @@ enum { PISA_OP_SELECT = 1, PISA_OP_ATTN = 2, PISA_OP_DECODE = 3, PISA_OP_BSA = 4
 
 /* Problem shape, passed by pointer to every call.
  * Limits of these kernels (PISA_EUNSUPPORTED otherwise): head_dim in {64, 128}; block C in
- * {32, 64}; 1 <= top_k <= 32; branch (merge factor g) == 2; G = Hq/Hkv in {1, 2, 4, 8, 16};
+ * {32, 64}; 1 <= top_k <= 32; branch (merge factor g) == 2; causal == 1 (the walk's eligibility and
+ * every score take the tokens t <= i of position i only); G = Hq/Hkv in {1, 2, 4, 8, 16};
  * q_tile in {1, 2, 4, 8, 16} with q_tile*G <= 16 (q_tile > 1 groups q_tile units that share a
  * candidate block into one matrix tile; q_tile == 1 walks each unit to its leaves directly);
  * units B*Hkv*seq_len < 2^27. */
@@ -73,6 +74,7 @@ typedef struct {
   int32_t block;      /* C: tokens per leaf block                                          */
   int32_t top_k;      /* K: nodes kept per level                                           */
   int32_t branch;     /* g: merge factor of the pyramid                                    */
+  int32_t causal;     /* 1: position i sees tokens t <= i (the only mode)                   */
   int32_t q_tile;     /* units per matrix tile in the leaf stage (see above)               */
   float scale;        /* score scale s; 0 means 1/sqrt(d)                                  */
   int32_t dtype;      /* pisa_dtype of Q, K, V, O                                          */

@@ -144,6 +144,7 @@ pisa_status plan(const pisa_shape* s, Plan* pl) {
   if (s->top_k < 1) return fail(PISA_EINVAL, "top_k must be >= 1");
   if (s->top_k > 32) return fail(PISA_EUNSUPPORTED, "top_k must be <= 32");
   if (s->branch != 2) return fail(PISA_EUNSUPPORTED, "branch (merge factor) must be 2");
+  if (s->causal != 1) return fail(PISA_EUNSUPPORTED, "causal must be 1 (the selection and attention are causal)");
   const int qt = s->q_tile;
   if (qt != 1 && qt != 2 && qt != 4 && qt != 8 && qt != 16) return fail(PISA_EINVAL, "q_tile must be 1, 2, 4, 8 or 16");
   if (qt * G > 16) return fail(PISA_EUNSUPPORTED, "q_tile * G must be <= 16");
@@ -363,6 +364,7 @@ pisa_status chunk_plan(const AttnChunks& c, long long n, Plan* p) {
   sub.block = c.cp.sd.C;
   sub.top_k = c.cp.sd.K;
   sub.branch = 2;
+  sub.causal = 1;
   sub.q_tile = c.cp.sd.q_tile;
   sub.scale = c.cp.sd.scale;
   sub.dtype = c.cp.sd.bf16 ? PISA_BF16 : PISA_FP32;

@@ -28,14 +28,15 @@ EXPORTED = ["pisa_pyramid_layout", "pisa_workspace_size", "pisa_build_pyramid", 
 class Shape(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("seq_len", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
                 ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("block", ctypes.c_int32),
-                ("top_k", ctypes.c_int32), ("branch", ctypes.c_int32), ("q_tile", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("branch", ctypes.c_int32), ("causal", ctypes.c_int32),
+                ("q_tile", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("dtype", ctypes.c_int32)]
 
 
 def make_shape(*, batch, seq_len, n_q_heads, n_kv_heads, head_dim, block, top_k, branch=2, q_tile=1, scale=0.0,
-               dtype="bf16") -> Shape:
+               dtype="bf16", causal=1) -> Shape:
     dt = {"bf16": PISA_BF16, "fp32": PISA_FP32}.get(dtype, dtype)
-    return Shape(batch, seq_len, n_q_heads, n_kv_heads, head_dim, block, top_k, branch, q_tile, scale, dt)
+    return Shape(batch, seq_len, n_q_heads, n_kv_heads, head_dim, block, top_k, branch, causal, q_tile, scale, dt)
 
 
 PISA_POOL_MEAN, PISA_POOL_SUM, PISA_POOL_MAX = 0, 1, 2

@@ -33,6 +33,7 @@ static pisa_shape shape(int batch = 1, int seq_len = 1024, int hq = 4, int hkv =
   s.block = c;
   s.top_k = k;
   s.branch = 2;
+  s.causal = 1;
   s.q_tile = q_tile;
   s.scale = 0.f;
   s.dtype = dtype;
@@ -105,6 +106,13 @@ int main() {
       {shape(64, 1 << 17, 64, 16), PISA_EUNSUPPORTED},
   };
   bad[0].s.branch = 2;
+  {
+    pisa_shape nc = shape();
+    nc.causal = 0;
+    size_t b = 0;
+    expect(pisa_workspace_size(&nc, PISA_OP_SELECT, &b) == PISA_EUNSUPPORTED, "non-causal shape");
+    expect(pisa_select(&nc, g, g, gf, gi, nullptr, g, big, nullptr) == PISA_EUNSUPPORTED, "non-causal select");
+  }
   for (const Bad& x : bad) {
     size_t b = 0;
     expect(pisa_workspace_size(&x.s, PISA_OP_SELECT, &b) == x.st, "bad shape: workspace_size");

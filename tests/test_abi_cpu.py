@@ -73,6 +73,7 @@ BAD_SHAPES = [
     (dict(block=16), P.PISA_EUNSUPPORTED),
     (dict(top_k=0), P.PISA_EINVAL),
     (dict(top_k=33), P.PISA_EUNSUPPORTED),
+    (dict(causal=0), P.PISA_EUNSUPPORTED),  # the method is causal
     (dict(branch=3), P.PISA_EUNSUPPORTED),
     (dict(q_tile=3), P.PISA_EINVAL),
     (dict(q_tile=8), P.PISA_EUNSUPPORTED),  # 8 * G(4) > 16
