@@ -23,7 +23,9 @@
 
 namespace pisa {
 
-constexpr int kWgTaskBwd = 1024;  // sorted pairs per work-group task
+constexpr int kWgTaskBwd = 1024;  // sorted pairs per work-group task (dq)
+// dkdv: 512-pair tasks, so that two work-groups (77 KiB of LDS each) share a CU
+constexpr int kWgTaskDkdv = 512;
 
 struct BwdParams {
   const uint16_t* q;
@@ -197,7 +199,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
 constexpr int kBwdCols = 32;  // columns per tile pair
 
 template <int D, int C>
-__global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(BwdParams p) {
   constexpr int MO = D / 16;
   constexpr int NSL = C / 16;  // token slices of 16
   __shared__ __align__(16) uint16_t s_k[C][D];
@@ -208,17 +210,17 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   __shared__ __align__(16) uint16_t s_dot[D][kBwdCols + 8];
   __shared__ float s_lse[kBwdCols], s_dsum[kBwdCols];
   __shared__ long long s_pos[kBwdCols];
-  __shared__ uint32_t s_pair[kWgTaskBwd];
-  __shared__ long long s_key[kWgTaskBwd];
-  __shared__ int s_run[kWgTaskBwd + 1];
+  __shared__ uint32_t s_pair[kWgTaskDkdv];
+  __shared__ long long s_key[kWgTaskDkdv];
+  __shared__ uint16_t s_run[kWgTaskDkdv + 1];
   __shared__ int s_wcount[4];
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6, r16 = lane & 15, grp = lane >> 4;
   const long long total = *p.total;
-  const long long base = (long long)xcd_logical_block(gridDim.x) * kWgTaskBwd;
+  const long long base = (long long)xcd_logical_block(gridDim.x) * kWgTaskDkdv;
   if (base >= total) return;
-  const int n = (int)(total - base < kWgTaskBwd ? total - base : kWgTaskBwd);
+  const int n = (int)(total - base < kWgTaskDkdv ? total - base : kWgTaskDkdv);
   const long long nch = ((long long)p.N + (1LL << p.chunk_log2) - 1) >> p.chunk_log2;
-  const int nrun = stage_pair_runs<kWgTaskBwd>(
+  const int nrun = stage_pair_runs<kWgTaskDkdv>(
       p.pairs, base, n,
       [&](uint32_t pr) {
         const long long u = pr >> 5;
@@ -260,18 +262,48 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
     const long long hrow = (long long)bi * p.Hq + (long long)ri * p.G;
     const long long ubase = bh * p.N;
     const int npairs = (b - a + units_per_pair - 1) / units_per_pair;
-    for (int tp = 0; tp < npairs; ++tp) {
-      // stage the tile pair's 32 columns: column c = (unit a + tp * 32 / G + c / G, head c % G); a column
-      // past the run has position -1 (every score masked) and zero rows
-      for (int x = tid; x < kBwdCols * CHR; x += 256) {
+    // A tile pair's 32 columns: column c = (unit a + tp * 32 / G + c / G, head c % G); a column past the
+    // run has position -1 (every score masked) and zero rows. Its q and dO rows, LSE and D are fetched
+    // into registers one tile pair ahead, so that the gathers are in flight while the previous tile pair
+    // computes; each thread holds chunks x = tid + 256 it.
+    constexpr int SIT = (kBwdCols * CHR + 255) / 256;
+    uint4 fq[SIT], fo[SIT];
+    long long fpos = -1;
+    float fl = 0.f, fds = 0.f;
+    auto fetch = [&](int tp) {
+#pragma unroll
+      for (int it = 0; it < SIT; ++it) {
+        const int x = tid + 256 * it;
         const int c = x / CHR, ch = x % CHR;
         const int xu = a + tp * units_per_pair + c / p.G;
-        uint4 qv = make_uint4(0u, 0u, 0u, 0u), ov = qv;
-        if (xu < b) {
+        fq[it] = fo[it] = make_uint4(0u, 0u, 0u, 0u);
+        if (x < kBwdCols * CHR && xu < b) {
           const long long row = (hrow + c % p.G) * p.N + ((long long)(s_pair[xu] >> 5) - ubase);
-          qv = *reinterpret_cast<const uint4*>(p.q + row * D + 8 * ch);
-          ov = *reinterpret_cast<const uint4*>(p.d_o + row * D + 8 * ch);
+          fq[it] = *reinterpret_cast<const uint4*>(p.q + row * D + 8 * ch);
+          fo[it] = *reinterpret_cast<const uint4*>(p.d_o + row * D + 8 * ch);
         }
+      }
+      if (tid < kBwdCols) {
+        const int xu = a + tp * units_per_pair + tid / p.G;
+        fpos = -1;
+        fl = fds = 0.f;
+        if (xu < b) {
+          fpos = (long long)(s_pair[xu] >> 5) - ubase;
+          const long long row = (hrow + tid % p.G) * p.N + fpos;
+          fl = p.o_lse[row];
+          fds = p.dsum[row];
+        }
+      }
+    };
+    fetch(0);
+    for (int tp = 0; tp < npairs; ++tp) {
+      // stage the fetched tile pair (rows, and their transposes for the dV / dK products)
+#pragma unroll
+      for (int it = 0; it < SIT; ++it) {
+        const int x = tid + 256 * it;
+        if (x >= kBwdCols * CHR) continue;
+        const int c = x / CHR, ch = x % CHR;
+        const uint4 qv = fq[it], ov = fo[it];
         *reinterpret_cast<uint4*>(&s_q[c][8 * (ch ^ kswz<D>(c))]) = qv;
         *reinterpret_cast<uint4*>(&s_do[c][8 * (ch ^ kswz<D>(c))]) = ov;
         const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w}, ow[4] = {ov.x, ov.y, ov.z, ov.w};
@@ -283,21 +315,12 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
         }
       }
       if (tid < kBwdCols) {
-        const int c = tid;
-        const int xu = a + tp * units_per_pair + c / p.G;
-        long long pos = -1;
-        float l = 0.f, ds = 0.f;
-        if (xu < b) {
-          pos = (long long)(s_pair[xu] >> 5) - ubase;
-          const long long row = (hrow + c % p.G) * p.N + pos;
-          l = p.o_lse[row];
-          ds = p.dsum[row];
-        }
-        s_pos[c] = pos;
-        s_lse[c] = l * kLog2e;
-        s_dsum[c] = ds;
+        s_pos[tid] = fpos;
+        s_lse[tid] = fl * kLog2e;
+        s_dsum[tid] = fds;
       }
       __syncthreads();
+      if (tp + 1 < npairs) fetch(tp + 1);
       if (tp % nphase == phase) {
         // S^T and dP^T: rows = the 32 columns (permuted so that lane group g ends up with columns
         // 8 g .. 8 g + 7), columns = this wave's 16 tokens
@@ -412,7 +435,8 @@ static hipError_t bwd_t(const SelDims& sd, const BwdParams& p0, const int* pos, 
   const long long max_pairs = (long long)sd.B * sd.Hkv * sd.N * sd.K;
   const long long wg = (max_pairs + kWgTaskBwd - 1) / kWgTaskBwd;
   hipLaunchKernelGGL((attn_bwd_dq_kernel<D, C>), dim3((unsigned)wg), dim3(256), 0, st, p);
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, C>), dim3((unsigned)wg), dim3(256), 0, st, p);
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, C>), dim3((unsigned)((max_pairs + kWgTaskDkdv - 1) / kWgTaskDkdv)),
+                     dim3(256), 0, st, p);
   const long long mt = rows * (D / 8);
   hipLaunchKernelGGL((bwd_dq_merge_kernel<D>), dim3((unsigned)((mt + 255) / 256)), dim3(256), 0, st, p.sel, pos,
                      p.part, sd.B, sd.Hq, sd.Hkv, sd.G, sd.N, sd.K, sd.scale, (uint16_t*)d_q);
