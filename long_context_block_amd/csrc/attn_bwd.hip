@@ -198,6 +198,18 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
 // ------------------------------------------------------------------------------------------ dkdv pass
 constexpr int kBwdCols = 32;  // columns per tile pair
 
+// The transposed column tiles (row = dimension, 32 columns): 16-byte chunk k of row r is stored at chunk
+// k ^ ((r >> 5) & 3), so that the staging writes of one wave, which span dimensions 32 apart, fall on
+// different banks. colt_frag reads the B-operand fragment of rows 16 mt .. 16 mt + 15 (k = the columns).
+__device__ __forceinline__ int colt_chunk(int row, int k) { return k ^ ((row >> 5) & 3); }
+__device__ __forceinline__ Frag<uint16_t> colt_frag(const uint16_t (*t)[kBwdCols + 8], int mt) {
+  const int r16 = lane_id() & 15, grp = lane_id() >> 4;
+  const int row = 16 * mt + r16;
+  Frag<uint16_t> f;
+  f.u = *reinterpret_cast<const uint4*>(&t[row][8 * colt_chunk(row, grp)]);
+  return f;
+}
+
 template <int D, int C>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(BwdParams p) {
   constexpr int MO = D / 16;
@@ -265,22 +277,28 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(BwdParams p) {
     // A tile pair's 32 columns: column c = (unit a + tp * 32 / G + c / G, head c % G); a column past the
     // run has position -1 (every score masked) and zero rows. Its q and dO rows, LSE and D are fetched
     // into registers one tile pair ahead, so that the gathers are in flight while the previous tile pair
-    // computes; each thread holds chunks x = tid + 256 it.
-    constexpr int SIT = (kBwdCols * CHR + 255) / 256;
-    uint4 fq[SIT], fo[SIT];
+    // computes. A thread takes chunk ch of the rows of the column pair (2 cp, 2 cp + 1), item
+    // x = tid + 256 it, so that it writes the transposed tiles as 32-bit column pairs.
+    constexpr int CP = kBwdCols / 2;
+    constexpr int SIT = (CP * CHR + 255) / 256;
+    uint4 fq[SIT][2], fo[SIT][2];
     long long fpos = -1;
     float fl = 0.f, fds = 0.f;
     auto fetch = [&](int tp) {
 #pragma unroll
       for (int it = 0; it < SIT; ++it) {
         const int x = tid + 256 * it;
-        const int c = x / CHR, ch = x % CHR;
-        const int xu = a + tp * units_per_pair + c / p.G;
-        fq[it] = fo[it] = make_uint4(0u, 0u, 0u, 0u);
-        if (x < kBwdCols * CHR && xu < b) {
-          const long long row = (hrow + c % p.G) * p.N + ((long long)(s_pair[xu] >> 5) - ubase);
-          fq[it] = *reinterpret_cast<const uint4*>(p.q + row * D + 8 * ch);
-          fo[it] = *reinterpret_cast<const uint4*>(p.d_o + row * D + 8 * ch);
+        const int cp = x / CHR, ch = x % CHR;
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          const int c = 2 * cp + k2;
+          const int xu = a + tp * units_per_pair + c / p.G;
+          fq[it][k2] = fo[it][k2] = make_uint4(0u, 0u, 0u, 0u);
+          if (x < CP * CHR && xu < b) {
+            const long long row = (hrow + c % p.G) * p.N + ((long long)(s_pair[xu] >> 5) - ubase);
+            fq[it][k2] = *reinterpret_cast<const uint4*>(p.q + row * D + 8 * ch);
+            fo[it][k2] = *reinterpret_cast<const uint4*>(p.d_o + row * D + 8 * ch);
+          }
         }
       }
       if (tid < kBwdCols) {
@@ -297,21 +315,30 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(BwdParams p) {
     };
     fetch(0);
     for (int tp = 0; tp < npairs; ++tp) {
-      // stage the fetched tile pair (rows, and their transposes for the dV / dK products)
+      // stage the fetched tile pair: rows (swizzled), and the transposes for the dV / dK products
 #pragma unroll
       for (int it = 0; it < SIT; ++it) {
         const int x = tid + 256 * it;
-        if (x >= kBwdCols * CHR) continue;
-        const int c = x / CHR, ch = x % CHR;
-        const uint4 qv = fq[it], ov = fo[it];
-        *reinterpret_cast<uint4*>(&s_q[c][8 * (ch ^ kswz<D>(c))]) = qv;
-        *reinterpret_cast<uint4*>(&s_do[c][8 * (ch ^ kswz<D>(c))]) = ov;
-        const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w}, ow[4] = {ov.x, ov.y, ov.z, ov.w};
+        if (x >= CP * CHR) continue;
+        const int cp = x / CHR, ch = x % CHR;
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          const int c = 2 * cp + k2;
+          *reinterpret_cast<uint4*>(&s_q[c][8 * (ch ^ kswz<D>(c))]) = fq[it][k2];
+          *reinterpret_cast<uint4*>(&s_do[c][8 * (ch ^ kswz<D>(c))]) = fo[it][k2];
+        }
+        const uint32_t q0[4] = {fq[it][0].x, fq[it][0].y, fq[it][0].z, fq[it][0].w};
+        const uint32_t q1[4] = {fq[it][1].x, fq[it][1].y, fq[it][1].z, fq[it][1].w};
+        const uint32_t o0[4] = {fo[it][0].x, fo[it][0].y, fo[it][0].z, fo[it][0].w};
+        const uint32_t o1[4] = {fo[it][1].x, fo[it][1].y, fo[it][1].z, fo[it][1].w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
+          // element e of both columns: the low half from column 2 cp, the high half from 2 cp + 1
+          const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
           const int dr = attn_vt_row<D>(8 * ch + e);
-          s_qt[dr][c] = (uint16_t)((e & 1) ? (qw[e >> 1] >> 16) : (qw[e >> 1] & 0xffffu));
-          s_dot[dr][c] = (uint16_t)((e & 1) ? (ow[e >> 1] >> 16) : (ow[e >> 1] & 0xffffu));
+          const int col = 8 * colt_chunk(dr, cp >> 2) + 2 * (cp & 3);
+          *reinterpret_cast<uint32_t*>(&s_qt[dr][col]) = __builtin_amdgcn_perm(q1[e >> 1], q0[e >> 1], sel);
+          *reinterpret_cast<uint32_t*>(&s_dot[dr][col]) = __builtin_amdgcn_perm(o1[e >> 1], o0[e >> 1], sel);
         }
       }
       if (tid < kBwdCols) {
@@ -352,8 +379,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(BwdParams p) {
                           pack_bf16x2(dv[6], dv[7]));
 #pragma unroll
         for (int mt = 0; mt < MO; ++mt) {
-          mma(dva[mt], vt_frag<kBwdCols>(s_dot, mt, 0), pf);
-          mma(dka[mt], vt_frag<kBwdCols>(s_qt, mt, 0), df);
+          mma(dva[mt], colt_frag(s_dot, mt), pf);
+          mma(dka[mt], colt_frag(s_qt, mt), df);
         }
       }
       __syncthreads();  // the tile pair is consumed before the next one is staged
