@@ -418,15 +418,35 @@ __global__ __launch_bounds__(256) void bwd_dq_merge_kernel(const int* __restrict
   if (task >= U * G) return;
   const long long u = task / G;
   const int h = (int)(task % G);
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < K; ++s) {
-    if (sel[u * K + s] < 0) break;  // selections are left-packed
-    const uint4 x = *reinterpret_cast<const uint4*>(part + ((long long)pos[u * K + s] * G + h) * D + 8 * li);
-    const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
+  // the unit's slots first (selections are left-packed: nsel leading entries), then its partial rows
+  // eight at a time, so that many loads are in flight; the sum runs over the slots in order
+  constexpr int KMAX = 32;
+  int at[KMAX];
+  int nsel = 0;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc[2 * e] += __uint_as_float(xs[e] << 16);
-      acc[2 * e + 1] += __uint_as_float(xs[e] & 0xffff0000u);
+  for (int s = 0; s < KMAX; ++s) {
+    const bool in = s < K && sel[u * K + s] >= 0;
+    at[s] = in ? pos[u * K + s] : 0;
+    nsel += in ? 1 : 0;
+  }
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s0 = 0; s0 < KMAX; s0 += 8) {
+    if (s0 >= nsel) break;
+    uint4 x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (s0 + j < nsel) x[j] = *reinterpret_cast<const uint4*>(part + ((long long)at[s0 + j] * G + h) * D + 8 * li);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (s0 + j < nsel) {
+        const uint32_t xs[4] = {x[j].x, x[j].y, x[j].z, x[j].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] += __uint_as_float(xs[e] << 16);
+          acc[2 * e + 1] += __uint_as_float(xs[e] & 0xffff0000u);
+        }
+      }
     }
   }
   const long long bh = u / N, i = u % N;
