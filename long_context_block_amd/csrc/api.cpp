@@ -63,20 +63,24 @@ struct Stage {
   hipStream_t s;
   const char* name;
   hipEvent_t a = nullptr;
+  // an event that cannot be recorded drops this stage's interval (the timer is advisory)
   Stage(hipStream_t st, const char* n) : s(st), name(n) {
     if (g_timer.on) {
       a = g_timer.get();
-      if (a) hipEventRecord(a, s);
+      if (a && hipEventRecord(a, s) != hipSuccess) {
+        g_timer.pool.push_back(a);
+        a = nullptr;
+      }
     }
   }
   ~Stage() {
     if (a) {
       hipEvent_t b = g_timer.get();
-      if (b) {
-        hipEventRecord(b, s);
+      if (b && hipEventRecord(b, s) == hipSuccess) {
         g_timer.pending.push_back({name, a, b});
       } else {
         g_timer.pool.push_back(a);
+        if (b) g_timer.pool.push_back(b);
       }
     }
   }
@@ -956,7 +960,7 @@ pisa_status pisa_stage_timing(int32_t enable) {
   g_timer.on = enable != 0;
   if (!enable) {
     for (auto& e : g_timer.pending) {
-      hipEventSynchronize(e.b);
+      (void)hipEventSynchronize(e.b);  // only so that the events can be reused; their times are dropped
       g_timer.pool.push_back(e.a);
       g_timer.pool.push_back(e.b);
     }
