@@ -195,21 +195,6 @@ struct NodeRows<float, D> {
 // nodes below e_child are eligible (first token <= i); since the candidates are the children of an
 // ascending kept list, only the last candidate can miss its second child. KM = M-tiles for 2K
 // candidates (2 rows each). The scores land in s_sc[c] (LDS).
-// Child rows staged in LDS in MFMA-row order (row 2c + bit = child bit of candidate c): bf16 hi/lo
-// planes, or fp32 rows. `index` maps (level offset, child node, MFMA row) to the row to read.
-template <typename T, int D>
-struct StagedRows;
-
-template <int D>
-struct StagedRows<uint16_t, D> : NodeRows<uint16_t, D> {
-  __device__ __forceinline__ int index(int, int, int local_row) const { return local_row; }
-};
-
-template <int D>
-struct StagedRows<float, D> : NodeRows<float, D> {
-  __device__ __forceinline__ int index(int, int, int local_row) const { return local_row; }
-};
-
 template <typename T, int D, int KM, class Rows = NodeRows<T, D>>
 __device__ void score_candidates(const Rows& rows, int level_off, const Frag<T> (&qf)[D / 32], int cn,
                                  int n_cand, int e_child, int G, float scale, float* s_sc) {
@@ -252,27 +237,6 @@ __device__ void score_candidates(const Rows& rows, int level_off, const Frag<T> 
     }
   }
   __threadfence_block();
-}
-
-// One M-tile (candidates 8 m .. 8 m + 7) of score_candidates over rows already staged in MFMA-row
-// order (local row 16 m + r = child r & 1 of candidate 8 m + r / 2): the same per-candidate arithmetic,
-// so a level's M-tiles can be scored by different waves. n_full = candidates with two eligible children.
-template <typename T, int D>
-__device__ __forceinline__ void score_staged_mtile(const StagedRows<T, D>& rows, const Frag<T> (&qf)[D / 32], int m,
-                                                   int n_full, int G, float scale, float* s_sc) {
-  const int r16 = lane_id() & 15, grp = lane_id() >> 4;
-  typename NodeRows<T, D>::Row f;
-  rows.load(f, 16 * m + r16, grp);
-  f32x4 acc = zero4();
-  rows.dot(acc, f, qf);
-#pragma unroll
-  for (int a = 0; a < 2; ++a) {
-    const int c = 8 * m + 2 * grp + a;
-    const float x0 = scale * acc[2 * a], x1 = scale * acc[2 * a + 1];
-    float l = c < n_full ? lse2(x0, x1) : x0;
-    l = row_sum16(r16 < G ? l : 0.f);
-    if (r16 == 0) s_sc[c] = l;
-  }
 }
 
 // One scored level for bf16 inputs, in two passes over the <= 4K child rows of the fp16 routing planes
