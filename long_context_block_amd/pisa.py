@@ -65,8 +65,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     if _lib is not None:
         return _lib
     if not os.path.exists(path):
-        raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build() "
-                           "(python -m long_context_block_amd.build)")
+        raise RuntimeError(f"{path} is missing: build it with python -m long_context_block_amd.build")
     lib = ctypes.CDLL(path)
     i32, i64, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     sig = {
