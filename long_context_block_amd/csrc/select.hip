@@ -393,11 +393,14 @@ __global__ __launch_bounds__(256) void leaf_lse_kernel(LeafParams<T> p) {
 // every K fragment from LDS. The per-column arithmetic (fragment values, MFMA order, LSE code) is the
 // unit-major leaf stage's, so both give the same bits. Four work-groups share a CU (at most 128
 // registers per lane and 40 KiB of LDS each: 512-pair tasks, 16-bit run offsets), so that many waves
-// cover the query gathers' latency, each with one register set of queries in flight.
+// cover the query gathers' latency, each with one register set of queries in flight. The bound names
+// three work-groups per CU: under it the compiler keeps two key-fragment reads from LDS in flight
+// ahead of the MFMAs (under a bound of four it waits for each read) and still ends at 124 registers,
+// so four work-groups fit all the same.
 constexpr int kLeafWgTask = 512;
 
 template <int D, int C>
-__global__ __launch_bounds__(256, 4) void leaf_lse_wg_kernel(LeafParams<uint16_t> p) {
+__global__ __launch_bounds__(256, 3) void leaf_lse_wg_kernel(LeafParams<uint16_t> p) {
   __shared__ __align__(16) uint16_t s_k[2 * C][D];
   __shared__ uint32_t s_pair[kLeafWgTask];
   __shared__ long long s_key[kLeafWgTask];
