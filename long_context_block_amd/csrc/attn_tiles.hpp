@@ -169,7 +169,7 @@ __device__ __forceinline__ void attend_tile_kv(KFrag kfrag, VFrag vfrag, const F
 #pragma unroll
     for (int m = 0; m < MS; ++m)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) mx = fmaxf(mx, sacc[m][j]);
+      for (int j = 0; j < 4; ++j) mx = max_nn(mx, sacc[m][j]);
   } else {
 #pragma unroll
     for (int m = 0; m < MS; ++m)
@@ -177,7 +177,7 @@ __device__ __forceinline__ void attend_tile_kv(KFrag kfrag, VFrag vfrag, const F
       for (int j = 0; j < 4; ++j) {
         const float x = attn_token(m, grp, j) <= lim ? sacc[m][j] : kNegInf;
         sacc[m][j] = x;
-        mx = fmaxf(mx, x);
+        mx = max_nn(mx, x);
       }
   }
   mx = colgroup_max(mx);

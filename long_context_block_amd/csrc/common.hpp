@@ -184,13 +184,12 @@ __device__ __forceinline__ void swap32(float v, float& lo, float& hi) {
   lo = __uint_as_float(r[0]);
   hi = __uint_as_float(r[1]);
 }
-// max(a, b) for values that are never NaN, as one v_max_f32: fmaxf first quiets each operand that the
-// compiler cannot prove is not a signalling NaN (two extra instructions after a lane swap)
-__device__ __forceinline__ float max_nn(float a, float b) {
-  float r;
-  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-  return r;
-}
+// max(a, b) for values that are never NaN, as one instruction: fmaxf first quiets each operand that the
+// compiler cannot prove is not a signalling NaN (two extra instructions after a lane swap), while the
+// NaN-propagating maximum needs no quieting and agrees with fmaxf on every value that is not NaN (up to
+// the sign of a zero result); chains of it become three-operand maxima
+__device__ __forceinline__ float max_nn(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float min_nn(float a, float b) { return __builtin_elementwise_minimum(a, b); }
 __device__ __forceinline__ float colgroup_max(float v) {
   float a, b;
   swap16(v, a, b);
@@ -212,7 +211,7 @@ template <int NV>
 __device__ __forceinline__ float column_lse(const float (&x)[NV], float scale) {
   float m = x[0];
 #pragma unroll
-  for (int j = 1; j < NV; ++j) m = fmaxf(m, x[j]);
+  for (int j = 1; j < NV; ++j) m = max_nn(m, x[j]);
   m = colgroup_max(m);
   const bool any = m != kNegInf;
   const float ms = any ? m : 0.f;
@@ -226,8 +225,8 @@ __device__ __forceinline__ float column_lse(const float (&x)[NV], float scale) {
 
 // LSE of two already-scaled values.
 __device__ __forceinline__ float lse2(float a, float b) {
-  const float m = fmaxf(a, b);
-  const float d = fminf(a, b) - m;
+  const float m = max_nn(a, b);
+  const float d = min_nn(a, b) - m;
   return m + kLn2 * fast_log2(1.f + fast_exp2(d * kLog2e));
 }
 
@@ -272,10 +271,10 @@ __device__ __forceinline__ float group_sum(float v) {
 }
 template <int G>
 __device__ __forceinline__ float group_max(float v) {
-  if constexpr (G >= 16) v = fmaxf(v, xor_lane<8>(v));
-  if constexpr (G >= 8) v = fmaxf(v, xor_lane<4>(v));
-  if constexpr (G >= 4) v = fmaxf(v, xor_lane<2>(v));
-  if constexpr (G >= 2) v = fmaxf(v, xor_lane<1>(v));
+  if constexpr (G >= 16) v = max_nn(v, xor_lane<8>(v));
+  if constexpr (G >= 8) v = max_nn(v, xor_lane<4>(v));
+  if constexpr (G >= 4) v = max_nn(v, xor_lane<2>(v));
+  if constexpr (G >= 2) v = max_nn(v, xor_lane<1>(v));
   return v;
 }
 
@@ -288,18 +287,18 @@ __device__ __forceinline__ float readlane(float v, int c) {
 // Max / min over all 64 lanes of the wave (every lane gets the result): DPP row reductions, then the
 // four row results read back with readlane.
 __device__ __forceinline__ float wave_max(float v) {
-  v = fmaxf(v, dpp_rot<0x128>(v));
-  v = fmaxf(v, dpp_rot<0x124>(v));
-  v = fmaxf(v, dpp_rot<0x122>(v));
-  v = fmaxf(v, dpp_rot<0x121>(v));
-  return fmaxf(fmaxf(readlane(v, 0), readlane(v, 16)), fmaxf(readlane(v, 32), readlane(v, 48)));
+  v = max_nn(v, dpp_rot<0x128>(v));
+  v = max_nn(v, dpp_rot<0x124>(v));
+  v = max_nn(v, dpp_rot<0x122>(v));
+  v = max_nn(v, dpp_rot<0x121>(v));
+  return max_nn(max_nn(readlane(v, 0), readlane(v, 16)), max_nn(readlane(v, 32), readlane(v, 48)));
 }
 __device__ __forceinline__ float wave_min(float v) {
-  v = fminf(v, dpp_rot<0x128>(v));
-  v = fminf(v, dpp_rot<0x124>(v));
-  v = fminf(v, dpp_rot<0x122>(v));
-  v = fminf(v, dpp_rot<0x121>(v));
-  return fminf(fminf(readlane(v, 0), readlane(v, 16)), fminf(readlane(v, 32), readlane(v, 48)));
+  v = min_nn(v, dpp_rot<0x128>(v));
+  v = min_nn(v, dpp_rot<0x124>(v));
+  v = min_nn(v, dpp_rot<0x122>(v));
+  v = min_nn(v, dpp_rot<0x121>(v));
+  return min_nn(min_nn(readlane(v, 0), readlane(v, 16)), min_nn(readlane(v, 32), readlane(v, 48)));
 }
 
 

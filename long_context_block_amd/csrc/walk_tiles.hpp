@@ -409,12 +409,8 @@ __device__ __forceinline__ void load_leaf_pair(const T* kbh, long long t0, int N
   }
 }
 
-// Per-column LSE over leaf 2p (lse0) and leaf 2p+1 (lse1) of scale * q_col . k_t for t <= icol.
-// kfrag(m, s) returns the A-fragment of tokens t0 + 16 m + (0..15), k step s.
-// kPhased: a scheduling fence after each k step, so that LDS-sourced fragments of one step at a time
-// are live (the arithmetic is unchanged).
 // Per-column LSEs of the two leaves from the accumulated tile dot products (acc[m]: tokens t0 + 16 m +
-// (0..15)), masking tokens after icol.
+// (0..15)), masking tokens after icol in place.
 template <typename T, int C>
 __device__ __forceinline__ void leaf_pair_lse_acc(f32x4 (&acc)[C / 8], long long t0, long long icol, float scale,
                                                   float& lse0, float& lse1) {
@@ -443,49 +439,6 @@ __device__ __forceinline__ void leaf_pair_lse_acc(f32x4 (&acc)[C / 8], long long
     for (int mm = 0; mm < ML; ++mm)
 #pragma unroll
       for (int j = 0; j < 4; ++j) x[mm * 4 + j] = acc[bit * ML + mm][j];
-    const float l = column_lse<ML * 4>(x, scale);
-    if (bit == 0)
-      lse0 = l;
-    else
-      lse1 = l;
-  }
-}
-
-// Per-column LSE over leaf 2p (lse0) and leaf 2p+1 (lse1) of scale * q_col . k_t for t <= icol.
-// kfrag(m, s) returns the A-fragment of tokens t0 + 16 m + (0..15), k step s.
-// kPhased: a scheduling fence after each k step, so that LDS-sourced fragments of one step at a time
-// are live (the arithmetic is unchanged).
-// Per-column LSEs of the two leaves from the accumulated tile dot products (acc[m]: tokens t0 + 16 m +
-// (0..15)), masking tokens after icol.
-template <typename T, int C>
-__device__ __forceinline__ void leaf_pair_lse_acc(const f32x4 (&acc)[C / 8], long long t0, long long icol, float scale,
-                                                  float& lse0, float& lse1) {
-  constexpr int ML = C / 16;  // M-tiles per leaf
-  const int grp = lane_id() >> 4;
-  // causal mask on offsets within the tile: token t0 + o is visible iff o <= icol - t0
-  const long long lim64 = icol - t0;
-  const int lim = lim64 < 0 ? -1 : (lim64 > 2 * C ? 2 * C : (int)lim64);
-  // bf16: every column sees all 2C tokens (the usual case away from the diagonal): no mask (same values)
-  bool all_visible = false;
-  if constexpr (sizeof(T) == 2) all_visible = __all(lim >= 2 * C - 1);
-#pragma unroll
-  for (int bit = 0; bit < 2; ++bit) {
-    float x[ML * 4];
-    if (all_visible) {
-#pragma unroll
-      for (int mm = 0; mm < ML; ++mm)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) x[mm * 4 + j] = acc[bit * ML + mm][j];
-    } else {
-#pragma unroll
-      for (int mm = 0; mm < ML; ++mm) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int o = 16 * (bit * ML + mm) + 4 * grp + j;
-          x[mm * 4 + j] = o <= lim ? acc[bit * ML + mm][j] : kNegInf;
-        }
-      }
-    }
     const float l = column_lse<ML * 4>(x, scale);
     if (bit == 0)
       lse0 = l;
