@@ -226,18 +226,18 @@ __global__ __launch_bounds__(256, 3) void attn_leaf_wg_kernel(AttnParams<uint16_
     // partial rows in sorted-pair order: a tile's rows are contiguous
     auto store = [&](const Out& out) {
       const long long prow = (base + out.xc) * p.G + h;
+      const long long prow_o = (base + row_partner(out.xc)) * p.G + (r16 ^ 8) % p.G;  // row r16 ^ 8
       // lane group grp holds dimensions 32 c + 8 grp .. +8 in o[2c], o[2c + 1]
-      uint16_t* dst = p.part + prow * D + 8 * grp;
       const float inv = out.inv;
+      uint4 w[MO / 2];
 #pragma unroll
       for (int c = 0; c < MO / 2; ++c) {
-        uint4 w;
-        w.x = pack_bf16x2(out.o[2 * c][0] * inv, out.o[2 * c][1] * inv);
-        w.y = pack_bf16x2(out.o[2 * c][2] * inv, out.o[2 * c][3] * inv);
-        w.z = pack_bf16x2(out.o[2 * c + 1][0] * inv, out.o[2 * c + 1][1] * inv);
-        w.w = pack_bf16x2(out.o[2 * c + 1][2] * inv, out.o[2 * c + 1][3] * inv);
-        *reinterpret_cast<uint4*>(dst + 32 * c) = w;
+        w[c].x = pack_bf16x2(out.o[2 * c][0] * inv, out.o[2 * c][1] * inv);
+        w[c].y = pack_bf16x2(out.o[2 * c][2] * inv, out.o[2 * c][3] * inv);
+        w[c].z = pack_bf16x2(out.o[2 * c + 1][0] * inv, out.o[2 * c + 1][1] * inv);
+        w[c].w = pack_bf16x2(out.o[2 * c + 1][2] * inv, out.o[2 * c + 1][3] * inv);
       }
+      store_rows_lines<D>(p.part + prow * D + 8 * grp, p.part + prow_o * D + 8 * grp, w);
       if (grp == 0) p.part_lse[prow] = out.lse;  // the column's 4 lanes hold the same value
     };
     if (wave < ntiles) {

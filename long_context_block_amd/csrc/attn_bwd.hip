@@ -180,16 +180,17 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
         for (int ks = 0; ks < KS; ++ks) mma(qacc[mt], vt_frag<C>(s_kt, mt, ks), df[ks]);
       }
       // lane group grp holds dimensions 32 c + 8 grp .. +8 in qacc[2c], qacc[2c + 1]
-      uint16_t* dst = p.part + ((base + xc) * p.G + h) * D + 8 * grp;
+      uint4 w[MO / 2];
 #pragma unroll
       for (int c = 0; c < MO / 2; ++c) {
-        uint4 w;
-        w.x = pack_bf16x2(qacc[2 * c][0], qacc[2 * c][1]);
-        w.y = pack_bf16x2(qacc[2 * c][2], qacc[2 * c][3]);
-        w.z = pack_bf16x2(qacc[2 * c + 1][0], qacc[2 * c + 1][1]);
-        w.w = pack_bf16x2(qacc[2 * c + 1][2], qacc[2 * c + 1][3]);
-        *reinterpret_cast<uint4*>(dst + 32 * c) = w;
+        w[c].x = pack_bf16x2(qacc[2 * c][0], qacc[2 * c][1]);
+        w[c].y = pack_bf16x2(qacc[2 * c][2], qacc[2 * c][3]);
+        w[c].z = pack_bf16x2(qacc[2 * c + 1][0], qacc[2 * c + 1][1]);
+        w[c].w = pack_bf16x2(qacc[2 * c + 1][2], qacc[2 * c + 1][3]);
       }
+      const long long prow = (base + xc) * p.G + h;
+      const long long prow_o = (base + row_partner(xc)) * p.G + (r16 ^ 8) % p.G;  // row r16 ^ 8
+      store_rows_lines<D>(p.part + prow * D + 8 * grp, p.part + prow_o * D + 8 * grp, w);
     }
     __syncthreads();  // every wave is done with this leaf's tiles before they are restaged
   }

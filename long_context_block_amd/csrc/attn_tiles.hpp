@@ -15,11 +15,41 @@ __device__ __forceinline__ int attn_token(int m, int grp, int j) { return 32 * (
 
 // Output dimension in D-row 4*grp + j of M-tile mt of O^T. The rows of V^T are permuted so that the
 // pair of M-tiles (2c, 2c + 1) gives lane group grp the 8 consecutive dimensions 32 c + 8 grp .. +8:
-// one 16-byte store per lane then covers 64 contiguous bytes of each output row per instruction.
+// a row's 4 lanes hold 64 contiguous bytes of it per M-tile pair.
 template <int D>
 __device__ __forceinline__ int attn_out_dim(int mt, int grp, int j) {
   return 32 * (mt >> 1) + 8 * grp + 4 * (mt & 1) + j;
 }
+// Stores 16 bf16 rows of D dimensions that a wave holds in that output layout: lane (r16, grp) has chunk c
+// of row r16 (dimensions 32 c + 8 grp .. +8, 16 bytes) in w[c]; own points at dimension 8 grp of row r16
+// and other at dimension 8 grp of row r16 ^ 8. Rows r16 and r16 ^ 8 trade chunks by a DPP rotation by 8
+// within each 16-lane row, so that every store writes whole 128-byte lines: for the chunk pair (2 L,
+// 2 L + 1) the first store covers rows 0-7 (the lanes of rows 8-15 writing chunk 2 L + 1 of row r16 ^ 8)
+// and the second rows 8-15, instead of four stores of 64-byte half lines. The same bytes reach the same
+// places.
+template <int D>
+__device__ __forceinline__ void store_rows_lines(uint16_t* own, uint16_t* other, const uint4 (&w)[D / 32]) {
+  static_assert(D % 64 == 0, "row of whole 128-byte lines");
+  const bool lo = (lane_id() & 15) < 8;
+  uint16_t* dst_a = lo ? own : other;  // rows 0-7
+  uint16_t* dst_b = lo ? other : own;  // rows 8-15
+  auto ror8 = [](uint32_t v) { return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xf, 0xf, false); };
+#pragma unroll
+  for (int L = 0; L < D / 64; ++L) {
+    const uint4 a = w[2 * L], b = w[2 * L + 1];
+    const uint4 xa = make_uint4(ror8(a.x), ror8(a.y), ror8(a.z), ror8(a.w));  // row r16 ^ 8's chunk 2 L
+    const uint4 xb = make_uint4(ror8(b.x), ror8(b.y), ror8(b.z), ror8(b.w));  // and its chunk 2 L + 1
+    const int c = lo ? 2 * L : 2 * L + 1;  // the chunk this lane writes in both stores
+    // component-wise selects (a select of whole vectors would go through memory)
+    *reinterpret_cast<uint4*>(dst_a + 32 * c) =
+        make_uint4(lo ? a.x : xb.x, lo ? a.y : xb.y, lo ? a.z : xb.z, lo ? a.w : xb.w);
+    *reinterpret_cast<uint4*>(dst_b + 32 * c) =
+        make_uint4(lo ? xa.x : b.x, lo ? xa.y : b.y, lo ? xa.z : b.z, lo ? xa.w : b.w);
+  }
+}
+// The value v of lane r16 ^ 8 (same lane group).
+__device__ __forceinline__ int row_partner(int v) { return __builtin_amdgcn_update_dpp(0, v, 0x128, 0xf, 0xf, false); }
+
 // Inverse: the V^T row (16 mt + 4 grp + j) that holds dimension d.
 template <int D>
 __device__ __forceinline__ int attn_vt_row(int d) {
