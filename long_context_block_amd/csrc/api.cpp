@@ -285,7 +285,8 @@ struct AttnBwdWs {
   int* ranks;
   uint32_t* pairs;
   float* dsum;
-  float* acc;  // dk accumulators, then dv accumulators
+  float* acc;      // dk accumulators, then dv accumulators
+  float* kv_part;  // per-task dK / dV sums of leaves shared between tasks
   void* part;
 };
 
@@ -300,6 +301,7 @@ size_t carve_attn_bwd(const Plan& p, void* ws, AttnBwdWs* w) {
   x.pairs = (uint32_t*)c.take(pairs * 4);
   x.dsum = (float*)c.take((size_t)p.sd.B * p.sd.Hq * p.sd.N * 4);
   x.acc = (float*)c.take((size_t)2 * p.U * p.sd.D * 4);
+  x.kv_part = (float*)c.take(pisa::attn_backward_kv_part_bytes(p.sd));
   x.part = c.take(pairs * p.sd.G * p.sd.D * 2);
   if (w) *w = x;
   return c.off;
@@ -767,9 +769,9 @@ pisa_status pisa_sparse_attn_backward(const pisa_shape* shape, const void* q, co
     {
       Stage sc(s, "attn_backward");
       e = pisa::launch_attn_backward(cp.sd, q16 + qo, k16 + ko, v16 + ko, selc, (const uint16_t*)o + qo,
-                                     o_lse + f * G * N, (const uint16_t*)d_o + qo, w.pairs, total, w.ranks, w.dsum,
-                                     w.acc, w.acc + (size_t)cp.U * cp.sd.D, w.part, (uint16_t*)d_q + qo,
-                                     (uint16_t*)d_k + ko, (uint16_t*)d_v + ko, s);
+                                     o_lse + f * G * N, (const uint16_t*)d_o + qo, w.pairs, total, w.ranks,
+                                     w.offsets, w.dsum, w.acc, w.acc + (size_t)cp.U * cp.sd.D, w.kv_part, w.part,
+                                     (uint16_t*)d_q + qo, (uint16_t*)d_k + ko, (uint16_t*)d_v + ko, s);
     }
     if (e != hipSuccess) return hip_status(e, "pisa_sparse_attn_backward");
   }

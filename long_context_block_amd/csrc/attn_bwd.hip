@@ -13,8 +13,10 @@
 //   dkdv:  per run, wave w owns tokens 16 w .. 16 w + 15 of the leaf (C = 32: two waves per slice, on
 //          alternate tile pairs); tiles of 32 columns (q, dO rows and their transposes staged in LDS);
 //          S^T = q K_w^T with the column rows permuted so that P^T and dS^T come out in the B-operand layout
-//          of the next products; dv^T += dO^T P^T, dk^T += q^T dS^T in registers, added to the fp32
-//          accumulators (atomics) at the end of the run.
+//          of the next products; dv^T += dO^T P^T, dk^T += q^T dS^T in registers. At the end of the run
+//          (C = 64) the sums go to the fp32 accumulators when no other task holds pairs of the leaf, else to
+//          one of the task's two slots, which bwd_kv_reduce adds up per leaf in task order (no atomics:
+//          they took a third of the backward's time); C = 32 adds them into the accumulators with atomics.
 //   merge: dq = s * sum of the unit's partial rows; finish: the accumulators in the output type.
 #include "attn_tiles.hpp"
 #include "common.hpp"
@@ -43,6 +45,7 @@ struct BwdParams {
   uint16_t* part;  // [pairs, G, D] unscaled dq partials (dq pass)
   float* dk_acc;   // [B, Hkv, N, D]
   float* dv_acc;
+  float* kv_part;  // C = 64: [dkdv tasks, 2 slots, 2 (dk, dv), C, D] sums of runs shared with another task
 };
 
 // ------------------------------------------------------------------------------------------ prep
@@ -233,14 +236,23 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(BwdParams p) {
   if (base >= total) return;
   const int n = (int)(total - base < kWgTaskDkdv ? total - base : kWgTaskDkdv);
   const long long nch = ((long long)p.N + (1LL << p.chunk_log2) - 1) >> p.chunk_log2;
-  const int nrun = stage_pair_runs<kWgTaskDkdv>(
-      p.pairs, base, n,
-      [&](uint32_t pr) {
-        const long long u = pr >> 5;
-        const unsigned bh = (unsigned)u / (unsigned)p.N, i = (unsigned)u - bh * (unsigned)p.N;
-        return ((long long)bh * nch + (i >> p.chunk_log2)) * (1LL << 32) + p.sel[u * p.K + (pr & 31)];
-      },
-      s_pair, s_key, s_run, s_wcount);
+  auto key_of = [&](uint32_t pr) {
+    const long long u = pr >> 5;
+    const unsigned bh = (unsigned)u / (unsigned)p.N, i = (unsigned)u - bh * (unsigned)p.N;
+    return ((long long)bh * nch + (i >> p.chunk_log2)) * (1LL << 32) + p.sel[u * p.K + (pr & 31)];
+  };
+  const int nrun = stage_pair_runs<kWgTaskDkdv>(p.pairs, base, n, key_of, s_pair, s_key, s_run, s_wcount);
+  // C = 64 (one wave per token slice): a run whose leaf has pairs in no other task stores its sums
+  // straight to the accumulators; the task's first run, if its leaf began in an earlier task, and its
+  // last run, if its leaf goes on in a later one, store them to the task's slots 0 and 1 (the first run
+  // takes slot 0 when it is also the last), and bwd_kv_reduce adds a leaf's slots in task order. C = 32
+  // (two waves per slice) adds into the accumulators with atomics.
+  constexpr bool kSlots = NSL == 4;
+  __shared__ int s_cont[2];  // the first run continues an earlier task's; the last run goes on
+  if (kSlots && tid == 0) {
+    s_cont[0] = base > 0 && key_of(p.pairs[base - 1]) == s_key[0];
+    s_cont[1] = base + n < total && key_of(p.pairs[base + n]) == s_key[n - 1];
+  }
   // this wave's token slice, and (C = 32) which tile pairs it takes
   const int slice = wave % NSL, phase = wave / NSL, nphase = 4 / NSL;
   const int units_per_pair = kBwdCols / p.G;
@@ -387,8 +399,31 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(BwdParams p) {
       __syncthreads();  // the tile pair is consumed before the next one is staged
     }
     // the run's contributions: lane (t, g) holds dims attn_out_dim(mt, g, j) of token 16 slice + t
+    // (4 consecutive dimensions per M-tile)
     const long long tok = t0 + 16 * slice + r16;
-    if (tok < p.N) {
+    if constexpr (kSlots) {
+      const bool shared = (a == 0 && s_cont[0]) || (b == n && s_cont[1]);
+      float* dkr;
+      float* dvr;
+      if (shared) {
+        const long long task = base / kWgTaskDkdv;
+        float* slot = p.kv_part + (task * 2 + (a == 0 ? 0 : 1)) * 2 * C * D;
+        dkr = slot + (16 * slice + r16) * D;
+        dvr = dkr + C * D;
+      } else {
+        dkr = p.dk_acc + (bh * p.N + tok) * D;
+        dvr = p.dv_acc + (bh * p.N + tok) * D;
+      }
+      if (shared || tok < p.N) {
+#pragma unroll
+        for (int mt = 0; mt < MO; ++mt) {
+          const int dim = attn_out_dim<D>(mt, grp, 0);
+          *reinterpret_cast<float4*>(dvr + dim) = make_float4(dva[mt][0], dva[mt][1], dva[mt][2], dva[mt][3]);
+          *reinterpret_cast<float4*>(dkr + dim) = make_float4(p.scale * dka[mt][0], p.scale * dka[mt][1],
+                                                              p.scale * dka[mt][2], p.scale * dka[mt][3]);
+        }
+      }
+    } else if (tok < p.N) {
       float* dvr = p.dv_acc + (bh * p.N + tok) * D;
       float* dkr = p.dk_acc + (bh * p.N + tok) * D;
 #pragma unroll
@@ -461,6 +496,43 @@ __global__ __launch_bounds__(256) void bwd_dq_merge_kernel(const int* __restrict
   *reinterpret_cast<uint4*>(dq + row * D + 8 * li) = w;
 }
 
+// dK / dV of the leaves whose pairs span several dkdv tasks (C = 64): one work-group per (sequence, KV
+// head, leaf) bucket of the attention regroup (pairs [off[x], off[x + 1]) of the sorted list); the sum of
+// the leaf's slots over its tasks, in task order, to the accumulators. A leaf within one task was stored
+// by that task; a leaf without pairs keeps the cleared zeros.
+template <int D, int C>
+__global__ __launch_bounds__(256) void bwd_kv_reduce_kernel(const int* __restrict__ off, const float* __restrict__ kv_part,
+                                                            int leaves, int N, float* __restrict__ dk_acc,
+                                                            float* __restrict__ dv_acc) {
+  const int x = blockIdx.x;
+  const long long start = off[x], end = off[x + 1];
+  if (end <= start) return;
+  const long long t0 = start / kWgTaskDkdv, t1 = (end - 1) / kWgTaskDkdv;
+  if (t1 == t0) return;
+  const long long bh = x / leaves;
+  const int leaf = x % leaves;
+  constexpr int Q = C * D / 4;  // float4 items per array
+  const int s0 = start % kWgTaskDkdv == 0 ? 0 : 1;  // the leaf's slot in its first task
+  for (int it = threadIdx.x; it < 2 * Q; it += 256) {
+    const int arr = it / Q, rem = it % Q;  // arr 0: dk, 1: dv
+    const int tok_off = rem / (D / 4);
+    const float4* src = reinterpret_cast<const float4*>(kv_part) + arr * Q + rem;
+    float4 acc = src[(t0 * 2 + s0) * 2 * Q];
+    for (long long t = t0 + 1; t <= t1; ++t) {
+      const float4 v = src[t * 2 * 2 * Q];
+      acc.x += v.x;
+      acc.y += v.y;
+      acc.z += v.z;
+      acc.w += v.w;
+    }
+    const long long tok = (long long)leaf * C + tok_off;
+    if (tok < N) {
+      float* dst = (arr ? dv_acc : dk_acc) + (bh * N + tok) * D + 4 * (rem % (D / 4));
+      *reinterpret_cast<float4*>(dst) = acc;
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void bwd_finish_kernel(const float* __restrict__ acc, long long n,
                                                          uint16_t* __restrict__ out) {
   const long long j = ((long long)blockIdx.x * blockDim.x + threadIdx.x) * 2;
@@ -469,8 +541,8 @@ __global__ __launch_bounds__(256) void bwd_finish_kernel(const float* __restrict
 
 // ------------------------------------------------------------------------------------------ launchers
 template <int D, int C>
-static hipError_t bwd_t(const SelDims& sd, const BwdParams& p0, const int* pos, void* d_q, void* d_k, void* d_v,
-                        hipStream_t st) {
+static hipError_t bwd_t(const SelDims& sd, const BwdParams& p0, const int* pos, const int* offsets, void* d_q,
+                        void* d_k, void* d_v, hipStream_t st) {
   BwdParams p = p0;
   const long long rows = (long long)sd.B * sd.Hq * sd.N;
   const long long kv = (long long)sd.B * sd.Hkv * sd.N * D;
@@ -485,6 +557,11 @@ static hipError_t bwd_t(const SelDims& sd, const BwdParams& p0, const int* pos, 
   hipLaunchKernelGGL((attn_bwd_dq_kernel<D, C>), dim3((unsigned)wg), dim3(256), 0, st, p);
   hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, C>), dim3((unsigned)((max_pairs + kWgTaskDkdv - 1) / kWgTaskDkdv)),
                      dim3(256), 0, st, p);
+  if constexpr (C == 64) {
+    const int leaves = sd.lv.n[0];
+    hipLaunchKernelGGL((bwd_kv_reduce_kernel<D, C>), dim3((unsigned)((long long)sd.B * sd.Hkv * leaves)), dim3(256),
+                       0, st, offsets, p.kv_part, leaves, sd.N, p.dk_acc, p.dv_acc);
+  }
   const long long mt = rows * (D / 8);
   hipLaunchKernelGGL((bwd_dq_merge_kernel<D>), dim3((unsigned)((mt + 255) / 256)), dim3(256), 0, st, p.sel, pos,
                      p.part, sd.B, sd.Hq, sd.Hkv, sd.G, sd.N, sd.K, sd.scale, (uint16_t*)d_q);
@@ -497,8 +574,9 @@ static hipError_t bwd_t(const SelDims& sd, const BwdParams& p0, const int* pos, 
 
 hipError_t launch_attn_backward(const SelDims& sd, const void* q, const void* k, const void* v, const int* sel,
                                 const void* o, const float* o_lse, const void* d_o, const uint32_t* pairs,
-                                const int* total, const int* pos, float* dsum, float* dk_acc, float* dv_acc,
-                                void* part, void* d_q, void* d_k, void* d_v, hipStream_t st) {
+                                const int* total, const int* pos, const int* offsets, float* dsum, float* dk_acc,
+                                float* dv_acc, float* kv_part, void* part, void* d_q, void* d_k, void* d_v,
+                                hipStream_t st) {
   BwdParams p;
   p.q = (const uint16_t*)q;
   p.k = (const uint16_t*)k;
@@ -521,12 +599,19 @@ hipError_t launch_attn_backward(const SelDims& sd, const void* q, const void* k,
   p.part = (uint16_t*)part;
   p.dk_acc = dk_acc;
   p.dv_acc = dv_acc;
+  p.kv_part = kv_part;
   if (sd.D == 128) {
-    if (sd.C == 64) return bwd_t<128, 64>(sd, p, pos, d_q, d_k, d_v, st);
-    return bwd_t<128, 32>(sd, p, pos, d_q, d_k, d_v, st);
+    if (sd.C == 64) return bwd_t<128, 64>(sd, p, pos, offsets, d_q, d_k, d_v, st);
+    return bwd_t<128, 32>(sd, p, pos, offsets, d_q, d_k, d_v, st);
   }
-  if (sd.C == 64) return bwd_t<64, 64>(sd, p, pos, d_q, d_k, d_v, st);
-  return bwd_t<64, 32>(sd, p, pos, d_q, d_k, d_v, st);
+  if (sd.C == 64) return bwd_t<64, 64>(sd, p, pos, offsets, d_q, d_k, d_v, st);
+  return bwd_t<64, 32>(sd, p, pos, offsets, d_q, d_k, d_v, st);
+}
+
+size_t attn_backward_kv_part_bytes(const SelDims& sd) {
+  if (sd.C != 64) return 0;
+  const long long tasks = ((long long)sd.B * sd.Hkv * sd.N * sd.K + kWgTaskDkdv - 1) / kWgTaskDkdv;
+  return (size_t)tasks * 2 * 2 * sd.C * sd.D * sizeof(float);
 }
 
 }  // namespace pisa

@@ -74,12 +74,15 @@ hipError_t launch_attn_leaf(const SelDims& sd, const void* q, const void* k, con
 hipError_t launch_attn_merge(const SelDims& sd, const int* sel, const int* pos, const void* part,
                              const float* part_lse, void* o, float* o_lse, hipStream_t st);
 
-// Backward of the sparse attention (bf16): pairs/total/pos from launch_regroup over sel (to positions);
-// dsum [B Hq N], dk_acc and dv_acc = dk_acc + B Hkv N D (fp32 accumulators), part [pairs, G, D] (bf16).
+// Backward of the sparse attention (bf16): pairs/total/pos/offsets from launch_regroup over sel (to
+// positions); dsum [B Hq N], dk_acc and dv_acc = dk_acc + B Hkv N D (fp32 accumulators), kv_part
+// attn_backward_kv_part_bytes(sd) of per-task dK/dV slots, part [pairs, G, D] (bf16).
 hipError_t launch_attn_backward(const SelDims& sd, const void* q, const void* k, const void* v, const int* sel,
                                 const void* o, const float* o_lse, const void* d_o, const uint32_t* pairs,
-                                const int* total, const int* pos, float* dsum, float* dk_acc, float* dv_acc,
-                                void* part, void* d_q, void* d_k, void* d_v, hipStream_t st);
+                                const int* total, const int* pos, const int* offsets, float* dsum, float* dk_acc,
+                                float* dv_acc, float* kv_part, void* part, void* d_q, void* d_k, void* d_v,
+                                hipStream_t st);
+size_t attn_backward_kv_part_bytes(const SelDims& sd);
 
 // Flat block selection.
 hipError_t launch_bsa(const SelDims& sd, const void* q, const float* leaf_mean, const uint16_t* leaf_hilo, int* sel,

@@ -101,8 +101,9 @@ def test_backward_16k():
 def test_chunked_attention_equals_one_chunk(monkeypatch):
     """The attention and its backward cut the batch into chunks of (sequence, KV head) slices. Forced to one
     slice per chunk (a 1 MiB budget), they give the same forward bits (O and its LSE) and the same dq bits
-    as the single-chunk run; dk and dv, summed with floating-point atomics in either run, agree to the
-    last bits of their bf16 outputs."""
+    as the single-chunk run; dk and dv sum a leaf's pairs in an order set by the regroup (pairs of one leaf
+    are placed by atomic counters) and by where the task boundaries fall in the sorted pair list, which
+    moves with the chunking, so they agree to the last bits of their bf16 outputs."""
     pf = I.make_prefill(B=2, Hq=8, Hkv=2, N=1500, d=128, C=64, K=6, dtype="bf16", keys="ar1", seed=0,
                         workload_id=710)
     s = shape_of(pf, 4)
@@ -136,3 +137,4 @@ def test_chunked_attention_equals_one_chunk(monkeypatch):
         assert np.abs(a - b).max() <= 2 ** -7 * max(1.0, float(np.abs(a).max())), name
     summary(f"[attention chunking] 4 one-slice chunks equal one chunk: O, LSE and dq bit for bit, dk/dv within bf16 "
             f"rounding (max diff {max(float(np.abs(a - b).max()) for a, b in zip(one[3:], chunked[3:])):.3g})")
+
