@@ -678,27 +678,53 @@ __global__ __launch_bounds__(1024) void hist_kernel(const int* __restrict__ node
   }
 }
 
-// Exclusive scan of n counts into offsets[0..n] (one work-group of 1024 threads).
+// Exclusive scan of n counts into offsets[0..n] (one work-group of 1024 threads; counts and offsets
+// 16-byte aligned). Tiles of 4096 counts: each thread reads 4 consecutive counts of the tile as one 16-byte
+// load (the next tile's load is in flight meanwhile), the waves scan their threads' sums by lane
+// shuffles, the wave totals meet in LDS, and the tile's total carries into the next tile.
 __global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ counts, long long n, int* __restrict__ offsets) {
-  __shared__ long long s_part[1024];
-  const long long per = (n + 1023) / 1024;
-  const long long a = threadIdx.x * per, e = a + per < n ? a + per : n;
-  long long s = 0;
-  for (long long j = a; j < e; ++j) s += counts[j];
-  s_part[threadIdx.x] = s;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const long long v = threadIdx.x >= off ? s_part[threadIdx.x - off] : 0;
+  constexpr int kTile = 4096;
+  __shared__ int s_wave[16];
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  auto load4 = [&](long long j) {
+    if (j + 3 < n) return *reinterpret_cast<const int4*>(counts + j);
+    return make_int4(j < n ? counts[j] : 0, j + 1 < n ? counts[j + 1] : 0, j + 2 < n ? counts[j + 2] : 0, 0);
+  };
+  long long carry = 0;  // the counts of the tiles before this one
+  int4 c = load4(4LL * tid);
+  for (long long t0 = 0; t0 < n; t0 += kTile) {
+    const long long j = t0 + 4LL * tid;
+    const int4 nx = t0 + kTile < n ? load4(j + kTile) : make_int4(0, 0, 0, 0);
+    const int own = c.x + c.y + c.z + c.w;
+    int x = own;  // inclusive scan over the wave's lanes
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) s_wave[wave] = x;
     __syncthreads();
-    s_part[threadIdx.x] += v;
-    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+      const int v = s_wave[w];
+      before += w < wave ? v : 0;
+      total += v;
+    }
+    const int e0 = (int)carry + before + x - own;  // offset of this thread's first count
+    const int4 o4 = make_int4(e0, e0 + c.x, e0 + c.x + c.y, e0 + c.x + c.y + c.z);
+    if (j + 3 < n) {
+      *reinterpret_cast<int4*>(offsets + j) = o4;
+    } else {
+      if (j < n) offsets[j] = o4.x;
+      if (j + 1 < n) offsets[j + 1] = o4.y;
+      if (j + 2 < n) offsets[j + 2] = o4.z;
+    }
+    carry += total;
+    c = nx;
+    __syncthreads();  // s_wave is rewritten by the next tile
   }
-  long long run = threadIdx.x ? s_part[threadIdx.x - 1] : 0;
-  for (long long j = a; j < e; ++j) {
-    offsets[j] = (int)run;
-    run += counts[j];
-  }
-  if (threadIdx.x == 1023) offsets[n] = (int)s_part[1023];
+  if (tid == 0) offsets[n] = (int)carry;
 }
 
 // With to_positions, ranks[x] is replaced by the pair's index in the sorted list (its row in the
