@@ -58,7 +58,10 @@ def _oracle_head(task):
 
 
 def check_backward(pf, q_tile, label):
-    g = run_backward(pf, q_tile)
+    compare_backward(pf, run_backward(pf, q_tile), label)
+
+
+def compare_backward(pf, g, label):
     heads = [(b, r) for b in range(pf.B) for r in range(pf.Hkv)]
     GC._CTX.update(pf=pf, g=g)
     try:
@@ -138,3 +141,52 @@ def test_chunked_attention_equals_one_chunk(monkeypatch):
     summary(f"[attention chunking] 4 one-slice chunks equal one chunk: O, LSE and dq bit for bit, dk/dv within bf16 "
             f"rounding (max diff {max(float(np.abs(a - b).max()) for a, b in zip(one[3:], chunked[3:])):.3g})")
 
+
+
+def _boundary_selection(N, C, K, extra):
+    """Left-packed, ascending selection [N, K]: every position keeps its own leaf, and leaf j gets extra[j]
+    more positions (the first eligible ones with a free slot), so that leaf j's bucket of the attention
+    regroup holds (tokens of leaf j) + extra[j] pairs."""
+    sets = [[i // C] for i in range(N)]
+    for j, n in sorted(extra.items()):
+        i = C * (j + 1)
+        while n:
+            if len(sets[i]) < K and j not in sets[i]:
+                sets[i].append(j)
+                n -= 1
+            i += 1
+    sel = np.full((N, K), -1, dtype=np.int32)
+    for i, lv in enumerate(sets):
+        lv = sorted(lv)
+        sel[i, :len(lv)] = lv
+    return sel
+
+
+def test_backward_task_boundaries():
+    """dK / dV of leaves at every kind of edge of the dK/dV pass's 512-pair tasks, on a crafted selection
+    (B = 1, one KV head, N = 4096, C = 64, K = 4): leaf 0 fills task 0 exactly; leaf 1 fills tasks 1 and 2
+    (it starts on a task boundary and continues); leaf 2 lies inside task 3; leaf 3 starts inside task 3
+    and ends inside task 5, across the whole of task 4; leaf 4 ends exactly on a task boundary; leaf 5
+    starts on one. Gradients against the oracle, as in the other backward tests."""
+    pf = I.make_prefill(B=1, Hq=4, Hkv=1, N=4096, d=128, C=64, K=4, dtype="bf16", keys="ar1", seed=0,
+                        workload_id=730)
+    sel_np = _boundary_selection(pf.N, pf.C, pf.K, {0: 448, 1: 960, 2: 36, 3: 936, 4: 372})
+    counts = np.bincount(sel_np[sel_np >= 0], minlength=pf.N // pf.C)
+    starts = np.concatenate([[0], np.cumsum(counts)])
+    assert list(counts[:6]) == [512, 1024, 100, 1000, 436, 64]
+    assert list(starts[:7]) == [0, 512, 1536, 1636, 2636, 3072, 3136]
+    s = shape_of(pf, 4)
+    q, k, v = to_device(pf.q), to_device(pf.k), to_device(pf.v)
+    sel = torch.from_numpy(sel_np.reshape(1, 1, pf.N, pf.K)).cuda()
+    o = torch.empty_like(q)
+    o_lse = torch.empty((pf.B, pf.Hq, pf.N), dtype=torch.float32, device="cuda")
+    P.pisa_sparse_attn(s, q, k, v, sel, o, o_lse, P.alloc_workspace(s, P.PISA_OP_ATTN))
+    rng = np.random.default_rng(5)
+    do_np = I.bf16_bits(rng.standard_normal(q.shape, dtype=np.float32))
+    d_o = torch.from_numpy(do_np.view(np.int16)).cuda().view(torch.bfloat16)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    P.pisa_sparse_attn_backward(s, q, k, v, sel, o, o_lse, d_o, dq, dk, dv, P.alloc_workspace(s, P.PISA_OP_ATTN_BWD))
+    torch.cuda.synchronize()
+    g = dict(sel=sel.cpu().numpy(), do=I.bf16_to_f32(do_np).astype(np.float64), dq=dq.float().cpu().numpy(),
+             dk=dk.float().cpu().numpy(), dv=dv.float().cpu().numpy())
+    compare_backward(pf, g, "task boundaries")
