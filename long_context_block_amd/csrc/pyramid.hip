@@ -59,8 +59,23 @@ __global__ __launch_bounds__(256) void pool_subtree_kernel(const T* __restrict__
       for (int w = 0; w < 3; ++w)
 #pragma unroll
         for (int e = 0; e < 8; ++e) part[w][e] = 0.f;
+      // sixteen tokens per step while they last (sixteen loads in flight), added to the same four
+      // partial sums in the same order as the steps of four below
+      const int c16 = cnt & ~15;
+      for (int t = 0; t < c16; t += 16) {
+        Frag<T> f[16];
+#pragma unroll
+        for (int x = 0; x < 16; ++x) f[x].load(src + (long long)(t + x) * D);
+#pragma unroll
+        for (int x = 0; x < 16; x += 4) {
+          add(acc, f[x]);
+          add(part[0], f[x + 1]);
+          add(part[1], f[x + 2]);
+          add(part[2], f[x + 3]);
+        }
+      }
       const int c4 = cnt & ~3;
-      for (int t = 0; t < c4; t += 4) {
+      for (int t = c16; t < c4; t += 4) {
         Frag<T> f0, f1, f2, f3;
         f0.load(src + (long long)t * D);
         f1.load(src + (long long)(t + 1) * D);
