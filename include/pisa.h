@@ -173,8 +173,8 @@ pisa_status pisa_sparse_attn(const pisa_shape* shape, const void* q, const void*
  *   d_o [B, Hq, N, d]: the gradient of o. d_q [B, Hq, N, d], d_k and d_v [B, Hkv, N, d]: out.
  *   bfloat16 inputs and outputs only (fp32 accumulation); PISA_EUNSUPPORTED for fp32.
  *   ws: pisa_workspace_size(shape, PISA_OP_ATTN_BWD) bytes. d_k and d_v add the pairs of a leaf in the
- *   order in which the pairs were bucketed (by atomic counters; with block = 32 the sums themselves use
- *   floating-point atomics), so their last bits may differ from run to run. */
+ *   order in which the pairs were bucketed (by atomic counters), so their last bits may differ from run
+ *   to run. */
 pisa_status pisa_sparse_attn_backward(const pisa_shape* shape, const void* q, const void* k, const void* v,
                                       const int32_t* sel, const void* o, const float* o_lse, const void* d_o,
                                       void* d_q, void* d_k, void* d_v, void* ws, size_t ws_bytes, void* stream);

@@ -13,10 +13,10 @@
 //   dkdv:  per run, wave w owns tokens 16 w .. 16 w + 15 of the leaf (C = 32: two waves per slice, on
 //          alternate tile pairs); tiles of 32 columns (q, dO rows and their transposes staged in LDS);
 //          S^T = q K_w^T with the column rows permuted so that P^T and dS^T come out in the B-operand layout
-//          of the next products; dv^T += dO^T P^T, dk^T += q^T dS^T in registers. At the end of the run
-//          (C = 64) the sums go to the fp32 accumulators when no other task holds pairs of the leaf, else to
-//          one of the task's two slots, which bwd_kv_reduce adds up per leaf in task order (no atomics:
-//          they took a third of the backward's time); C = 32 adds them into the accumulators with atomics.
+//          of the next products; dv^T += dO^T P^T, dk^T += q^T dS^T in registers (C = 32: the two waves of
+//          a slice add theirs through LDS). At the end of the run the sums go to the fp32 accumulators when
+//          no other task holds pairs of the leaf, else to one of the task's two slots, which bwd_kv_reduce
+//          adds up per leaf in task order (no atomics: they took a third of the backward's time).
 //   merge: dq = s * sum of the unit's partial rows; finish: the accumulators in the output type.
 #include "attn_tiles.hpp"
 #include "common.hpp"
@@ -45,7 +45,7 @@ struct BwdParams {
   uint16_t* part;  // [pairs, G, D] unscaled dq partials (dq pass)
   float* dk_acc;   // [B, Hkv, N, D]
   float* dv_acc;
-  float* kv_part;  // C = 64: [dkdv tasks, 2 slots, 2 (dk, dv), C, D] sums of runs shared with another task
+  float* kv_part;  // [dkdv tasks, 2 slots, 2 (dk, dv), C, D] sums of runs shared with another task
 };
 
 // ------------------------------------------------------------------------------------------ prep
@@ -242,14 +242,12 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(BwdParams p) {
     return ((long long)bh * nch + (i >> p.chunk_log2)) * (1LL << 32) + p.sel[u * p.K + (pr & 31)];
   };
   const int nrun = stage_pair_runs<kWgTaskDkdv>(p.pairs, base, n, key_of, s_pair, s_key, s_run, s_wcount);
-  // C = 64 (one wave per token slice): a run whose leaf has pairs in no other task stores its sums
-  // straight to the accumulators; the task's first run, if its leaf began in an earlier task, and its
-  // last run, if its leaf goes on in a later one, store them to the task's slots 0 and 1 (the first run
-  // takes slot 0 when it is also the last), and bwd_kv_reduce adds a leaf's slots in task order. C = 32
-  // (two waves per slice) adds into the accumulators with atomics.
-  constexpr bool kSlots = NSL == 4;
+  // A run whose leaf has pairs in no other task stores its sums straight to the accumulators; the task's
+  // first run, if its leaf began in an earlier task, and its last run, if its leaf goes on in a later one,
+  // store them to the task's slots 0 and 1 (the first run takes slot 0 when it is also the last), and
+  // bwd_kv_reduce adds a leaf's slots in task order.
   __shared__ int s_cont[2];  // the first run continues an earlier task's; the last run goes on
-  if (kSlots && tid == 0) {
+  if (tid == 0) {
     s_cont[0] = base > 0 && key_of(p.pairs[base - 1]) == s_key[0];
     s_cont[1] = base + n < total && key_of(p.pairs[base + n]) == s_key[n - 1];
   }
@@ -401,7 +399,32 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(BwdParams p) {
     // the run's contributions: lane (t, g) holds dims attn_out_dim(mt, g, j) of token 16 slice + t
     // (4 consecutive dimensions per M-tile)
     const long long tok = t0 + 16 * slice + r16;
-    if constexpr (kSlots) {
+    if constexpr (NSL == 2) {
+      // C = 32: the phase-1 wave of each slice hands its sums to the phase-0 wave through the staging
+      // tiles, which the tile pairs no longer use (16 D floats per array and wave, the same lane layout)
+      float* xv = reinterpret_cast<float*>(slice == 0 ? (void*)&s_q[0][0] : (void*)&s_qt[0][0]);
+      float* xk = reinterpret_cast<float*>(slice == 0 ? (void*)&s_do[0][0] : (void*)&s_dot[0][0]);
+      if (phase == 1) {
+#pragma unroll
+        for (int mt = 0; mt < MO; ++mt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            xv[(mt * 4 + j) * 64 + lane] = dva[mt][j];
+            xk[(mt * 4 + j) * 64 + lane] = dka[mt][j];
+          }
+      }
+      __syncthreads();
+      if (phase == 0) {
+#pragma unroll
+        for (int mt = 0; mt < MO; ++mt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            dva[mt][j] += xv[(mt * 4 + j) * 64 + lane];
+            dka[mt][j] += xk[(mt * 4 + j) * 64 + lane];
+          }
+      }
+    }
+    if (phase == 0) {
       const bool shared = (a == 0 && s_cont[0]) || (b == n && s_cont[1]);
       float* dkr;
       float* dvr;
@@ -423,17 +446,6 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(BwdParams p) {
                                                               p.scale * dka[mt][2], p.scale * dka[mt][3]);
         }
       }
-    } else if (tok < p.N) {
-      float* dvr = p.dv_acc + (bh * p.N + tok) * D;
-      float* dkr = p.dk_acc + (bh * p.N + tok) * D;
-#pragma unroll
-      for (int mt = 0; mt < MO; ++mt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int dim = attn_out_dim<D>(mt, grp, j);
-          atomicAdd(dvr + dim, dva[mt][j]);
-          atomicAdd(dkr + dim, p.scale * dka[mt][j]);
-        }
     }
     __syncthreads();  // K and V of this leaf are consumed before the next run restages them
   }
@@ -496,7 +508,7 @@ __global__ __launch_bounds__(256) void bwd_dq_merge_kernel(const int* __restrict
   *reinterpret_cast<uint4*>(dq + row * D + 8 * li) = w;
 }
 
-// dK / dV of the leaves whose pairs span several dkdv tasks (C = 64): one work-group per (sequence, KV
+// dK / dV of the leaves whose pairs span several dkdv tasks: one work-group per (sequence, KV
 // head, leaf) bucket of the attention regroup (pairs [off[x], off[x + 1]) of the sorted list); the sum of
 // the leaf's slots over its tasks, in task order, to the accumulators. A leaf within one task was stored
 // by that task; a leaf without pairs keeps the cleared zeros.
@@ -557,7 +569,7 @@ static hipError_t bwd_t(const SelDims& sd, const BwdParams& p0, const int* pos, 
   hipLaunchKernelGGL((attn_bwd_dq_kernel<D, C>), dim3((unsigned)wg), dim3(256), 0, st, p);
   hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, C>), dim3((unsigned)((max_pairs + kWgTaskDkdv - 1) / kWgTaskDkdv)),
                      dim3(256), 0, st, p);
-  if constexpr (C == 64) {
+  {
     const int leaves = sd.lv.n[0];
     hipLaunchKernelGGL((bwd_kv_reduce_kernel<D, C>), dim3((unsigned)((long long)sd.B * sd.Hkv * leaves)), dim3(256),
                        0, st, offsets, p.kv_part, leaves, sd.N, p.dk_acc, p.dv_acc);
@@ -609,7 +621,6 @@ hipError_t launch_attn_backward(const SelDims& sd, const void* q, const void* k,
 }
 
 size_t attn_backward_kv_part_bytes(const SelDims& sd) {
-  if (sd.C != 64) return 0;
   const long long tasks = ((long long)sd.B * sd.Hkv * sd.N * sd.K + kWgTaskDkdv - 1) / kWgTaskDkdv;
   return (size_t)tasks * 2 * 2 * sd.C * sd.D * sizeof(float);
 }

@@ -162,19 +162,22 @@ def _boundary_selection(N, C, K, extra):
     return sel
 
 
-def test_backward_task_boundaries():
+@pytest.mark.parametrize("C", [64, 32])
+def test_backward_task_boundaries(C):
     """dK / dV of leaves at every kind of edge of the dK/dV pass's 512-pair tasks, on a crafted selection
-    (B = 1, one KV head, N = 4096, C = 64, K = 4): leaf 0 fills task 0 exactly; leaf 1 fills tasks 1 and 2
-    (it starts on a task boundary and continues); leaf 2 lies inside task 3; leaf 3 starts inside task 3
-    and ends inside task 5, across the whole of task 4; leaf 4 ends exactly on a task boundary; leaf 5
-    starts on one. Gradients against the oracle, as in the other backward tests."""
-    pf = I.make_prefill(B=1, Hq=4, Hkv=1, N=4096, d=128, C=64, K=4, dtype="bf16", keys="ar1", seed=0,
+    (B = 1, one KV head, N = 4096, K = 4; C = 32 has two waves per token slice): leaf 0 fills task 0
+    exactly; leaf 1 fills tasks 1 and 2 (it starts on a task boundary and continues); leaf 2 lies inside
+    task 3; leaf 3 starts inside task 3 and ends inside task 5, across the whole of task 4; leaf 4 ends
+    exactly on a task boundary; leaf 5 starts on one. Gradients against the oracle, as in the other
+    backward tests."""
+    pf = I.make_prefill(B=1, Hq=4, Hkv=1, N=4096, d=128, C=C, K=4, dtype="bf16", keys="ar1", seed=0,
                         workload_id=730)
-    sel_np = _boundary_selection(pf.N, pf.C, pf.K, {0: 448, 1: 960, 2: 36, 3: 936, 4: 372})
+    sizes = [512, 1024, 100, 1000, 436]
+    sel_np = _boundary_selection(pf.N, pf.C, pf.K, {j: n - C for j, n in enumerate(sizes)})
     counts = np.bincount(sel_np[sel_np >= 0], minlength=pf.N // pf.C)
     starts = np.concatenate([[0], np.cumsum(counts)])
-    assert list(counts[:6]) == [512, 1024, 100, 1000, 436, 64]
-    assert list(starts[:7]) == [0, 512, 1536, 1636, 2636, 3072, 3136]
+    assert list(counts[:6]) == sizes + [C]
+    assert list(starts[:7]) == [0, 512, 1536, 1636, 2636, 3072, 3072 + C]
     s = shape_of(pf, 4)
     q, k, v = to_device(pf.q), to_device(pf.k), to_device(pf.v)
     sel = torch.from_numpy(sel_np.reshape(1, 1, pf.N, pf.K)).cuda()
@@ -189,4 +192,4 @@ def test_backward_task_boundaries():
     torch.cuda.synchronize()
     g = dict(sel=sel.cpu().numpy(), do=I.bf16_to_f32(do_np).astype(np.float64), dq=dq.float().cpu().numpy(),
              dk=dk.float().cpu().numpy(), dv=dv.float().cpu().numpy())
-    compare_backward(pf, g, "task boundaries")
+    compare_backward(pf, g, f"task boundaries C={C}")
